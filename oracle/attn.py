@@ -1,0 +1,70 @@
+"""Sparse attention given a plan: the plain definition, in fp64.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+Follows the AB-Attention page (onedev.kr/papers/1521): the fused pass of
+section "전제와 한계" (first paragraph) gathers the sampled KV blocks and runs
+softmax attention over them with the logit of every token of block j shifted
+by -log pi_ij (section "어떻게 쓰나", where this shift is shown equal to
+weighting the numerator and the denominator by 1/pi_ij).  Only a plain
+definition is written here: gather the keys, one dense softmax, no tiling and
+no online rescaling.
+
+Readings: scale 1/sqrt(d) unless given; no causal mask (full 3D attention of
+a video DiT); natural log; the shift applies to every token of the block;
+keys with index >= Nk (partial last block, padding) are left out.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def gather_keys(blocks: np.ndarray, bias: np.ndarray, kv_block: int, Nk: int):
+    """Token indices and per-token logit shift of the listed blocks."""
+    keys = (blocks[:, None].astype(np.int64) * kv_block + np.arange(kv_block)).ravel()
+    kb = np.repeat(bias.astype(np.float64), kv_block)
+    valid = keys < Nk
+    return keys[valid], kb[valid]
+
+
+def attn_fwd(q, k, v, q_block: int, kv_block: int, idx, bias, count,
+             scale: float | None = None, blocks=None):
+    """One head.  q (Nq, d), k/v (Nk, d) fp64; idx (nqb, L) int, bias (nqb, L)
+    fp32 or None (all pi = 1), count (nqb,) int.
+
+    Returns (O (Nq, d) fp64, LSE (Nq,) fp64 natural log).  ``blocks`` limits the
+    work to the listed query blocks (other rows stay NaN).
+    """
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nqb = -(-Nq // q_block)
+    O = np.full((Nq, d), np.nan)
+    lse = np.full(Nq, np.nan)
+    todo = range(nqb) if blocks is None else blocks
+    for i in todo:
+        c = int(count[i])
+        bl = np.asarray(idx[i][:c])
+        b = np.zeros(c, np.float32) if bias is None else np.asarray(bias[i][:c])
+        keys, kb = gather_keys(bl, b, kv_block, Nk)
+        r0, r1 = i * q_block, min(Nq, (i + 1) * q_block)
+        logits = (q[r0:r1] @ k[keys].T) * scale + kb[None, :]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        den = e.sum(axis=1, keepdims=True)
+        O[r0:r1] = (e @ v[keys]) / den
+        lse[r0:r1] = (m + np.log(den))[:, 0]
+    return O, lse
+
+
+def dense_attn(q, k, v, scale: float | None = None):
+    """Full softmax attention (every key, no shift), fp64."""
+    d = q.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    logits = (q @ k.T) * scale
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    den = e.sum(axis=1, keepdims=True)
+    return (e @ v) / den, (m + np.log(den))[:, 0]

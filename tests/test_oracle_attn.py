@@ -1,0 +1,98 @@
+"""Pins of the attention oracle: dense reduction (torch SDPA, fp64 CPU),
+the -log pi shift versus explicit 1/pi weighting, Horvitz-Thompson
+unbiasedness of numerator and denominator, and key masking."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn as oat
+from oracle import plan as opl
+from oracle.splitmix import UNIT
+from synth import bf16_bits_to_f64, make_qkv
+
+
+def _head(T, Hg, Wg, d, seed=0):
+    q, k, v = make_qkv(T, Hg, Wg, 1, d, seed)
+    return tuple(bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("kv_block", [1, 4, 64, 128])
+def test_all_blocks_pi_one_is_dense_attention(kv_block):
+    q, k, v = _head(1, 16, 24, 64, seed=1)
+    N = q.shape[0]
+    M = -(-N // kv_block)
+    nqb = -(-N // 128)
+    idx = np.tile(np.arange(M), (nqb, 1))
+    cnt = np.full(nqb, M)
+    O, lse = oat.attn_fwd(q, k, v, 128, kv_block, idx, None, cnt)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, 0].numpy()
+    np.testing.assert_allclose(O, ref, atol=1e-12, rtol=1e-10)
+    lref = torch.logsumexp(torch.from_numpy(q @ k.T / 8.0), dim=-1).numpy()
+    np.testing.assert_allclose(lse, lref, rtol=1e-13)
+
+
+def test_shift_equals_inverse_probability_weighting():
+    q, k, v = _head(1, 16, 32, 64, seed=2)
+    N, d = q.shape
+    kvb, M, s = 4, N // 4, 40
+    rng = np.random.default_rng(3)
+    S = rng.gamma(0.5, size=(4, M))
+    S /= S.sum(axis=1, keepdims=True)
+    idx, bias, cnt, _ = opl.plan(S, s, opl.SIP, seed=5)
+    O, _ = oat.attn_fwd(q, k, v, 128, kvb, idx, bias, cnt)
+    for i in range(4):
+        pi = opl.inclusion_probabilities(S[i], s)
+        # weights 1/pi from the stored (fp32) shift, then from the exact pi
+        for inv_pi, tol in ((lambda t, j: np.exp(np.float64(bias[i, t])), 1e-12),
+                            (lambda t, j: 1.0 / pi[j], 1e-6)):
+            num = np.zeros((128, d)); den = np.zeros((128, 1))
+            for t, j in enumerate(idx[i, :cnt[i]]):
+                e = np.exp(q[i * 128:(i + 1) * 128] @ k[j * 4:(j + 1) * 4].T / np.sqrt(d))
+                num += e @ v[j * 4:(j + 1) * 4] * inv_pi(t, j)
+                den += e.sum(axis=1, keepdims=True) * inv_pi(t, j)
+            np.testing.assert_allclose(O[i * 128:(i + 1) * 128], num / den, rtol=0, atol=tol)
+
+
+def test_ht_numerator_and_denominator_unbiased_over_offsets():
+    """Mean over an offset sweep of the 1/pi-weighted numerator and
+    denominator tends to the dense ones (the ratio itself is not asserted)."""
+    q, k, v = _head(1, 8, 16, 32, seed=4)
+    d = q.shape[1]
+    kvb, M, s, G = 4, 32, 8, 1024
+    qrow = q[:4]
+    e_blocks = [np.exp(qrow @ k[j * 4:(j + 1) * 4].T / np.sqrt(d)) for j in range(M)]
+    dense_num = sum(e @ v[j * 4:(j + 1) * 4] for j, e in enumerate(e_blocks))
+    dense_den = sum(e.sum(axis=1) for e in e_blocks)
+    S = np.array([e.sum() for e in e_blocks]); S /= S.sum()
+    pi = opl.inclusion_probabilities(S, s)
+    num = np.zeros_like(dense_num); den = np.zeros_like(dense_den)
+    for g in range(G):
+        idx, _, _, _ = opl.sip_row(S, s, (g * UNIT) // G)
+        for j in idx:
+            num += e_blocks[j] @ v[j * 4:(j + 1) * 4] / pi[j]
+            den += e_blocks[j].sum(axis=1) / pi[j]
+    bn = sum(np.abs(e_blocks[j] @ v[j * 4:(j + 1) * 4]) / pi[j] for j in range(M)) / G
+    bd = sum(e_blocks[j].sum(axis=1) / pi[j] for j in range(M)) / G
+    assert np.all(np.abs(num / G - dense_num) <= bn + 1e-9)
+    assert np.all(np.abs(den / G - dense_den) <= bd + 1e-9)
+
+
+def test_keys_beyond_nk_are_masked():
+    q, k, v = _head(1, 10, 13, 32, seed=6)       # N = 130: last 4-block has 2 rows
+    N = q.shape[0]
+    M = -(-N // 4)
+    idx = np.tile(np.arange(M), (2, 1))
+    O, _ = oat.attn_fwd(q, k, v, 128, 4, idx, None, np.full(2, M))
+    ref, _ = oat.dense_attn(q, k, v)
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_topk_plan_attention_equals_dense_over_selected_keys():
+    q, k, v = _head(1, 8, 16, 32, seed=7)
+    S = np.random.default_rng(1).random((1, 32))
+    idx, bias, cnt, _ = opl.plan(S, 5, opl.TOPK)
+    O, _ = oat.attn_fwd(q, k, v, 128, 4, idx, bias, cnt)
+    keys = np.concatenate([np.arange(j * 4, j * 4 + 4) for j in idx[0]])
+    ref, _ = oat.dense_attn(q, k[keys], v[keys])
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-13)
