@@ -1,0 +1,231 @@
+"""Block-sparse attention forward on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbsa.so`` (declared in
+``include/bsa.h``).  It only marshals arguments: every step of the path runs
+in the library's HIP kernels.  PyTorch provides device memory and the
+current stream.  The library must be built (``python -m
+block_sparse_attention_mean_amd.build``); importing the binding without it
+raises ImportError -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
+    "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
+    "bsa_basa_plan", "bsa_window_unpermute", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+PLAN_SIP, PLAN_TOPK = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with "
+                      "`python -m block_sparse_attention_mean_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _f, _sz, _u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
+_pi, _psz = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)
+
+lib.bsa_status_string.restype = ctypes.c_char_p
+lib.bsa_status_string.argtypes = [_i]
+lib.bsa_version.restype = ctypes.c_char_p
+lib.bsa_version.argtypes = []
+lib.bsa_sampling_offset.restype = _u64
+lib.bsa_sampling_offset.argtypes = [_u64, _u64]
+lib.bsa_select_workspace_bytes.restype = _i
+lib.bsa_select_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _psz]
+lib.bsa_select_scores.restype = _i
+lib.bsa_select_scores.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
+lib.bsa_sip_plan.restype = _i
+lib.bsa_sip_plan.argtypes = [_p, _i, _i, _i, _i, _i, _i, _u64, _p, _p, _p, _p, _p, _p]
+lib.bsa_attn_fwd.restype = _i
+lib.bsa_attn_fwd.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _f, _p, _p, _p]
+lib.bsa_basa_layout.restype = _i
+lib.bsa_basa_layout.argtypes = [_i] * 12 + [_pi] * 5 + [_psz]
+lib.bsa_basa_plan.restype = _i
+lib.bsa_basa_plan.argtypes = [_p, _p, _p] + [_i] * 14 + [_p] * 6 + [_p, _sz, _p]
+lib.bsa_window_unpermute.restype = _i
+lib.bsa_window_unpermute.argtypes = [_p, _p] + [_i] * 10 + [_p]
+
+# Exported symbols of include/bsa.h (checked by the CPU tests).
+SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bsa_select_scores",
+           "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
+           "bsa_basa_plan", "bsa_window_unpermute"]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {lib.bsa_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise BsaError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+def bsa_sampling_offset(seed: int, row: int) -> int:
+    return int(lib.bsa_sampling_offset(seed & (2**64 - 1), row))
+
+
+def bsa_select_workspace_bytes(B, H, N, d, q_block=128, kv_block=4, n_clusters=8) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.bsa_select_workspace_bytes(B, H, N, d, q_block, kv_block, n_clusters,
+                                          ctypes.byref(out)), "bsa_select_workspace_bytes")
+    return out.value
+
+
+def bsa_select_scores(q, k, q_block=128, kv_block=4, n_clusters=8, kmeans_iters=1,
+                      scores=None, centroids=None, weights=None, workspace=None,
+                      want_centroids=False, stream=None):
+    """q, k: [B,H,N,d] bf16 -> scores [B,H,nQB,M] fp32 (+ centroids, weights)."""
+    import torch
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    B, H, N, d = q.shape
+    nqb, M = -(-N // q_block), -(-N // kv_block)
+    if scores is None:
+        scores = torch.empty((B, H, nqb, M), dtype=torch.float32, device=q.device)
+    if want_centroids and centroids is None:
+        centroids = torch.empty((B, H, nqb, n_clusters, d), dtype=torch.float32, device=q.device)
+    if want_centroids and weights is None:
+        weights = torch.empty((B, H, nqb, n_clusters), dtype=torch.float32, device=q.device)
+    need = bsa_select_workspace_bytes(B, H, N, d, q_block, kv_block, n_clusters)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_select_scores(_ptr(q), _ptr(k), B, H, N, d, q_block, kv_block, n_clusters,
+                                 kmeans_iters, _ptr(scores), _ptr(centroids), _ptr(weights),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "bsa_select_scores")
+    return scores, centroids, weights
+
+
+def bsa_sip_plan(scores, budget, mode=PLAN_SIP, seed=0, offsets=None, idx=None, bias=None,
+                 count=None, lam=None, want_lambda=False, stream=None):
+    """scores [B,H,nQB,M] fp32 -> (idx, bias, count, lambda) device tensors."""
+    import torch
+    _need(scores, torch.float32, "scores", 4)
+    B, H, nqb, M = scores.shape
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((B, H, nqb, budget), dtype=torch.int32, device=dev)
+    if bias is None:
+        bias = torch.empty((B, H, nqb, budget), dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
+    if want_lambda and lam is None:
+        lam = torch.empty((B, H, nqb), dtype=torch.float64, device=dev)
+    if offsets is not None:
+        _need(offsets, torch.int64, "offsets")
+    _check(lib.bsa_sip_plan(_ptr(scores), B, H, nqb, M, budget, mode, seed & (2**64 - 1),
+                            _ptr(offsets), _ptr(idx), _ptr(bias), _ptr(count), _ptr(lam),
+                            _stream(stream)), "bsa_sip_plan")
+    return idx, bias, count, lam
+
+
+def bsa_attn_fwd(q, k, v, idx, bias, count, q_block=128, kv_block=4, softmax_scale=0.0,
+                 out=None, lse=None, want_lse=False, stream=None):
+    """q [B,H,Nq,d], k/v [B,H,Nk,d] bf16; idx [B,H,nQB,L] int32; bias (optional)
+    [B,H,nQB,L] fp32; count [B,H,nQB] int32 -> out [B,H,Nq,d] bf16 (+ lse)."""
+    import torch
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    _need(v, torch.bfloat16, "v", 4)
+    _need(idx, torch.int32, "idx", 4)
+    _need(count, torch.int32, "count", 3)
+    if bias is not None:
+        _need(bias, torch.float32, "bias", 4)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.bsa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, q_block, kv_block,
+                            _ptr(idx), _ptr(bias), _ptr(count), idx.shape[-1],
+                            float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "bsa_attn_fwd")
+    return out, lse
+
+
+def bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block=4, B=1, H=1):
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    ws = ctypes.c_size_t(0)
+    _check(lib.bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H,
+                               *[ctypes.byref(x) for x in vals], ctypes.byref(ws)),
+           "bsa_basa_layout")
+    keys = ["nwin", "Nq_pad", "Nk_valid", "Nk_alloc", "max_blocks"]
+    out = {k: v.value for k, v in zip(keys, vals)}
+    out["workspace"] = ws.value
+    return out
+
+
+def bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
+                  want_routes=False, stream=None):
+    """Window-major Q/K/V (+ pooled memory) and the block lists of BASA."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, d = q.shape
+    lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
+    dev = q.device
+    qp = torch.empty((B, H, lay["Nq_pad"], d), dtype=torch.bfloat16, device=dev)
+    kp = torch.empty((B, H, lay["Nk_alloc"], d), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    nqb = lay["Nq_pad"] // 128
+    idx = torch.empty((B, H, nqb, lay["max_blocks"]), dtype=torch.int32, device=dev)
+    count = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
+    routes = (torch.empty((B, H, lay["nwin"], max(topk, 1)), dtype=torch.int32, device=dev)
+              if want_routes else None)
+    ws = torch.empty(max(lay["workspace"], 256), dtype=torch.uint8, device=dev)
+    _check(lib.bsa_basa_plan(_ptr(q), _ptr(k), _ptr(v), B, H, T, Hg, Wg, d, wh, ww, dy, dx, ph,
+                             pw, topk, kv_block, _ptr(qp), _ptr(kp), _ptr(vp), _ptr(idx),
+                             _ptr(count), _ptr(routes), _ptr(ws), ws.numel(), _stream(stream)),
+           "bsa_basa_plan")
+    return dict(qp=qp, kp=kp, vp=vp, idx=idx, count=count, routes=routes, **lay)
+
+
+def bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=None, stream=None):
+    import torch
+    _need(out_perm, torch.bfloat16, "out_perm", 4)
+    B, H, _, d = out_perm.shape
+    if out is None:
+        out = torch.empty((B, H, T * Hg * Wg, d), dtype=torch.bfloat16, device=out_perm.device)
+    _check(lib.bsa_window_unpermute(_ptr(out_perm), _ptr(out), B, H, T, Hg, Wg, d, wh, ww, dy,
+                                    dx, _stream(stream)), "bsa_window_unpermute")
+    return out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

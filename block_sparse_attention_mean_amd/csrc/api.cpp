@@ -1,0 +1,186 @@
+// C ABI entry points: host-side validation and kernel dispatch.
+//
+// Every check here runs before any HIP call so that invalid calls return a
+// status without touching the GPU (and can be tested on a machine without
+// one).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/bsa.h"
+
+namespace bsa {
+int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int Nq, int Nk,
+                    int d, int kv_block, const int32_t *idx, const float *bias,
+                    const int32_t *count, int max_blocks, float scale, void *out, float *lse,
+                    hipStream_t stream);
+int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, int mode,
+                    uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
+                    int32_t *count, double *lambda, hipStream_t stream);
+int launch_select_scores(const void *q, const void *k, int B, int H, int N, int d, int kv_block,
+                         int n_clusters, int kmeans_iters, float *scores, float *centroids,
+                         float *weights, void *workspace, hipStream_t stream);
+size_t select_workspace_bytes(int B, int H, int N, int d, int kv_block, int n_clusters);
+int basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
+                int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
+                int *Nk_alloc, int *max_blocks, size_t *workspace);
+int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
+                     int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
+                     int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
+                     int32_t *routes, void *workspace, hipStream_t stream);
+int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg,
+                            int Wg, int d, int wh, int ww, int dy, int dx, hipStream_t stream);
+uint64_t sampling_offset(uint64_t seed, uint64_t row);
+}  // namespace bsa
+
+namespace {
+
+constexpr long long kMaxIndex = 0x7fffffffLL;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool pow2_block(int b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char *bsa_status_string(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_ARG: return "invalid argument (null pointer, non-positive size or bad mode)";
+    case BSA_ERR_UNSUPPORTED: return "unsupported head dim, block size or cluster count";
+    case BSA_ERR_BUDGET: return "budget outside [1, M]";
+    case BSA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case BSA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case BSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BSA_ERR_SIZE: return "size product exceeds the supported index range";
+    default: return "unknown status";
+  }
+}
+
+const char *bsa_version(void) { return "bsa 0.1 gfx950"; }
+
+uint64_t bsa_sampling_offset(uint64_t seed, uint64_t row) { return bsa::sampling_offset(seed, row); }
+
+int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int Nq, int Nk,
+                 int d, int q_block, int kv_block, const int32_t *idx, const float *bias,
+                 const int32_t *count, int max_blocks, float softmax_scale, void *out,
+                 float *lse, void *stream) {
+  if (!q || !k || !v || !idx || !count || !out) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
+  if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)) ||
+      (lse && !aligned(lse, 4)))
+    return BSA_ERR_ALIGN;
+  const long long nqb = (Nq + 127) / 128;
+  if ((long long)B * H * nqb > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  return bsa::launch_attn_fwd(q, k, v, B, H, Nq, Nk, d, kv_block, idx, bias, count, max_blocks,
+                              scale, out, lse, (hipStream_t)stream);
+}
+
+int bsa_sip_plan(const float *scores, int B, int H, int nQB, int M, int budget, int mode,
+                 uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
+                 int32_t *count, double *lambda, void *stream) {
+  if (!scores || !idx || !count) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || nQB < 1 || M < 1) return BSA_ERR_ARG;
+  if (mode != BSA_PLAN_SIP && mode != BSA_PLAN_TOPK) return BSA_ERR_ARG;
+  if (budget < 1 || budget > M) return BSA_ERR_BUDGET;
+  if (!aligned(scores, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
+      (bias && !aligned(bias, 4)) || (lambda && !aligned(lambda, 8)) ||
+      (offsets && !aligned(offsets, 8)))
+    return BSA_ERR_ALIGN;
+  if ((long long)B * H * nQB > kMaxIndex) return BSA_ERR_SIZE;
+  if (M > (1 << 20)) return BSA_ERR_SIZE;  // one row must fit the on-chip sampler
+  return bsa::launch_sip_plan(scores, B * H * nQB, nQB, M, budget, mode, seed, offsets, idx,
+                              bias, count, lambda, (hipStream_t)stream);
+}
+
+int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_block,
+                               int n_clusters, size_t *bytes) {
+  if (!bytes) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || N < 1) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || n_clusters < 1 ||
+      n_clusters > 16)
+    return BSA_ERR_UNSUPPORTED;
+  *bytes = bsa::select_workspace_bytes(B, H, N, d, kv_block, n_clusters);
+  return BSA_OK;
+}
+
+int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d, int q_block,
+                      int kv_block, int n_clusters, int kmeans_iters, float *scores,
+                      float *centroids, float *weights, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+  if (!q || !k || !scores) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || N < 1 || kmeans_iters < 0 || kmeans_iters > 16) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || n_clusters < 1 ||
+      n_clusters > 16)
+    return BSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 16) ||
+      (centroids && !aligned(centroids, 16)) || (weights && !aligned(weights, 4)))
+    return BSA_ERR_ALIGN;
+  const long long nqb = (N + 127) / 128;
+  const long long M = (N + kv_block - 1) / kv_block;
+  if ((long long)B * H * nqb * n_clusters > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)B * H * M > kMaxIndex) return BSA_ERR_SIZE;
+  const size_t need = bsa::select_workspace_bytes(B, H, N, d, kv_block, n_clusters);
+  if (!workspace || workspace_bytes < need) return BSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;
+  return bsa::launch_select_scores(q, k, B, H, N, d, kv_block, n_clusters, kmeans_iters, scores,
+                                   centroids, weights, workspace, (hipStream_t)stream);
+}
+
+int bsa_basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
+                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
+                    int *Nk_alloc, int *max_blocks, size_t *workspace) {
+  if (!nwin || !Nq_pad || !Nk_valid || !Nk_alloc || !max_blocks || !workspace)
+    return BSA_ERR_ARG;
+  if (T < 1 || Hg < 1 || Wg < 1 || wh < 1 || ww < 1 || ph < 1 || pw < 1 || topk < 0 || B < 1 ||
+      H < 1)
+    return BSA_ERR_ARG;
+  if (wh > Hg || ww > Wg) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  return bsa::basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, nwin, Nq_pad,
+                          Nk_valid, Nk_alloc, max_blocks, workspace);
+}
+
+int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
+                  int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
+                  int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
+                  int32_t *routes, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !qp || !kp || !vp || !idx || !count) return BSA_ERR_ARG;
+  int nwin, nqp, nkv, nka, mb;
+  size_t ws;
+  int st = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, &nwin, &nqp, &nkv,
+                           &nka, &mb, &ws);
+  if (st != BSA_OK) return st;
+  if (topk > nwin - 1) return BSA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||
+      !aligned(kp, 16) || !aligned(vp, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
+      (routes && !aligned(routes, 4)))
+    return BSA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < ws) return BSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;
+  return bsa::launch_basa_plan(q, k, v, B, H, T, Hg, Wg, d, wh, ww, dy, dx, ph, pw, topk,
+                               kv_block, qp, kp, vp, idx, count, routes, workspace,
+                               (hipStream_t)stream);
+}
+
+int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
+                         int d, int wh, int ww, int dy, int dx, void *stream) {
+  if (!out_perm || !out) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || T < 1 || Hg < 1 || Wg < 1 || wh < 1 || ww < 1 || wh > Hg || ww > Wg)
+    return BSA_ERR_ARG;
+  if (!head_dim_ok(d)) return BSA_ERR_UNSUPPORTED;
+  if (!aligned(out_perm, 16) || !aligned(out, 16)) return BSA_ERR_ALIGN;
+  return bsa::launch_window_unpermute(out_perm, out, B, H, T, Hg, Wg, d, wh, ww, dy, dx,
+                                      (hipStream_t)stream);
+}
+
+}  // extern "C"

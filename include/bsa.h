@@ -1,0 +1,231 @@
+/*
+ * bsa.h -- C ABI of the block-sparse attention forward library for AMD
+ * MI355X (gfx950).
+ *
+ * The library computes the hot path of training-free dynamic block-sparse
+ * attention for video diffusion transformers:
+ *
+ *   bsa_select_scores  KV-block mean pooling, k-means inside every 128-query
+ *                      block, block scores (AB-Attention page, onedev.kr/
+ *                      papers/1521, section "무엇과 다른가": the
+ *                      Intra-Block Clustering Selector);
+ *   bsa_sip_plan       SIP inclusion probabilities pi = min(1, lambda * S)
+ *                      fitted to the budget, systematic sample of exactly s
+ *                      distinct blocks; or top-k (same page, section
+ *                      "어떻게 쓰나", and the ablation paragraph of
+ *                      "전제와 한계");
+ *   bsa_attn_fwd       one fused pass that gathers the listed small KV
+ *                      blocks into full tiles, shifts logits by -log pi,
+ *                      and runs online softmax with P.V accumulation (same
+ *                      page, section "전제와 한계", first paragraph);
+ *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
+ *                      structure of the BASA page (onedev.kr/papers/688,
+ *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
+ *                      into block lists for bsa_attn_fwd.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, row-major and contiguous.  [B,H,N,d] means
+ *     element (b,h,n,c) sits at ((b*H + h)*N + n)*d + c.  bf16 tensors are
+ *     passed as `const void*` / `void*` holding IEEE bfloat16 bit patterns.
+ *   - Every pointer argument is a DEVICE pointer unless its comment says
+ *     host.  The caller allocates and owns every buffer; the library never
+ *     allocates, frees or keeps device memory and holds no state between
+ *     calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued asynchronously on it; no entry point synchronises.
+ *   - All argument checks run on the host before any HIP call, so an
+ *     invalid call returns an error code without touching the GPU.  A HIP
+ *     launch failure returns BSA_ERR_HIP.  Errors that only the device can
+ *     see (non-finite scores, out-of-range block indices) are reported in
+ *     the outputs as documented per call; they never fault.
+ *   - Supported sizes: head dim d in {64, 128}; q_block = 128; kv_block a
+ *     power of two in [1, 128]; B, H >= 1; N >= 1; every 16-byte vector
+ *     access requires bf16 tensors to be 16-byte aligned.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BSA_OK = 0,
+  BSA_ERR_ARG = -1,         /* null pointer, non-positive size, bad mode   */
+  BSA_ERR_UNSUPPORTED = -2, /* head dim, block size or cluster count       */
+  BSA_ERR_BUDGET = -3,      /* budget outside [1, M]                       */
+  BSA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned     */
+  BSA_ERR_HIP = -5,         /* a HIP runtime call or launch failed         */
+  BSA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required  */
+  BSA_ERR_SIZE = -7         /* a size product overflows the index range    */
+};
+
+enum { BSA_PLAN_SIP = 0, BSA_PLAN_TOPK = 1 };
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *bsa_status_string(int status);
+
+/* Library version string, e.g. "bsa 0.1 gfx950" (static storage). */
+const char *bsa_version(void);
+
+/* ------------------------------------------------------------------------
+ * Selector (AB-Attention page, section "무엇과 다른가").
+ *
+ * For every (b, h) and query block i (rows [128 i, min(N, 128 i + 128))):
+ *   pooled key   kbar_j = mean of K rows of KV block j (the last block
+ *                averages its valid rows only), j < M = ceil(N / kv_block);
+ *   k-means      n_clusters clusters start from contiguous segment means
+ *                (segment c = rows [floor(c n / C), floor((c+1) n / C)));
+ *                each of kmeans_iters iterations assigns every query to the
+ *                nearest centroid (squared Euclidean distance, ties to the
+ *                lowest cluster) and moves every non-empty cluster to its
+ *                members' mean; share w_c = members / n.  This runs in fp32
+ *                in a fixed operation order (ascending-row member sums, one
+ *                IEEE division, distances summed over dims in ascending
+ *                order without fused multiply-add), so its decisions are
+ *                reproducible bit for bit;
+ *   scores       S_ij = sum_c w_c softmax_j(mu_c . kbar_j / sqrt(d)), the
+ *                softmax running over all M KV blocks of the head.
+ *
+ * q, k        [B,H,N,d] bf16, 16-byte aligned.
+ * scores      out: [B,H,nQB,M] fp32, nQB = ceil(N / q_block).
+ * centroids   optional out (NULL = not written): [B,H,nQB,C,d] fp32.
+ * weights     optional out (NULL = not written): [B,H,nQB,C] fp32.
+ * workspace   device scratch of at least bsa_select_workspace_bytes() bytes,
+ *             256-byte aligned; its contents are undefined after the call.
+ * n_clusters  1..16; kmeans_iters 0..16 (0 = segment means).
+ * --------------------------------------------------------------------- */
+int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_block,
+                               int n_clusters, size_t *bytes /* host out */);
+
+int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d,
+                      int q_block, int kv_block, int n_clusters, int kmeans_iters,
+                      float *scores, float *centroids, float *weights,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Sampling plan (AB-Attention page, section "어떻게 쓰나").
+ *
+ * One row = one (b, h, i).  mode BSA_PLAN_SIP:
+ *   M+ = number of positive scores.  If budget >= M+, every positive block
+ *   is taken with pi = 1 (count = M+, lambda = +inf).  Otherwise r is the
+ *   smallest number of saturated blocks with (s - r) * S_(r+1) <= T_r
+ *   decided exactly (S_(1) >= S_(2) >= ... sorted scores, T_r the exact sum
+ *   of all but the r largest), found by bisection; lambda = (s - r) / T_r
+ *   with T_r correctly rounded to fp64 and one IEEE fp64 division;
+ *   pi_j = min(1, lambda * S_j) (one IEEE fp64 multiply);
+ *   Pi_j = floor(pi_j * 2^44), C_j = Pi_0 + ... + Pi_j (exact integers);
+ *   block j is drawn when some x_k = U + k * 2^44 (k = 0..s-1) falls in
+ *   [C_{j-1}, C_j).  Exactly s distinct blocks are drawn; every block with
+ *   pi = 1 is among them.
+ * mode BSA_PLAN_TOPK: the s largest scores, ties to the lowest index, pi = 1,
+ *   count = s.
+ *
+ * scores   [B,H,nQB,M] fp32, finite and >= 0.
+ * budget   s, 1 <= s <= M.
+ * seed     used when offsets == NULL: U of row r = (b*H + h)*nQB + i is
+ *          bsa_sampling_offset(seed, r).
+ * offsets  optional [B*H*nQB] uint64 offsets U, each < 2^44 - 2^16.
+ * idx      out: [B,H,nQB,budget] int32, the drawn blocks in ascending order,
+ *          entries beyond count set to -1.
+ * bias     out: [B,H,nQB,budget] fp32 logit shift -ln(pi_j) of each drawn
+ *          block (0 for top-k and for saturated blocks), 0 beyond count.
+ *          May be NULL.
+ * count    out: [B,H,nQB] int32 blocks drawn.  A row holding a NaN, an
+ *          infinity or a negative score gets count = -1 and no blocks.
+ * lambda   optional out (NULL = not written): [B,H,nQB] fp64; +inf when
+ *          every positive block is taken, 0 for top-k.
+ * The plan is caller-owned and stays valid for any number of later
+ * bsa_attn_fwd calls (the page rebuilds it every 4 denoising steps).
+ * --------------------------------------------------------------------- */
+int bsa_sip_plan(const float *scores, int B, int H, int nQB, int M, int budget, int mode,
+                 uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
+                 int32_t *count, double *lambda, void *stream);
+
+/* Host helper, no GPU needed: U = floor((x >> 20) * (2^44 - 2^16) / 2^44)
+ * where x is output number `row` (0-based) of SplitMix64 (Steele, Lea and
+ * Flood 2014) seeded with `seed`. */
+uint64_t bsa_sampling_offset(uint64_t seed, uint64_t row);
+
+/* ------------------------------------------------------------------------
+ * Fused sparse attention (AB-Attention page, section "전제와 한계", first
+ * paragraph; the shift of section "어떻게 쓰나").
+ *
+ * For query row n of query block i = n / q_block of (b, h):
+ *   keys  = tokens j*kv_block + t (t < kv_block) of every listed block
+ *           j = idx[b,h,i,e], e < count[b,h,i], with token index < Nk;
+ *   logit = scale * q_n . k_t + bias[b,h,i,e]   (bias = -ln pi; NULL = 0);
+ *   out_n = softmax(logits) . V_keys;  lse_n = ln sum exp(logits).
+ *
+ * q        [B,H,Nq,d] bf16.   k, v  [B,H,Nk,d] bf16.  16-byte aligned.
+ * idx      [B,H,nQB,max_blocks] int32, nQB = ceil(Nq / q_block).  Order is
+ *          free (ascending gives the best gather locality).  Entries outside
+ *          [0, ceil(Nk / kv_block)) are skipped.
+ * bias     optional [B,H,nQB,max_blocks] fp32 added to every logit of the
+ *          listed block.
+ * count    [B,H,nQB] int32, clamped to [0, max_blocks] (negative = 0).
+ * scale    softmax_scale <= 0 selects 1/sqrt(d).
+ * out      [B,H,Nq,d] bf16 (round to nearest even).  A row with no valid
+ *          key gets zeros (and lse = -inf).
+ * lse      optional [B,H,Nq] fp32 natural-log sum of exponentials.
+ * --------------------------------------------------------------------- */
+int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int Nq, int Nk,
+                 int d, int q_block, int kv_block, const int32_t *idx, const float *bias,
+                 const int32_t *count, int max_blocks, float softmax_scale, void *out,
+                 float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
+ * BASA-structured lists (BASA page, onedev.kr/papers/688).
+ *
+ * Geometry: a latent grid T x Hg x Wg (token n = (t*Hg + y)*Wg + x) is
+ * shifted cyclically by -(dy, dx) and cut into wh x ww spatial windows that
+ * keep every frame (a ragged last window row/column keeps its smaller
+ * size).  Window w of the shifted grid is laid out window-major: its tokens
+ * in (t, shifted row, shifted column) order, padded with zero rows to a
+ * multiple of 128, windows in row-major window order.  The pooled memory G
+ * (per-frame non-overlapping ph x pw spatial means of K and V on the
+ * unshifted grid, T * ceil(Hg/ph) * ceil(Wg/pw) tokens, raster order) is
+ * appended after the last window in the key/value buffers.  Every query
+ * window routes to the `topk` other windows with the largest
+ * mean(Q_w) . mean(K_w') (fp32, fixed order: window-local token order sums,
+ * one IEEE division, ascending-dim dot product without fused multiply-add;
+ * ties to the lowest window).  The block list of a query block of window w
+ * is: w's KV blocks, then each routed window's KV blocks (ascending window
+ * id), then every pooled block; pi = 1 (no bias).
+ *
+ * bsa_basa_layout (host, no GPU) reports the sizes:
+ *   nwin         number of windows;
+ *   Nq_pad       padded query rows (= padded window-major rows);
+ *   Nk_valid     Nq_pad + pooled tokens (keys at or beyond are masked);
+ *   Nk_alloc     rows to allocate for kp/vp (Nk_valid rounded up to kv_block);
+ *   max_blocks   list stride;
+ *   workspace    bytes of device scratch bsa_basa_plan needs.
+ * kv_block must divide every window's token count and 128.
+ *
+ * bsa_basa_plan: q,k,v [B,H,N,d] bf16 -> qp [B,H,Nq_pad,d], kp, vp
+ * [B,H,Nk_alloc,d] bf16 (caller-allocated), idx [B,H,Nq_pad/128,max_blocks]
+ * int32, count [B,H,Nq_pad/128] int32, routes optional [B,H,nwin,topk] int32.
+ * Then bsa_attn_fwd(qp, kp, vp, B, H, Nq_pad, Nk_valid, d, 128, kv_block,
+ * idx, NULL, count, max_blocks, ...) and bsa_window_unpermute() give the
+ * output in raster order.
+ * --------------------------------------------------------------------- */
+int bsa_basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
+                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
+                    int *Nk_alloc, int *max_blocks, size_t *workspace /* all host out */);
+
+int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
+                  int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
+                  int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
+                  int32_t *routes, void *workspace, size_t workspace_bytes, void *stream);
+
+int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
+                         int d, int wh, int ww, int dy, int dx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

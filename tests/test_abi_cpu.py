@@ -1,0 +1,127 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/bsa.h declares, and rejects invalid calls with status codes before
+any HIP call (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import block_sparse_attention_mean_amd as m
+    return m
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(bsa):
+    declared = _declared_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(bsa.lib, name), name
+    assert sorted(bsa.SYMBOLS) == declared
+
+
+def test_status_strings(bsa):
+    for s in range(-7, 1):
+        assert len(bsa.lib.bsa_status_string(s)) > 0
+    assert bsa.lib.bsa_status_string(-99) == b"unknown status"
+    assert b"gfx950" in bsa.lib.bsa_version()
+
+
+def test_sampling_offset_matches_oracle(bsa):
+    from oracle.splitmix import sampling_offset
+    for seed in (0, 1, 12345, 2**64 - 1):
+        for row in (0, 1, 2, 99, 23639, 10**9):
+            assert bsa.bsa_sampling_offset(seed, row) == sampling_offset(seed, row)
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced
+
+
+def _attn(bsa, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=1, Nq=256, Nk=256, d=128, qb=128, kvb=4, idx=FAKE,
+             bias=None, count=FAKE, L=8, scale=0.0, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return bsa.lib.bsa_attn_fwd(a["q"], a["k"], a["v"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                a["qb"], a["kvb"], a["idx"], a["bias"], a["count"], a["L"],
+                                a["scale"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(idx=None), -1), (dict(out=None), -1), (dict(count=None), -1),
+    (dict(B=0), -1), (dict(Nq=0), -1), (dict(Nk=-3), -1), (dict(L=0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(d=96), -2), (dict(d=256), -2), (dict(qb=64), -2), (dict(kvb=3), -2), (dict(kvb=256), -2),
+    (dict(q=FAKE + 8), -4), (dict(out=FAKE + 2), -4), (dict(idx=FAKE + 2), -4),
+    (dict(H=2**20, Nq=2**20 * 4), -7), (dict(L=2**28, kvb=128), -7),
+])
+def test_attn_fwd_rejects_invalid_arguments(bsa, kw, status):
+    assert _attn(bsa, **kw) == status
+
+
+def _plan(bsa, **kw):
+    a = dict(S=FAKE, B=1, H=1, nqb=4, M=100, s=10, mode=0, seed=0, off=None, idx=FAKE, bias=FAKE,
+             count=FAKE, lam=None, stream=None)
+    a.update(kw)
+    return bsa.lib.bsa_sip_plan(a["S"], a["B"], a["H"], a["nqb"], a["M"], a["s"], a["mode"],
+                                a["seed"], a["off"], a["idx"], a["bias"], a["count"], a["lam"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), -1), (dict(idx=None), -1), (dict(count=None), -1), (dict(M=0), -1),
+    (dict(mode=2), -1), (dict(s=0), -3), (dict(s=101), -3), (dict(S=FAKE + 4), -4),
+    (dict(lam=FAKE + 4), -4), (dict(M=(1 << 20) + 1, s=5), -7),
+])
+def test_sip_plan_rejects_invalid_arguments(bsa, kw, status):
+    assert _plan(bsa, **kw) == status
+
+
+def test_select_rejects_invalid_arguments(bsa):
+    L = bsa.lib
+    n = ctypes.c_size_t(0)
+    assert L.bsa_select_workspace_bytes(1, 1, 256, 128, 128, 4, 8, None) == -1
+    assert L.bsa_select_workspace_bytes(1, 1, 256, 96, 128, 4, 8, ctypes.byref(n)) == -2
+    assert L.bsa_select_workspace_bytes(1, 1, 256, 128, 128, 4, 17, ctypes.byref(n)) == -2
+    assert L.bsa_select_workspace_bytes(1, 1, 256, 128, 128, 4, 8, ctypes.byref(n)) == 0
+    base = (FAKE, FAKE, 1, 1, 256, 128, 128, 4, 8, 1, FAKE, None, None, FAKE, 1 << 30, None)
+
+    def call(i, val):
+        a = list(base)
+        a[i] = val
+        return L.bsa_select_scores(*a)
+    assert call(0, None) == -1
+    assert call(10, None) == -1
+    assert call(9, -1) == -1
+    assert call(8, 0) == -2
+    assert call(5, 32) == -2
+    assert call(0, FAKE + 2) == -4
+    assert call(13, None) == -6
+    assert call(14, 0) == -6
+    assert call(13, FAKE + 16) == -4
+
+
+def test_basa_layout_of_the_1664x960_grid(bsa):
+    lay = bsa.bsa_basa_layout(21, 60, 104, 128, 10, 10, 4, 4, 2, 4, 1, 12)
+    assert lay["nwin"] == 66
+    assert lay["Nq_pad"] == 135936          # 60 windows of 2176 rows + 6 of 896
+    assert lay["Nk_valid"] == 135936 + 8190
+    assert lay["Nk_alloc"] == 135936 + 8192
+    assert lay["max_blocks"] == 3 * 525 + 2048
+
+
+def test_basa_rejects_invalid_arguments(bsa):
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_basa_layout(21, 60, 104, 96, 10, 10, 4, 4, 2)
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_basa_layout(21, 60, 104, 128, 70, 10, 4, 4, 2)
+    with pytest.raises(bsa.BsaError):   # 3-token kv blocks are not powers of two
+        bsa.bsa_basa_layout(21, 60, 104, 128, 10, 10, 4, 4, 2, kv_block=3)

@@ -1,0 +1,155 @@
+"""GPU parity of bsa_attn_fwd against the fp64 oracle (plain masked, shifted
+softmax over the gathered keys), on plans built by the oracle so that this
+check does not depend on the selector or the planner."""
+import numpy as np
+import pytest
+
+from oracle import attn as oat
+from oracle import plan as opl
+from oracle import select as osel
+from synth import CONFIGS, bf16_bits_to_f64, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_mean_amd as bsa
+    from tests import _gpu
+    return bsa, _gpu, torch
+
+
+def _random_plan(nqb, M, s, mode, seed, zeros=0):
+    rng = np.random.default_rng(seed)
+    S = rng.gamma(0.4, size=(nqb, M))
+    if zeros:
+        S[:, rng.integers(0, M, zeros)] = 0.0
+    S /= S.sum(axis=1, keepdims=True)
+    return opl.plan(S, s, mode, seed=seed)
+
+
+def _run(env, qb, kb, vb, kvb, idx, bias, cnt, Nq=None, want_lse=True):
+    bsa, g, torch = env
+    q, k, v = g.to_dev_bf16(qb), g.to_dev_bf16(kb), g.to_dev_bf16(vb)
+    B, H, _, d = q.shape
+    nqb = idx.shape[2]
+    out, lse = bsa.bsa_attn_fwd(q, k, v, g.dev_i32(idx), None if bias is None else g.dev_f32(bias),
+                                g.dev_i32(cnt), 128, kvb, want_lse=want_lse)
+    torch.cuda.synchronize()
+    return g.from_dev_bf16(out), (lse.cpu().numpy() if lse is not None else None)
+
+
+@pytest.mark.parametrize("N,d,kvb,mode", [
+    (128, 64, 4, opl.SIP), (256, 128, 1, opl.SIP), (512, 128, 16, opl.TOPK),
+    (1000, 128, 4, opl.SIP), (1000, 64, 64, opl.TOPK), (640, 128, 128, opl.SIP),
+    (896, 128, 2, opl.SIP), (384, 64, 8, opl.SIP),
+])
+def test_attn_matches_oracle_fuzz(env, N, d, kvb, mode):
+    bsa, g, torch = env
+    g.say(f"case attn fuzz N={N} d={d} kv_block={kvb} mode={mode}")
+    qb, kb, vb = make_qkv(1, 1, N, 2, d, seed=N + d + kvb)
+    M = -(-N // kvb)
+    nqb = -(-N // 128)
+    s = max(1, M // 5)
+    idx = np.zeros((1, 2, nqb, s), np.int32)
+    bias = np.zeros((1, 2, nqb, s), np.float32)
+    cnt = np.zeros((1, 2, nqb), np.int32)
+    for h in range(2):
+        i_, b_, c_, _ = _random_plan(nqb, M, s, mode, seed=h + N)
+        idx[0, h], bias[0, h], cnt[0, h] = i_, b_, c_
+    O, lse = _run(env, qb, kb, vb, kvb, idx, bias, cnt)
+    for h in range(2):
+        q, k, v = (bf16_bits_to_f64(x[0, h]) for x in (qb, kb, vb))
+        ref, rlse = oat.attn_fwd(q, k, v, 128, kvb, idx[0, h], bias[0, h], cnt[0, h])
+        g.assert_attn_close(O[0, h], ref, f"head {h}")
+        np.testing.assert_allclose(lse[0, h], rlse, rtol=0, atol=2e-3)
+
+
+def test_attn_tiny_topk_config(env):
+    """Tiny grid 2x32x32, d = 64, KV block 64, mean-pooled scores (one
+    cluster), top-8 per query block, pi = 1; every query row checked."""
+    bsa, g, torch = env
+    c = CONFIGS["tiny_2x32x32"]
+    g.say("case attn tiny 2x32x32 top-8")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
+    S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, c["kv_block"], 1, 1)
+    idx, bias, cnt, _ = opl.plan(S, c["budget"], opl.TOPK)
+    O, _ = _run(env, qb, kb, vb, c["kv_block"], idx[None, None], None, cnt[None, None])
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    ref, _ = oat.attn_fwd(q, k, v, 128, c["kv_block"], idx, None, cnt)
+    g.assert_attn_close(O[0, 0], ref, "tiny")
+
+
+def test_attn_all_blocks_equals_dense(env):
+    bsa, g, torch = env
+    g.say("case attn dense equivalence N=768 d=128")
+    qb, kb, vb = make_qkv(1, 24, 32, 1, 128, seed=3)
+    N = 768
+    M = N // 4
+    idx = np.tile(np.arange(M, dtype=np.int32), (1, 1, 6, 1))
+    cnt = np.full((1, 1, 6), M, np.int32)
+    O, _ = _run(env, qb, kb, vb, 4, idx, None, cnt)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    ref, _ = oat.dense_attn(q, k, v)
+    g.assert_attn_close(O[0, 0], ref, "dense")
+
+
+def test_attn_edge_rows(env):
+    """count 0 -> zeros and lse -inf; out-of-range indices are skipped;
+    entries beyond count are ignored; Nk smaller than Nq."""
+    bsa, g, torch = env
+    g.say("case attn edge rows")
+    qb, kb, vb = make_qkv(1, 1, 384, 1, 64, seed=5)
+    kb2, vb2 = kb[:, :, :130], vb[:, :, :130]           # Nk = 130: last 4-block has 2 rows
+    M = 33
+    idx = np.full((1, 1, 3, 12), 7, np.int32)
+    cnt = np.array([[[0, 12, 9]]], np.int32)
+    idx[0, 0, 1] = [0, 5, -1, 32, 40, 2, 3, 1000, 4, 6, 8, 9]
+    idx[0, 0, 2, :9] = [32, 31, 30, 0, 1, 2, 3, 4, 5]
+    bias = np.random.default_rng(0).random((1, 1, 3, 12)).astype(np.float32)
+    O, lse = _run(env, qb, kb2, vb2, 4, idx, bias, cnt)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb2, vb2))
+    assert np.all(O[0, 0, :128] == 0) and np.all(np.isneginf(lse[0, 0, :128]))
+    keep = np.array([0, 5, 32, 2, 3, 4, 6, 8, 9])
+    b1 = bias[0, 0, 1][[0, 1, 3, 5, 6, 8, 9, 10, 11]]
+    ref1, _ = oat.attn_fwd(q[128:256], k, v, 128, 4, keep[None], b1[None], [9])
+    g.assert_attn_close(O[0, 0, 128:256], ref1, "row with invalid indices")
+    ref2, _ = oat.attn_fwd(q[256:], k, v, 128, 4, idx[0, 0, 2][None], bias[0, 0, 2][None], [9])
+    g.assert_attn_close(O[0, 0, 256:], ref2, "row with partial block")
+
+
+def test_attn_deterministic(env):
+    bsa, g, torch = env
+    g.say("case attn determinism")
+    qb, kb, vb = make_qkv(1, 8, 128, 2, 128, seed=9)
+    N = 1024
+    i_, b_, c_, _ = _random_plan(8, N // 4, 50, opl.SIP, seed=1)
+    idx = np.stack([i_, i_])[None]
+    bias = np.stack([b_, b_])[None]
+    cnt = np.stack([c_, c_])[None]
+    O1, l1 = _run(env, qb, kb, vb, 4, idx, bias, cnt)
+    O2, l2 = _run(env, qb, kb, vb, 4, idx, bias, cnt)
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+def test_attn_wan13b_head_full_size(env):
+    """One head of the Wan2.1-1.3B 480p shape (32,760 tokens, KV block 4,
+    budget 887) with the oracle's own SIP plan; 24 sampled query blocks
+    including the 120-row last block."""
+    bsa, g, torch = env
+    c = CONFIGS["wan13b_480p"]
+    g.say("case attn wan13b one head full size")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
+    S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, 4, 8, 1)
+    idx, bias, cnt, _ = opl.plan(S, c["budget"], opl.SIP, seed=0)
+    O, _ = _run(env, qb, kb, vb, 4, idx[None, None], bias[None, None], cnt[None, None],
+                want_lse=False)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    rng = np.random.default_rng(0)
+    blocks = sorted(set(rng.choice(255, 23, replace=False).tolist()) | {255})
+    ref, _ = oat.attn_fwd(q, k, v, 128, 4, idx, bias, cnt, blocks=blocks)
+    rows = np.concatenate([np.arange(i * 128, min(q.shape[0], i * 128 + 128)) for i in blocks])
+    g.assert_attn_close(O[0, 0][rows], ref[rows], "wan13b sampled blocks")
