@@ -1,0 +1,141 @@
+"""GPU parity of bsa_sip_plan against the oracle: indices and counts bit-exact,
+lambda bitwise, bias within 2 fp32 ulp, on the same fp32 scores and the same
+offsets (seeded or explicit)."""
+import numpy as np
+import pytest
+
+from oracle import plan as opl
+from oracle import select as osel
+from oracle.splitmix import OFFSET_LIMIT
+from synth import CONFIGS, make_qkv, random_offsets
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_mean_amd as bsa
+    from tests import _gpu
+    return bsa, _gpu, torch
+
+
+def _rows(rng, n, M, zeros=0, ties=0):
+    S = rng.gamma(0.3, size=(n, M))
+    for r in range(n):
+        if ties:
+            S[r, rng.integers(0, M, ties)] = S[r, rng.integers(0, M)]
+        if zeros:
+            S[r, rng.integers(0, M, zeros)] = 0.0
+    S /= S.sum(axis=1, keepdims=True)
+    return S.astype(np.float32)
+
+
+def _gpu_plan(env, S32, budget, mode, seed=0, offsets=None):
+    bsa, g, torch = env
+    t = torch.from_numpy(np.ascontiguousarray(S32)).cuda()
+    off = None if offsets is None else torch.from_numpy(offsets.astype(np.int64)).cuda()
+    idx, bias, cnt, lam = bsa.bsa_sip_plan(t, budget, mode, seed=seed, offsets=off,
+                                           want_lambda=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), bias.cpu().numpy(), cnt.cpu().numpy(), lam.cpu().numpy()
+
+
+def _compare(S32, got, want, what):
+    gi, gb, gc, gl = got
+    wi, wb, wc, wl = want
+    bad = np.flatnonzero((gi != wi).any(axis=-1).ravel() | (gc != wc).ravel())
+    assert bad.size == 0, f"{what}: {bad.size} rows differ, first {bad[:5]}"
+    assert np.array_equal(gl.view(np.int64), wl.view(np.int64)) or \
+        np.array_equal(gl, wl), f"{what}: lambda differs"
+    ulp = np.abs(gb.view(np.int32).astype(np.int64) - wb.view(np.int32).astype(np.int64))
+    close = (ulp <= 2) | (np.abs(gb) + np.abs(wb) == 0)
+    assert close.all(), f"{what}: bias off by {ulp.max()} ulp"
+
+
+@pytest.mark.parametrize("M,s,mode", [
+    (32, 8, opl.TOPK), (100, 7, opl.SIP), (1000, 100, opl.SIP), (1000, 100, opl.TOPK),
+    (8190, 887, opl.SIP), (18900, 2048, opl.SIP), (29700, 2272, opl.SIP),
+    (29700, 2272, opl.TOPK), (5000, 4990, opl.SIP), (333, 1, opl.SIP),
+])
+def test_plan_matches_oracle_random_rows(env, M, s, mode):
+    bsa, g, torch = env
+    g.say(f"case plan random M={M} s={s} mode={mode}")
+    rng = np.random.default_rng(M + s + mode)
+    S = _rows(rng, 24, M, zeros=M // 50, ties=M // 40).reshape(1, 2, 12, M)
+    got = _gpu_plan(env, S, s, mode, seed=123)
+    want = opl.plan(S, s, mode, seed=123)
+    _compare(S, got, want, f"M={M} s={s}")
+
+
+def test_plan_explicit_offsets(env):
+    bsa, g, torch = env
+    g.say("case plan explicit offsets")
+    rng = np.random.default_rng(5)
+    S = _rows(rng, 16, 2000, zeros=10).reshape(1, 1, 16, 2000)
+    off = random_offsets(3, 16)
+    off[0], off[1] = 0, OFFSET_LIMIT - 1
+    got = _gpu_plan(env, S, 300, opl.SIP, offsets=off)
+    want = opl.plan(S, 300, opl.SIP, offsets=off)
+    _compare(S, got, want, "explicit offsets")
+
+
+def test_plan_exact_ties_and_special_rows(env):
+    """Rows whose saturation test holds with equality (the exact-sum path),
+    equal scores, budget >= positives, all-zero and invalid rows."""
+    bsa, g, torch = env
+    g.say("case plan special rows")
+    M = 66
+    rows = []
+    a, y = 2.0 ** -5, 2.0 ** -10
+    r0 = np.array([a, a] + [y] * 64)                 # 4a = 2a + 64y: equality at r = 0
+    rows.append(r0)
+    r1 = np.zeros(M); r1[:64] = 1 / 64               # equal scores
+    rows.append(r1)
+    r2 = np.zeros(M); r2[[3, 9, 10]] = [0.5, 0.25, 0.25]   # 3 positives < budget
+    rows.append(r2)
+    r3 = np.array([3 * a, a, a] + [y] * 63)          # mixed with an exact boundary
+    rows.append(r3)
+    S = np.stack(rows).astype(np.float32).reshape(1, 1, 4, M)
+    got = _gpu_plan(env, S, 4, opl.SIP, seed=9)
+    want = opl.plan(S, 4, opl.SIP, seed=9)
+    _compare(S, got, want, "special rows")
+    assert got[2][0, 0, 2] == 3 and np.isinf(got[3][0, 0, 2])
+    zero = np.zeros((1, 1, 1, 40), np.float32)
+    got = _gpu_plan(env, zero, 5, opl.TOPK)
+    assert list(got[0][0, 0, 0]) == [0, 1, 2, 3, 4]
+    bad = np.ones((1, 1, 3, 40), np.float32)
+    bad[0, 0, 0, 7] = np.nan
+    bad[0, 0, 1, 3] = -1.0
+    bad[0, 0, 2, 0] = np.inf
+    for mode in (opl.SIP, opl.TOPK):
+        gi, gb, gc, gl = _gpu_plan(env, bad, 5, mode)
+        assert np.all(gc == -1) and np.all(gi == -1)
+
+
+def test_plan_on_selector_scores_full_rows(env):
+    """Rows of real selector output (oracle scores of one Wan2.1-14B 720p
+    head, rounded to fp32): 48 rows of M = 18,900 at budget 2048."""
+    bsa, g, torch = env
+    c = CONFIGS["wan14b_720p"]
+    g.say("case plan on selector scores wan14b")
+    qb, kb, _ = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
+    S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, 4, 8, 1)
+    rows = np.r_[0:24, 567:591]
+    S32 = S[rows].astype(np.float32)[None, None]
+    got = _gpu_plan(env, S32, 2048, opl.SIP, seed=0)
+    want = opl.plan(S32, 2048, opl.SIP, seed=0)
+    _compare(S32, got, want, "selector rows")
+    assert np.all(got[2] == 2048)
+
+
+def test_plan_deterministic(env):
+    bsa, g, torch = env
+    g.say("case plan determinism")
+    S = _rows(np.random.default_rng(1), 8, 3000).reshape(1, 1, 8, 3000)
+    a1 = _gpu_plan(env, S, 400, opl.SIP, seed=4)
+    a2 = _gpu_plan(env, S, 400, opl.SIP, seed=4)
+    for x, y in zip(a1, a2):
+        assert np.array_equal(x, y)
