@@ -41,6 +41,7 @@ constexpr long long kMaxIndex = 0x7fffffffLL;
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 bool pow2_block(int b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool clusters_ok(int c) { return c >= 1 && c <= 16 && (c & (c - 1)) == 0; }
 
 }  // namespace
 
@@ -106,8 +107,7 @@ int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_b
                                int n_clusters, size_t *bytes) {
   if (!bytes) return BSA_ERR_ARG;
   if (B < 1 || H < 1 || N < 1) return BSA_ERR_ARG;
-  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || n_clusters < 1 ||
-      n_clusters > 16)
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || !clusters_ok(n_clusters))
     return BSA_ERR_UNSUPPORTED;
   *bytes = bsa::select_workspace_bytes(B, H, N, d, kv_block, n_clusters);
   return BSA_OK;
@@ -119,8 +119,7 @@ int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d, 
                       void *stream) {
   if (!q || !k || !scores) return BSA_ERR_ARG;
   if (B < 1 || H < 1 || N < 1 || kmeans_iters < 0 || kmeans_iters > 16) return BSA_ERR_ARG;
-  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || n_clusters < 1 ||
-      n_clusters > 16)
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block) || !clusters_ok(n_clusters))
     return BSA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 16) ||
       (centroids && !aligned(centroids, 16)) || (weights && !aligned(weights, 4)))

@@ -96,7 +96,7 @@ const char *bsa_version(void);
  * weights     optional out (NULL = not written): [B,H,nQB,C] fp32.
  * workspace   device scratch of at least bsa_select_workspace_bytes() bytes,
  *             256-byte aligned; its contents are undefined after the call.
- * n_clusters  1..16; kmeans_iters 0..16 (0 = segment means).
+ * n_clusters  1, 2, 4, 8 or 16; kmeans_iters 0..16 (0 = segment means).
  * --------------------------------------------------------------------- */
 int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_block,
                                int n_clusters, size_t *bytes /* host out */);
