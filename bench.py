@@ -1,0 +1,248 @@
+"""Benchmark of the block-sparse attention forward hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input already resident
+in HBM: bsa_select_scores (pooling, k-means, block scores) -> bsa_sip_plan
+(SIP, budget 2048) -> bsa_attn_fwd, at the Wan2.1-14B 720p / 81-frame latent
+shape (21 x 45 x 80 = 75,600 tokens, 40 heads, d = 128, KV block 4, 89.16 %
+sparse).
+
+Prints ONE JSON line.  ``value`` is the effective attention throughput of the
+whole step: 4 d x (valid query, selected valid key) pairs / step time.  The
+attention kernel alone, the selector and the planner are reported beside it,
+with the roofline of the attention kernel (timed with HIP events on the
+stream it runs on) and the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published spec
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan14b_720p_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_mean_amd", "csrc", "attn_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="wan14b_720p")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-heads", type=int, default=3,
+                   help="whole heads of the workload in the oracle sample")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="after timing, run one device copy of this size (counter calibration)")
+    return p.parse_args()
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per attention launch from committed counter runs, if they
+    were taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, seed, heads):
+    """The oracle (as it stands) on whole heads 0..heads-1 of the workload:
+    pooling, k-means, scores, SIP plan and attention of every query block.
+    Returns effective TFLOP/s (same definition as the GPU value)."""
+    import numpy as np
+    from oracle import attn as oat
+    from oracle import plan as opl
+    from oracle import select as osel
+    from synth import bf16_bits_to_f32, bf16_bits_to_f64, head_qkv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    st = {"select": 0.0, "plan": 0.0, "attn": 0.0}
+    flops = 0.0
+    for h in range(heads):
+        qb, kb, vb = head_qkv(c["T"], c["Hg"], c["Wg"], c["d"], seed, h)
+        q32 = bf16_bits_to_f32(qb)
+        q, k, v = bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb)
+        N, d, kvb, s = q.shape[0], c["d"], c["kv_block"], c["budget"]
+        nqb = -(-N // 128)
+        t0 = time.perf_counter()
+        kbar = osel.pool_keys(k, kvb)
+        mu, w = osel.kmeans_head(q32, 128, c["n_clusters"], c["kmeans_iters"])
+        S = osel.scores_from_centroids(mu, w, kbar)
+        t1 = time.perf_counter()
+        idx, bias, cnt, _ = opl.plan(S, s, opl.SIP, seed=seed, row_base=h * nqb)
+        t2 = time.perf_counter()
+        oat.attn_fwd(q, k, v, 128, kvb, idx, bias, cnt)
+        t3 = time.perf_counter()
+        st["select"] += t1 - t0
+        st["plan"] += t2 - t1
+        st["attn"] += t3 - t2
+        flops += sum(4.0 * d * min(128, N - 128 * i) * int(cnt[i]) * kvb for i in range(nqb))
+    total = sum(st.values())
+    return {
+        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"heads 0..{heads - 1} of {c['name']} (all query blocks): pooling, k-means, "
+                   f"scores, SIP plan and attention, fp64 numpy (k-means in its stated fp32 order)"),
+        "seconds": round(total, 3),
+        "stage_seconds": {k2: round(v2, 3) for k2, v2 in st.items()},
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is built and "
+              "measured on a single MI355X; heads shard across GPUs with no communication.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    from synth import CONFIGS, make_qkv
+
+    c = dict(CONFIGS[args.workload])
+    c["name"] = args.workload
+    T, Hg, Wg, H, d = c["T"], c["Hg"], c["Wg"], c["H"], c["d"]
+    N, kvb, s, C = T * Hg * Wg, c["kv_block"], c["budget"], c["n_clusters"]
+    M, nqb = -(-N // kvb), -(-N // 128)
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] generating {args.workload}: H={H} N={N} d={d}")
+    t0 = time.time()
+    qb, kb, vb = make_qkv(T, Hg, Wg, H, d, seed=args.seed, workers=min(16, os.cpu_count() or 1))
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f}s")
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    del qb, kb, vb
+
+    ws_bytes = bsa.bsa_select_workspace_bytes(1, H, N, d, 128, kvb, C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scores = torch.empty((1, H, nqb, M), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, H, nqb, s), dtype=torch.int32, device=dev)
+    bias = torch.empty((1, H, nqb, s), dtype=torch.float32, device=dev)
+    cnt = torch.empty((1, H, nqb), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"], scores=scores, workspace=ws)
+        if marks is not None:
+            marks[1].record(stream)
+        bsa.bsa_sip_plan(scores, s, bsa.PLAN_SIP, seed=args.seed, idx=idx, bias=bias, count=cnt)
+        if marks is not None:
+            marks[2].record(stream)
+        bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
+        if marks is not None:
+            marks[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = g0.elapsed_time(g1) / args.steps
+    sel = [m[0].elapsed_time(m[1]) for m in marks]
+    pln = [m[1].elapsed_time(m[2]) for m in marks]
+    att = [m[2].elapsed_time(m[3]) for m in marks]
+
+    # algorithmic attention work of this plan (valid queries x selected valid keys)
+    cnt_h = cnt.cpu().numpy().astype(np.int64)
+    if (cnt_h != s).any():
+        raise SystemExit(f"plan check failed: counts {np.unique(cnt_h)}")
+    rows = np.minimum(128, N - 128 * np.arange(nqb))
+    # every drawn block is a full 4-token block except a block past N (none for these shapes)
+    flops = 4.0 * d * float((cnt_h[0] * kvb * rows[None, :]).sum())
+    if not torch.isfinite(out.float()).all():
+        raise SystemExit("non-finite attention output")
+    attn_ms = float(np.mean(att))
+    attn_tf = flops / attn_ms / 1e9
+    value = flops / ms_step / 1e9
+    traffic = traffic_for_current_kernel()
+    gathered = float(cnt_h.sum() * kvb * d * 2 * 2)
+    rec = {
+        "metric": "block-sparse attn ms/call + effective TFLOP/s at Wan-14B 720p shape, 89% sparse",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
+                        f"query block 128, KV block {kvb}, {C} clusters / {c['kmeans_iters']} "
+                        f"k-means iteration, SIP budget {s} of {M} blocks",
+            "B": 1, "H": H, "N": N, "d": d, "kv_block": kvb, "budget": s,
+            "sparsity": round(1 - s / M, 5), "seed": args.seed,
+            "step": "bsa_select_scores + bsa_sip_plan + bsa_attn_fwd",
+        },
+        "attn_ms_per_call": round(attn_ms, 4),
+        "attn_tflops": round(attn_tf, 2),
+        "select_ms": round(float(np.mean(sel)), 4),
+        "plan_ms": round(float(np.mean(pln)), 4),
+        "attn_flop_per_call": flops,
+        "roofline": {
+            "kernel": "bsa::attn_fwd_kernel<128>",
+            "bound": "mfma",
+            "achieved": round(attn_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "gathered_bytes_per_launch": gathered,
+        },
+    }
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calib_bytes"] = n
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(c, args.seed, args.cpu_sample_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

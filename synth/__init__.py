@@ -110,18 +110,32 @@ def head_qkv(T: int, Hg: int, Wg: int, d: int, seed: int, h: int, phi=None):
     return q, k, v
 
 
-def make_qkv(T: int, Hg: int, Wg: int, H: int, d: int, seed: int = 0, B: int = 1):
+def _head_job(args):
+    T, Hg, Wg, d, seed, h = args
+    return head_qkv(T, Hg, Wg, d, seed, h)
+
+
+def make_qkv(T: int, Hg: int, Wg: int, H: int, d: int, seed: int = 0, B: int = 1,
+             workers: int = 1):
     """(q, k, v) uint16 bf16 bit arrays of shape [B, H, N, d].
 
-    Batch b > 0 uses seed ``seed + 1000 * b`` so that batches differ.
+    Batch b > 0 uses seed ``seed + 1000 * b`` so that batches differ.  With
+    ``workers > 1`` heads are drawn in parallel processes (same values: every
+    head has its own generator).
     """
     N = T * Hg * Wg
-    phi = positional_features(T, Hg, Wg)
     out = [np.empty((B, H, N, d), dtype=np.uint16) for _ in range(3)]
-    for b in range(B):
-        for h in range(H):
-            q, k, v = head_qkv(T, Hg, Wg, d, seed + 1000 * b, h, phi)
-            out[0][b, h], out[1][b, h], out[2][b, h] = q, k, v
+    jobs = [(T, Hg, Wg, d, seed + 1000 * b, h) for b in range(B) for h in range(H)]
+    if workers > 1 and len(jobs) > 1:
+        from concurrent.futures import ProcessPoolExecutor
+        with ProcessPoolExecutor(max_workers=min(workers, len(jobs))) as ex:
+            results = list(ex.map(_head_job, jobs))
+    else:
+        phi = positional_features(T, Hg, Wg)
+        results = [head_qkv(T, Hg, Wg, d, s_, h, phi) for (_, _, _, _, s_, h) in jobs]
+    for (_, _, _, _, s_, h), (q, k, v) in zip(jobs, results):
+        b = (s_ - seed) // 1000
+        out[0][b, h], out[1][b, h], out[2][b, h] = q, k, v
     return tuple(out)
 
 
