@@ -7,21 +7,30 @@
 // and no reordered copy of the sequence in memory.  The shift itself is the
 // 1/pi weighting of section "어떻게 쓰나".
 //
-// Design (one workgroup = one 128-query block of one (b, h); 2 waves of 64
-// queries each):
-//   * Q stays in registers as the B operand of S^T = K Q^T (bf16 MFMA
-//     32x32x16), so every lane owns one query column and the row max / row
-//     sum need a single cross-half exchange;
-//   * per 64-key tile the workgroup gathers the listed blocks into LDS:
-//     K row-major [key][dim] and V transposed [dim][key], so both MFMA
-//     operands are 16-byte LDS reads; the next tile's global loads are in
-//     flight while the current tile computes;
-//   * the K rows are fed to the MFMA in a permuted order chosen so that the
-//     S^T accumulator registers of a lane hold 8 consecutive keys, which is
-//     exactly the B-operand layout of O^T = V^T P^T -- P never leaves
-//     registers;
-//   * logits are moved to base 2 once (scale * log2 e, bias * log2 e) so
-//     the softmax uses v_exp_f32 directly.
+// Design (one workgroup = one 128-query block of one (b, h), 8 waves):
+//   * wave w owns queries 32 (w & 3) .. +32 and the key half 32 (w >> 2) .. +32
+//     of every 64-key tile; each wave keeps its own online softmax and the
+//     two key halves are merged once at the end (no per-tile cross-wave
+//     traffic besides the shared tiles); two waves per SIMD let one wave's
+//     softmax overlap the other's matrix work;
+//   * the block list and shifts of the query block are staged in LDS, so
+//     gather addresses never wait on global memory;
+//   * listed blocks are gathered with direct global->LDS 16-byte loads into
+//     a ring of three 64-key K/V tiles (two tiles in flight while one is
+//     consumed); K and V stay row-major with 16-byte-chunk XOR swizzles
+//     (bank-conflict free for their MFMA operand reads) realised by each
+//     lane's choice of source address;
+//   * S^T = K Q^T (bf16 MFMA 32x32x16; Q stays in registers as the B
+//     operand), with the K rows fed in a permuted order so that each lane's
+//     accumulators hold 8 consecutive keys of one query -- exactly the
+//     B-operand layout of O^T = V^T P^T; the V^T operand comes from the
+//     row-major V tile through the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16); P never leaves registers;
+//   * base-2 softmax (scale and shift pre-multiplied by log2 e) with a
+//     lazy reference maximum: O and the row sum are rescaled only when a
+//     tile raises some row's maximum by more than 8 (a wave-uniform test).
+#include <type_traits>
+
 #include "common.h"
 
 namespace bsa {
@@ -38,244 +47,321 @@ struct AttnArgs {
   float scale_log2;
 };
 
-// MFMA A-row -> key within a 32-key sub-tile (see the file comment).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA A-row -> key within a 32-key sub-tile, chosen so that accumulator
+// register r of lane half h holds key 16 (r >> 3) + 8 h + (r & 7).
 __device__ __forceinline__ int key_of_row(int i) {
   return ((i >> 4) << 4) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KT = 64;            // keys per tile
-  constexpr int NCH = D / 8;        // 16-byte chunks per row
-  constexpr int KSTR = D + 8;       // K row stride (bf16 elements)
-  constexpr int VSTR = KT + 8;      // V^T row stride
-  constexpr int ITEMS = (KT / 4) * NCH;
-  constexpr int IPT = ITEMS / 128;  // gather items per thread
-  constexpr int DS = D / 16;        // k-steps of QK^T
-  constexpr int DT = D / 32;        // dim tiles of O^T
+// Workgroup barrier for the gather ring: this wave's gathers older than the
+// newest N vector-memory ops and all its LDS writes are complete, then
+// s_barrier.  The compiler-only fences keep LDS accesses from moving across
+// it; no release fence is used because that would also wait for the gathers
+// still in flight into other ring slots.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTR];
-  __shared__ __attribute__((aligned(16))) float bias_lds[KT];
+// 16-byte-chunk XOR swizzles of the row-major K and V tiles, chosen so
+// that the MFMA operand reads are free of LDS bank conflicts: K is read as
+// 16 rows x one chunk per 16 lanes, V (transposing read) as 4 consecutive
+// rows x 4 consecutive chunks per 32 lanes.  256-byte rows (d = 128) fill
+// the 64 banks; 128-byte rows (d = 64) pair up.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int NW = 8;              // waves: 4 query quarters x 2 key halves
+  constexpr int KT = 64;             // keys per tile
+  constexpr int NCH = D / 8;         // 16-byte chunks per row
+  constexpr int ROWB = D * 2;        // row bytes
+  constexpr int TILEB = KT * ROWB;   // bytes of one K (or V) tile
+  constexpr int RPI = 64 / NCH;      // rows per 1 KB wave load
+  constexpr int LPW = (KT / RPI) / NW;  // wave loads per operand per tile
+  constexpr int RPW = KT / NW;       // tile rows gathered by one wave
+  constexpr int LPT = 2 * LPW;       // vector-memory ops per wave per tile
+  constexpr int DS = D / 16;         // k-steps of QK^T
+  constexpr int DT = D / 32;         // dim tiles of O^T
+  constexpr int CAP = 4096;          // list entries staged per phase
+  static_assert(LPW >= 1, "tile too small for the gather split");
+
+  // Ring of three K/V tiles.  Separate arrays let the compiler see that a
+  // gather into one slot never aliases the reads of another, so it does not
+  // wait for in-flight gathers before reading the current slot.
+  __shared__ __attribute__((aligned(16))) unsigned char k0[TILEB], v0[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k1[TILEB], v1[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k2[TILEB], v2[TILEB];
+  __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
+  __shared__ __attribute__((aligned(16))) float bias_s[CAP];
+  __shared__ __attribute__((aligned(16))) float bring[3 * KT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
+  const int qq = wave & 3, kh = wave >> 2;
 
-  const int wg = blockIdx.x;
+  // XCD-aware order: the hardware deals workgroups round-robin over 8
+  // XCDs; give each XCD a contiguous run of query blocks.
+  int wg = blockIdx.x;
+  {
+    const int per = 8 * 32;
+    const int full = (a.total_wg / per) * per;
+    if (wg < full) {
+      const int r = wg / per, u = wg % per;
+      wg = r * per + (u & 7) * 32 + (u >> 3);
+    }
+  }
   const int qb = wg % a.nqb;
   const int bh = wg / a.nqb;
   const size_t row_id = (size_t)bh * a.nqb + qb;
   const uint16_t *qbase = a.q + (size_t)bh * a.Nq * D;
-  const uint16_t *kbase = a.k + (size_t)bh * a.Nk * D;
-  const uint16_t *vbase = a.v + (size_t)bh * a.Nk * D;
+  const unsigned char *kbase = (const unsigned char *)(a.k + (size_t)bh * a.Nk * D);
+  const unsigned char *vbase = (const unsigned char *)(a.v + (size_t)bh * a.Nk * D);
   const int32_t *idx_row = a.idx + row_id * a.max_blocks;
   const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
   int cnt = a.count[row_id];
   cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
   const int kvb = 1 << a.kv_shift;
-  const int nkeys = cnt << a.kv_shift;
-  const int ntiles = (nkeys + KT - 1) / KT;
 
-  // ---- Q fragments (B operand): lane holds query column l32, 8 dims.
-  bf16x8 qf[2][DS];
-#pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const int row = qb * 128 + wave * 64 + qs * 32 + l32;
+  // ---- Q fragments (B operand of S^T): query column l32, dims 16 ds + 8 hh ..
+  bf16x8 qf[DS];
+  {
+    const int row = qb * 128 + qq * 32 + l32;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row < a.Nq) v = ld16(qbase + (size_t)row * D + ds * 16 + hh * 8);
-      qf[qs][ds] = as_bf16x8(v);
+      qf[ds] = as_bf16x8(v);
     }
   }
 
-  // ---- gather staging registers
-  u32x4 kreg[IPT][4], vreg[IPT][4];
-  float breg = 0.f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
 
-  auto resolve = [&](int pos) -> int {
-    if (pos >= nkeys) return -1;
-    const int e = pos >> a.kv_shift;
-    const int blk = idx_row[e];
-    if (blk < 0 || blk >= a.M) return -1;
-    const int key = (blk << a.kv_shift) + (pos & (kvb - 1));
-    return key < a.Nk ? key : -1;
+  int nkeys = 0, ntiles = 0;
+
+  // Per-lane constants of the gather: tile row of load j and the swizzled
+  // source chunk offsets of that row in K and V.
+  int g_row[LPW], g_koff[LPW], g_voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = wave * RPW + j * RPI + lane / NCH;
+    const int cl = lane % NCH;
+    g_row[j] = r;
+    g_koff[j] = (cl ^ swz_k<D>(r)) << 4;
+    g_voff[j] = (cl ^ swz_v<D>(r)) << 4;
+  }
+
+  // Gather tile t into slot S: this wave loads rows [RPW w, RPW w + RPW).
+  // Keys outside the list or the tensors load row 0 and get a -inf shift.
+  auto issue = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    unsigned char *kt = S == 0 ? k0 : (S == 1 ? k1 : k2);
+    unsigned char *vt = S == 0 ? v0 : (S == 1 ? v1 : v2);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int r = g_row[j];
+      const int pos = t * KT + r;
+      const bool inl = pos < nkeys;
+      const int e = inl ? (pos >> a.kv_shift) : 0;
+      const int blk = idx_s[e];
+      const int kk = (blk << a.kv_shift) + (pos & (kvb - 1));
+      const bool ok = inl & (blk >= 0) & (blk < a.M) & (kk < a.Nk);
+      const float bv = ok ? bias_s[e] : -__builtin_inff();
+      const size_t src = (size_t)(ok ? kk : 0) * ROWB;
+      const int dst = (wave * RPW + j * RPI) * ROWB;  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const void *)(kbase + src + g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vbase + src + g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
+      if (lane % NCH == 0) bring[S * KT + r] = bv;
+    }
   };
 
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int item = tid + 128 * it;
-      const int g = item / NCH, c = item % NCH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = resolve(t * KT + 4 * g + kk);
-        u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-        if (key >= 0) {
-          zk = ld16(kbase + (size_t)key * D + c * 8);
-          zv = ld16(vbase + (size_t)key * D + c * 8);
-        }
-        kreg[it][kk] = zk;
-        vreg[it][kk] = zv;
-      }
-    }
-    if (tid < KT) {
-      const int pos = t * KT + tid;
-      const int key = resolve(pos);
-      breg = key >= 0 ? (bias_row ? bias_row[pos >> a.kv_shift] * kLog2e : 0.f)
-                      : -__builtin_inff();
-    }
-  };
+  const int krow = kh * 32 + key_of_row(l32);
+  const int gi = lane & 15;  // index inside a 16-lane group
+  const int gg = lane >> 4;  // group 0..3
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-      const int item = tid + 128 * it;
-      const int g = item / NCH, c = item % NCH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) st16(&k_lds[(4 * g + kk) * KSTR + c * 8], kreg[it][kk]);
-      // transpose 4 keys x 8 dims into V^T rows (4 consecutive keys per row)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned a0 = vreg[it][0][w], a1 = vreg[it][1][w];
-        const unsigned a2 = vreg[it][2][w], a3 = vreg[it][3][w];
-        u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *(u32x2 *)&vt_lds[(c * 8 + 2 * w) * VSTR + 4 * g] = lo;
-        *(u32x2 *)&vt_lds[(c * 8 + 2 * w + 1) * VSTR + 4 * g] = hi;
-      }
-    }
-    if (tid < KT) bias_lds[tid] = breg;
-  };
+  // One tile: wait for slot S, prefetch two tiles ahead, compute.
+  auto step = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    constexpr int SN = (S + 2) % 3;
+    const unsigned char *kt = S == 0 ? k0 : (S == 1 ? k1 : k2);
+    const unsigned char *vt = S == 0 ? v0 : (S == 1 ? v1 : v2);
+    if (t + 1 < ntiles) ring_barrier<LPT>();
+    else ring_barrier<0>();
+    if (t + 2 < ntiles) issue(std::integral_constant<int, SN>(), t + 2);
 
-  f32x16 oacc[2][DT];
+    // ---- S^T: 32 keys of this wave's half x 32 queries of its quarter
+    f32x16 sacc;
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qs][dt][r] = 0.f;
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.f, 0.f};
-
-  if (ntiles > 0) load_tile(0);
-
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-
-    // ---- S^T = K Q^T for 2 key sub-tiles x 2 query sub-tiles
-    f32x16 sacc[2][2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qs][ks][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int krow = ks * 32 + key_of_row(l32);
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 af = as_bf16x8(ld16(&k_lds[krow * KSTR + ds * 16 + hh * 8]));
-        sacc[0][ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[0][ds], sacc[0][ks], 0, 0, 0);
-        sacc[1][ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[1][ds], sacc[1][ks], 0, 0, 0);
-      }
+    for (int ds = 0; ds < DS; ++ds) {
+      const int ch = (2 * ds + hh) ^ swz_k<D>(krow);
+      const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + krow * ROWB + ch * 16));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ds], sacc, 0, 0, 0);
     }
 
-    // ---- per-key base-2 shift of this lane's keys: 32 ks + 16 (r>>3) + 8 hh + (r&7)
-    float bk[2][16];
+    // ---- base-2 logits with the per-key shift; lazy running maximum
+    const float *bt = bring + S * KT + kh * 32;
+    float mx = -__builtin_inff();
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const f32x4 b0 = *(const f32x4 *)&bt[m2 * 16 + hh * 8];
+      const f32x4 b1 = *(const f32x4 *)&bt[m2 * 16 + hh * 8 + 4];
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        const f32x4 b0 = *(const f32x4 *)&bias_lds[ks * 32 + m2 * 16 + hh * 8];
-        const f32x4 b1 = *(const f32x4 *)&bias_lds[ks * 32 + m2 * 16 + hh * 8 + 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bk[ks][m2 * 8 + e] = b0[e];
-          bk[ks][m2 * 8 + 4 + e] = b1[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        sacc[m2 * 8 + e] = __builtin_fmaf(sacc[m2 * 8 + e], a.scale_log2, b0[e]);
+        sacc[m2 * 8 + 4 + e] = __builtin_fmaf(sacc[m2 * 8 + 4 + e], a.scale_log2, b1[e]);
       }
-
-    // ---- online softmax (base 2); P^T stays in registers
-    bf16x8 pf[2][4];
+    }
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float tv = __builtin_fmaf(sacc[qs][ks][r], a.scale_log2, bk[ks][r]);
-          sacc[qs][ks][r] = tv;
-          mx = fmaxf(mx, tv);
-        }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[qs], mx);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qs] - m_use);
-      m_run[qs] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[qs][ks][r] - m_use);
-          sacc[qs][ks][r] = pv;
-          rs += pv;
-        }
-      l_run[qs] = l_run[qs] * alpha + rs;
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    const float mt = fmaxf(mx, xor32(mx));
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.f) != 0ull) {
+      const float m_new = mt > m_run + 8.f ? mt : m_run;
+      const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qs][dt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    bf16x8 pf[2];
+    {
+      const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
+      float rs = 0.f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int ks = m >> 1, r0 = 8 * (m & 1);
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[r] - mu);
+        sacc[r] = pv;
+        rs += pv;
+      }
+      l_run += rs;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2(sacc[qs][ks][r0 + 2 * e], sacc[qs][ks][r0 + 2 * e + 1]);
-        pf[qs][m] = as_bf16x8(w);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sacc[8 * m + 2 * e], sacc[8 * m + 2 * e + 1]);
+        pf[m] = as_bf16x8(w);
       }
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; V^T fragments through the transposing LDS read
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      const int n0 = dt * 32 + 16 * (gg & 1) + 4 * (gi & 3);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16x8 af = as_bf16x8(ld16(&vt_lds[(dt * 32 + l32) * VSTR + m * 16 + hh * 8]));
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[0][m], oacc[0][dt], 0, 0, 0);
-        oacc[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[1][m], oacc[1][dt], 0, 0, 0);
+      for (int m = 0; m < 2; ++m) {
+        s16x4 part[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int row = kh * 32 + 16 * m + 8 * (gg >> 1) + 4 * p + (gi >> 2);
+          const int ch = (n0 >> 3) ^ swz_v<D>(row);
+          const unsigned char *addr = vt + row * ROWB + ch * 16 + ((n0 >> 2) & 1) * 8;
+          part[p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)addr);
+        }
+        const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
+        const u32x4 w = {w0[0], w0[1], w1[0], w1[1]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[m], oacc[dt], 0, 0, 0);
       }
+    }
+  };
+
+  for (int base = 0; base < cnt; base += CAP) {
+    const int pc = min(CAP, cnt - base);
+    __syncthreads();
+    for (int e = tid; e < pc; e += NW * 64) {
+      idx_s[e] = idx_row[base + e];
+      bias_s[e] = bias_row ? bias_row[base + e] * kLog2e : 0.f;
+    }
+    __syncthreads();
+    nkeys = pc << a.kv_shift;
+    ntiles = (nkeys + KT - 1) / KT;
+    if (ntiles > 0) issue(std::integral_constant<int, 0>(), 0);
+    if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
+    for (int t = 0; t < ntiles; t += 3) {
+      step(std::integral_constant<int, 0>(), t);
+      if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
+      if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
+    }
   }
 
-  // ---- normalise and store
+  // ---- merge the two key halves of each query quarter: wave (qq, kh)
+  // finishes dim tiles [kh DT/2, (kh + 1) DT/2) and hands the others to its
+  // partner (qq, 1 - kh) through a slice of the former ring arrays.
+  __syncthreads();
+  constexpr int HT = DT / 2;                 // dim tiles handed over
+  constexpr int HSZ = HT * 16 * 64;          // floats per wave
+  auto hand = [&](int w) -> float * {
+    unsigned char *b = (w >> 1) == 0 ? k0 : ((w >> 1) == 1 ? v0 : ((w >> 1) == 2 ? k1 : v1));
+    return (float *)b + (w & 1) * HSZ;
+  };
+  float *xml = bias_s;  // [wave][m, l][64]
+  auto finish = [&](auto kh_c) {
+    constexpr int KH = decltype(kh_c)::value;
+    constexpr int OWN = KH * HT, OTH = (1 - KH) * HT;
+    float *po = hand(wave);
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const float l = l_run[qs] + xor32(l_run[qs]);
+    for (int d = 0; d < HT; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) po[(d * 16 + r) * 64 + lane] = oacc[OTH + d][r];
+    xml[(wave * 2) * 64 + lane] = m_run;
+    xml[(wave * 2 + 1) * 64 + lane] = l_run;
+    __syncthreads();
+    const int partner = wave ^ 4;
+    const float *pp = hand(partner);
+    const float m1 = xml[(partner * 2) * 64 + lane], l1 = xml[(partner * 2 + 1) * 64 + lane];
+    const float mc = fmaxf(m_run, m1);
+    const float mu = mc == -__builtin_inff() ? 0.f : mc;
+    const float f0 = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - mu);
+    const float f1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mu);
+    const float lh = l_run * f0 + l1 * f1;  // this lane half's keys
+    const float l = lh + xor32(lh);         // both lane halves
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int row = qb * 128 + wave * 64 + qs * 32 + l32;
+    const int row = qb * 128 + qq * 32 + l32;
     if (row < a.Nq) {
       uint16_t *orow = a.out + ((size_t)bh * a.Nq + row) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int d = 0; d < HT; ++d)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          u32x2 w = {pack_bf16x2(oacc[qs][dt][4 * g] * inv, oacc[qs][dt][4 * g + 1] * inv),
-                     pack_bf16x2(oacc[qs][dt][4 * g + 2] * inv, oacc[qs][dt][4 * g + 3] * inv)};
-          *(u32x2 *)&orow[dt * 32 + g * 8 + hh * 4] = w;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = (oacc[OWN + d][4 * g + e] * f0 + pp[(d * 16 + 4 * g + e) * 64 + lane] * f1) * inv;
+          u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *(u32x2 *)&orow[(OWN + d) * 32 + g * 8 + hh * 4] = w;
         }
-      if (a.lse && hh == 0)
-        a.lse[(size_t)bh * a.Nq + row] =
-            l > 0.f ? (m_run[qs] + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+      if (KH == 0 && a.lse && hh == 0)
+        a.lse[(size_t)bh * a.Nq + row] = l > 0.f ? (mu + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
     }
-  }
+  };
+  if (kh == 0) finish(std::integral_constant<int, 0>());
+  else finish(std::integral_constant<int, 1>());
 }
 
 int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int Nq, int Nk,
@@ -300,7 +386,7 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   a.scale_log2 = scale * kLog2e;
   const long long total = (long long)B * H * a.nqb;
   a.total_wg = (int)total;
-  dim3 grid((unsigned)total), block(128);
+  dim3 grid((unsigned)total), block(512);
   if (d == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, a);
   else

@@ -31,8 +31,11 @@ __device__ __forceinline__ unsigned bf16_bits(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
   return __builtin_bit_cast(float, (unsigned)b << 16);
