@@ -7,16 +7,14 @@
 // and no reordered copy of the sequence in memory.  The shift itself is the
 // 1/pi weighting of section "어떻게 쓰나".
 //
-// Design (one workgroup = one 128-query block of one (b, h), 8 waves):
-//   * wave w owns queries 32 (w & 3) .. +32 and the key half 32 (w >> 2) .. +32
-//     of every 64-key tile; each wave keeps its own online softmax and the
-//     two key halves are merged once at the end (no per-tile cross-wave
-//     traffic besides the shared tiles); two waves per SIMD let one wave's
-//     softmax overlap the other's matrix work;
+// Design (one workgroup = one 128-query block of one (b, h), 4 waves; two
+// workgroups share a CU, so a stall at one workgroup's barrier is covered
+// by the other):
+//   * wave w owns queries 32 w .. +32 and computes every key of every tile;
 //   * the block list and shifts of the query block are staged in LDS, so
 //     gather addresses never wait on global memory;
 //   * listed blocks are gathered with direct global->LDS 16-byte loads into
-//     a ring of three 64-key K/V tiles (two tiles in flight while one is
+//     a ring of four 32-key K/V tiles (tile t+3 is requested while tile t is
 //     consumed); K and V stay row-major with 16-byte-chunk XOR swizzles
 //     (bank-conflict free for their MFMA operand reads) realised by each
 //     lane's choice of source address;
@@ -26,9 +24,10 @@
 //     B-operand layout of O^T = V^T P^T; the V^T operand comes from the
 //     row-major V tile through the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16); P never leaves registers;
-//   * base-2 softmax (scale and shift pre-multiplied by log2 e) with a
-//     lazy reference maximum: O and the row sum are rescaled only when a
-//     tile raises some row's maximum by more than 8 (a wave-uniform test).
+//   * base-2 softmax (scale and shift pre-multiplied by log2 e) against a
+//     lazy reference maximum folded into the logit fma: O and the row sum
+//     are rescaled only when a tile exceeds the reference by more than 8
+//     (a wave-uniform test).
 #include <type_traits>
 
 #include "common.h"
@@ -86,46 +85,47 @@ __device__ __forceinline__ int swz_v(int r) {
 }
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int NW = 8;              // waves: 4 query quarters x 2 key halves
-  constexpr int KT = 64;             // keys per tile
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+  constexpr int NW = 4;              // waves: one 32-query quarter each
+  constexpr int KT = 32;             // keys per tile
+  constexpr int NBUF = 4;            // ring slots
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int ROWB = D * 2;        // row bytes
   constexpr int TILEB = KT * ROWB;   // bytes of one K (or V) tile
   constexpr int RPI = 64 / NCH;      // rows per 1 KB wave load
-  constexpr int LPW = (KT / RPI) / NW;  // wave loads per operand per tile
   constexpr int RPW = KT / NW;       // tile rows gathered by one wave
+  constexpr int LPW = RPW / RPI;     // wave loads per operand per tile
   constexpr int LPT = 2 * LPW;       // vector-memory ops per wave per tile
   constexpr int DS = D / 16;         // k-steps of QK^T
   constexpr int DT = D / 32;         // dim tiles of O^T
-  constexpr int CAP = 4096;          // list entries staged per phase
-  static_assert(LPW >= 1, "tile too small for the gather split");
+  constexpr int CAP = 1920;          // list entries staged per phase
+  static_assert(LPW >= 1 && RPW % RPI == 0, "tile too small for the gather split");
 
-  // Ring of three K/V tiles.  Separate arrays let the compiler see that a
-  // gather into one slot never aliases the reads of another, so it does not
-  // wait for in-flight gathers before reading the current slot.
+  // Ring of K/V tiles.  Separate arrays let the compiler see that a gather
+  // into one slot never aliases the reads of another, so it does not wait
+  // for in-flight gathers before reading the current slot.
   __shared__ __attribute__((aligned(16))) unsigned char k0[TILEB], v0[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k1[TILEB], v1[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k2[TILEB], v2[TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char k3[TILEB], v3[TILEB];
   __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
   __shared__ __attribute__((aligned(16))) float bias_s[CAP];
-  __shared__ __attribute__((aligned(16))) float bring[3 * KT];
+  __shared__ __attribute__((aligned(16))) float bring[NBUF * KT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qq = wave & 3, kh = wave >> 2;
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8
   // XCDs; give each XCD a contiguous run of query blocks.
   int wg = blockIdx.x;
   {
-    const int per = 8 * 32;
+    const int per = 8 * 64;
     const int full = (a.total_wg / per) * per;
     if (wg < full) {
       const int r = wg / per, u = wg % per;
-      wg = r * per + (u & 7) * 32 + (u >> 3);
+      wg = r * per + (u & 7) * 64 + (u >> 3);
     }
   }
   const int qb = wg % a.nqb;
@@ -141,15 +141,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const int kvb = 1 << a.kv_shift;
 
   // ---- Q fragments (B operand of S^T): query column l32, dims 16 ds + 8 hh ..
+  const int qrow = qb * 128 + wave * 32 + l32;
   bf16x8 qf[DS];
-  {
-    const int row = qb * 128 + qq * 32 + l32;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < a.Nq) v = ld16(qbase + (size_t)row * D + ds * 16 + hh * 8);
-      qf[ds] = as_bf16x8(v);
-    }
+  for (int ds = 0; ds < DS; ++ds) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qrow < a.Nq) v = ld16(qbase + (size_t)qrow * D + ds * 16 + hh * 8);
+    qf[ds] = as_bf16x8(v);
   }
 
   f32x16 oacc[DT];
@@ -157,8 +155,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -__builtin_inff();
+  float m_run = 0.f;   // reference maximum (base 2), raised lazily
   float l_run = 0.f;
+  bool fresh = true;    // no key of this query seen yet (same in both halves)
 
   int nkeys = 0, ntiles = 0;
 
@@ -174,46 +173,43 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     g_voff[j] = (cl ^ swz_v<D>(r)) << 4;
   }
 
+  auto kslot = [&](auto c) -> unsigned char * {
+    constexpr int S = decltype(c)::value;
+    return S == 0 ? k0 : (S == 1 ? k1 : (S == 2 ? k2 : k3));
+  };
+  auto vslot = [&](auto c) -> unsigned char * {
+    constexpr int S = decltype(c)::value;
+    return S == 0 ? v0 : (S == 1 ? v1 : (S == 2 ? v2 : v3));
+  };
+
   // Gather tile t into slot S: this wave loads rows [RPW w, RPW w + RPW).
-  // Keys outside the list or the tensors load row 0 and get a -inf shift.
+  // Masked keys (invalid or padded list entries, rows past Nk) load row 0
+  // and get a -inf shift.
   auto issue = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
-    unsigned char *kt = S == 0 ? k0 : (S == 1 ? k1 : k2);
-    unsigned char *vt = S == 0 ? v0 : (S == 1 ? v1 : v2);
+    unsigned char *kt = kslot(slot_c);
+    unsigned char *vt = vslot(slot_c);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int r = g_row[j];
-      const int pos = t * KT + r;
-      const bool inl = pos < nkeys;
-      const int e = inl ? (pos >> a.kv_shift) : 0;
-      const int blk = idx_s[e];
-      const int kk = (blk << a.kv_shift) + (pos & (kvb - 1));
-      const bool ok = inl & (blk >= 0) & (blk < a.M) & (kk < a.Nk);
-      const float bv = ok ? bias_s[e] : -__builtin_inff();
+      const int pos = t * KT + g_row[j];
+      const int e = pos >> a.kv_shift;  // staged entries cover whole tiles
+      const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
+      const bool ok = kk < a.Nk;        // rows past the last valid key
       const size_t src = (size_t)(ok ? kk : 0) * ROWB;
       const int dst = (wave * RPW + j * RPI) * ROWB;  // wave-uniform
       __builtin_amdgcn_global_load_lds((const void *)(kbase + src + g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(vbase + src + g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
-      if (lane % NCH == 0) bring[S * KT + r] = bv;
+      if (lane % NCH == 0) bring[S * KT + g_row[j]] = ok ? bias_s[e] : -__builtin_inff();
     }
   };
 
-  const int krow = kh * 32 + key_of_row(l32);
+  const int krow = key_of_row(l32);
   const int gi = lane & 15;  // index inside a 16-lane group
   const int gg = lane >> 4;  // group 0..3
 
-  // One tile: wait for slot S, prefetch two tiles ahead, compute.
-  auto step = [&](auto slot_c, int t) {
-    constexpr int S = decltype(slot_c)::value;
-    constexpr int SN = (S + 2) % 3;
-    const unsigned char *kt = S == 0 ? k0 : (S == 1 ? k1 : k2);
-    const unsigned char *vt = S == 0 ? v0 : (S == 1 ? v1 : v2);
-    if (t + 1 < ntiles) ring_barrier<LPT>();
-    else ring_barrier<0>();
-    if (t + 2 < ntiles) issue(std::integral_constant<int, SN>(), t + 2);
-
-    // ---- S^T: 32 keys of this wave's half x 32 queries of its quarter
-    f32x16 sacc;
+  // S^T of the tile in slot S (32 keys x this wave's 32 queries).
+  auto qk = [&](auto slot_c, f32x16 &sacc) {
+    const unsigned char *kt = kslot(slot_c);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
@@ -222,28 +218,42 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + krow * ROWB + ch * 16));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ds], sacc, 0, 0, 0);
     }
+  };
 
-    // ---- base-2 logits with the per-key shift; lazy running maximum
-    const float *bt = bring + S * KT + kh * 32;
-    float mx = -__builtin_inff();
+  // Softmax of the tile in slot S (logits in sacc) and O^T += V^T P^T.
+  auto softmax_pv = [&](auto slot_c, f32x16 &sacc) {
+    constexpr int S = decltype(slot_c)::value;
+    const unsigned char *vt = vslot(slot_c);
+    // Base-2 logits relative to the running reference m_run of each query:
+    // t = s * scale * log2 e + (shift - m_run), one fma per logit.  The
+    // reference is raised (and O, l rescaled) only when some lane sees a
+    // logit above it by more than 8, or sees its first valid key; the two
+    // lane halves (different keys of the same query) then agree on the new
+    // reference through one exchange.
+    const float *bt = bring + S * KT;
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
       const f32x4 b0 = *(const f32x4 *)&bt[m2 * 16 + hh * 8];
       const f32x4 b1 = *(const f32x4 *)&bt[m2 * 16 + hh * 8 + 4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sacc[m2 * 8 + e] = __builtin_fmaf(sacc[m2 * 8 + e], a.scale_log2, b0[e]);
-        sacc[m2 * 8 + 4 + e] = __builtin_fmaf(sacc[m2 * 8 + 4 + e], a.scale_log2, b1[e]);
+        sacc[m2 * 8 + e] = __builtin_fmaf(sacc[m2 * 8 + e], a.scale_log2, b0[e] - m_run);
+        sacc[m2 * 8 + 4 + e] = __builtin_fmaf(sacc[m2 * 8 + 4 + e], a.scale_log2, b1[e] - m_run);
       }
     }
+    float mx = sacc[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    const float mt = fmaxf(mx, xor32(mx));
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.f) != 0ull) {
-      const float m_new = mt > m_run + 8.f ? mt : m_run;
-      const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    if (__builtin_amdgcn_ballot_w64(mx > 8.f || (fresh && mx > -__builtin_inff())) != 0ull) {
+      const float mt = fmaxf(mx, xor32(mx));
+      const bool raise = mt > 8.f || (fresh && mt > -__builtin_inff());
+      const float delta = raise ? mt : 0.f;
+      const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(-delta);
+      fresh = fresh && !raise;
+      m_run += delta;
       l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] -= delta;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -251,11 +261,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     bf16x8 pf[2];
     {
-      const float mu = m_run == -__builtin_inff() ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[r] - mu);
+        const float pv = __builtin_amdgcn_exp2f(sacc[r]);
         sacc[r] = pv;
         rs += pv;
       }
@@ -268,8 +277,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         pf[m] = as_bf16x8(w);
       }
     }
-
-    // ---- O^T += V^T P^T; V^T fragments through the transposing LDS read
+    // V^T fragments through the transposing LDS read
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int n0 = dt * 32 + 16 * (gg & 1) + 4 * (gi & 3);
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
         s16x4 part[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int row = kh * 32 + 16 * m + 8 * (gg >> 1) + 4 * p + (gi >> 2);
+          const int row = 16 * m + 8 * (gg >> 1) + 4 * p + (gi >> 2);
           const int ch = (n0 >> 3) ^ swz_v<D>(row);
           const unsigned char *addr = vt + row * ROWB + ch * 16 + ((n0 >> 2) & 1) * 8;
           part[p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)addr);
@@ -291,77 +299,66 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // One tile in slot S: wait for it, prefetch tile t+3 into the slot of
+  // tile t-1, compute.
+  f32x16 sA;
+  auto step = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    constexpr int S3 = (S + 3) % NBUF;
+    if (t + 2 < ntiles) ring_barrier<2 * LPT>();
+    else if (t + 1 < ntiles) ring_barrier<LPT>();
+    else ring_barrier<0>();
+    if (t + 3 < ntiles) issue(std::integral_constant<int, S3>(), t + 3);
+    qk(slot_c, sA);
+    softmax_pv(slot_c, sA);
+  };
+
   for (int base = 0; base < cnt; base += CAP) {
     const int pc = min(CAP, cnt - base);
-    __syncthreads();
-    for (int e = tid; e < pc; e += NW * 64) {
-      idx_s[e] = idx_row[base + e];
-      bias_s[e] = bias_row ? bias_row[base + e] * kLog2e : 0.f;
-    }
-    __syncthreads();
     nkeys = pc << a.kv_shift;
     ntiles = (nkeys + KT - 1) / KT;
+    // entries covering whole tiles (list tail padded with masked entries)
+    const int padded = min(CAP, ((ntiles * KT) >> a.kv_shift) + 1);
+    __syncthreads();
+    for (int e = tid; e < padded; e += NW * 64) {
+      int blk = e < pc ? idx_row[base + e] : -1;
+      float bv = (e < pc && bias_row) ? bias_row[base + e] * kLog2e : 0.f;
+      if (blk < 0 || blk >= a.M) {
+        blk = 0;
+        bv = -__builtin_inff();
+      }
+      idx_s[e] = blk;
+      bias_s[e] = bv;
+    }
+    __syncthreads();
     if (ntiles > 0) issue(std::integral_constant<int, 0>(), 0);
     if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
-    for (int t = 0; t < ntiles; t += 3) {
+    if (ntiles > 2) issue(std::integral_constant<int, 2>(), 2);
+    for (int t = 0; t < ntiles; t += 4) {
       step(std::integral_constant<int, 0>(), t);
       if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
       if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
+      if (t + 3 < ntiles) step(std::integral_constant<int, 3>(), t + 3);
     }
   }
 
-  // ---- merge the two key halves of each query quarter: wave (qq, kh)
-  // finishes dim tiles [kh DT/2, (kh + 1) DT/2) and hands the others to its
-  // partner (qq, 1 - kh) through a slice of the former ring arrays.
-  __syncthreads();
-  constexpr int HT = DT / 2;                 // dim tiles handed over
-  constexpr int HSZ = HT * 16 * 64;          // floats per wave
-  auto hand = [&](int w) -> float * {
-    unsigned char *b = (w >> 1) == 0 ? k0 : ((w >> 1) == 1 ? v0 : ((w >> 1) == 2 ? k1 : v1));
-    return (float *)b + (w & 1) * HSZ;
-  };
-  float *xml = bias_s;  // [wave][m, l][64]
-  auto finish = [&](auto kh_c) {
-    constexpr int KH = decltype(kh_c)::value;
-    constexpr int OWN = KH * HT, OTH = (1 - KH) * HT;
-    float *po = hand(wave);
+  // ---- normalise and store (the lane halves hold different keys of the
+  // same query: their maxima agree, their partial sums add up)
+  const float l = l_run + xor32(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (qrow < a.Nq) {
+    uint16_t *orow = a.out + ((size_t)bh * a.Nq + qrow) * D;
 #pragma unroll
-    for (int d = 0; d < HT; ++d)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) po[(d * 16 + r) * 64 + lane] = oacc[OTH + d][r];
-    xml[(wave * 2) * 64 + lane] = m_run;
-    xml[(wave * 2 + 1) * 64 + lane] = l_run;
-    __syncthreads();
-    const int partner = wave ^ 4;
-    const float *pp = hand(partner);
-    const float m1 = xml[(partner * 2) * 64 + lane], l1 = xml[(partner * 2 + 1) * 64 + lane];
-    const float mc = fmaxf(m_run, m1);
-    const float mu = mc == -__builtin_inff() ? 0.f : mc;
-    const float f0 = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - mu);
-    const float f1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mu);
-    const float lh = l_run * f0 + l1 * f1;  // this lane half's keys
-    const float l = lh + xor32(lh);         // both lane halves
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int row = qb * 128 + qq * 32 + l32;
-    if (row < a.Nq) {
-      uint16_t *orow = a.out + ((size_t)bh * a.Nq + row) * D;
-#pragma unroll
-      for (int d = 0; d < HT; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = (oacc[OWN + d][4 * g + e] * f0 + pp[(d * 16 + 4 * g + e) * 64 + lane] * f1) * inv;
-          u32x2 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          *(u32x2 *)&orow[(OWN + d) * 32 + g * 8 + hh * 4] = w;
-        }
-      if (KH == 0 && a.lse && hh == 0)
-        a.lse[(size_t)bh * a.Nq + row] = l > 0.f ? (mu + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
-    }
-  };
-  if (kh == 0) finish(std::integral_constant<int, 0>());
-  else finish(std::integral_constant<int, 1>());
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w = {pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                   pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
+        *(u32x2 *)&orow[dt * 32 + g * 8 + hh * 4] = w;
+      }
+    if (a.lse && hh == 0)
+      a.lse[(size_t)bh * a.Nq + qrow] = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+  }
 }
 
 int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int Nq, int Nk,
@@ -386,7 +383,7 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   a.scale_log2 = scale * kLog2e;
   const long long total = (long long)B * H * a.nqb;
   a.total_wg = (int)total;
-  dim3 grid((unsigned)total), block(512);
+  dim3 grid((unsigned)total), block(256);
   if (d == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, a);
   else
