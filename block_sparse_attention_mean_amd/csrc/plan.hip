@@ -6,14 +6,16 @@
 // blocks shared by the whole query block.  Top-k at the same budget is the
 // "SIP without pi weighting" level of the ablation paragraph in "전제와 한계".
 //
-// One workgroup (256 threads) per row.  The row sits in LDS when it fits.
+// One workgroup (512 threads) per row; the row sits in LDS when it fits,
+// else it is re-read from global memory on every pass.
 //
 // SIP, exactly as the C ABI documents it:
 //   * the number r of saturated blocks is the smallest r with
 //     (s - r) S_(r+1) <= T_r.  Over the row values v this reads
 //     cond(v): (s - #{S >= v}) v <= sum_{S < v} S, which is monotone in v;
-//     a bisection over fp32 bit patterns finds the largest x with cond(x),
-//     and then r = #{S > x}, T_r = sum_{S <= x} S;
+//     the largest x with cond(x) is bracketed by secant steps down from
+//     T / s and a bisection over fp32 bit patterns that stops once no row
+//     value lies inside the bracket; then r = #{S > x}, T_r = sum_{S <= x} S;
 //   * each bisection step decides cond from an fp64 sum whose rounding
 //     error is bounded; only when the margin is inside that bound is the
 //     sum recomputed exactly (integer superaccumulator, 320 bits in units
@@ -44,7 +46,7 @@ uint64_t sampling_offset(uint64_t seed, uint64_t row) { return offset_of_row(see
 
 namespace {
 
-constexpr int PT = 256;               // threads per row
+constexpr int PT = 512;               // threads per row
 constexpr int NW = PT / 64;           // waves
 constexpr int NDIG = 10;              // 32-bit digits of the superaccumulator
 constexpr uint64_t UNIT = 1ull << 44;  // fixed-point 1.0 of pi
@@ -62,6 +64,7 @@ struct PlanArgs {
 
 struct Shared {
   uint64_t digits[NDIG * PT];   // per-thread carry-save digits [digit][thread]
+  uint64_t partial[NDIG * (PT / 16)];  // first-level column sums
   uint64_t total[NDIG + 1];     // normalised digits of the last exact sum
   double red_d[NW];
   long long red_l[NW];
@@ -156,16 +159,53 @@ __device__ uint64_t block_exscan_u64(Shared &sh, uint64_t v, uint64_t &total) {
   return base + inc - v;
 }
 
+// Row access: thread t owns the contiguous chunk [lo, hi) (a multiple of
+// 4 long, so LDS reads are 16 bytes wide); the row sits in LDS when it
+// fits, else it is re-read from global memory on every pass.
+template <bool IN_LDS>
+struct RowView {
+  const float *p;  // LDS copy or global row
+  int lo, hi;
+  __device__ __forceinline__ void init(const float *grow, float *srow, int M) {
+    const int chunk = ((M + PT - 1) / PT + 3) & ~3;
+    lo = min(M, (int)threadIdx.x * chunk);
+    hi = min(M, lo + chunk);
+    if (IN_LDS) {
+      for (int j = threadIdx.x; j < M; j += PT) srow[j] = grow[j];
+      __syncthreads();
+      p = srow;
+    } else {
+      p = grow;
+    }
+  }
+  // f(j, value) over this thread's chunk, ascending j
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+    int j = lo;
+    if (IN_LDS) {
+      for (; j + 4 <= hi; j += 4) {
+        const float4 q = *(const float4 *)(p + j);
+        f(j, q.x);
+        f(j + 1, q.y);
+        f(j + 2, q.z);
+        f(j + 3, q.w);
+      }
+    }
+    for (; j < hi; ++j) f(j, p[j]);
+  }
+};
+
 // Exact sum of {S_j : S_j < x} (strict) or {S_j <= x} (!strict) into
-// sh.total as 11 normalised 32-bit digits (units of 2^-149).
-template <typename RowT>
-__device__ void exact_sum(Shared &sh, RowT row, int lo, int hi, float x, bool strict) {
+// sh.total as 11 normalised 32-bit digits (units of 2^-149).  Each thread
+// accumulates carry-save digits in its own LDS column (no contention); the
+// columns are reduced in two levels.
+template <typename Row>
+__device__ __forceinline__ void exact_sum(Shared &sh, const Row &row, float x, bool strict) {
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < NDIG; ++i) sh.digits[i * PT + t] = 0ull;
-  for (int j = lo; j < hi; ++j) {
-    const float s = row[j];
-    if (strict ? !(s < x) : !(s <= x)) continue;
+  row.each([&](int, float s) {
+    if (strict ? !(s < x) : !(s <= x)) return;
     const unsigned b = __builtin_bit_cast(unsigned, s);
     const unsigned e = b >> 23;
     const uint64_t mant = e ? ((b & 0x7fffffu) | 0x800000u) : (b & 0x7fffffu);
@@ -174,20 +214,30 @@ __device__ void exact_sum(Shared &sh, RowT row, int lo, int hi, float x, bool st
     const unsigned d = shift >> 5;
     atomicAdd((unsigned long long *)&sh.digits[d * PT + t], (unsigned long long)(v & 0xffffffffull));
     atomicAdd((unsigned long long *)&sh.digits[(d + 1) * PT + t], (unsigned long long)(v >> 32));
-  }
+  });
   __syncthreads();
-  if (t < NDIG) {
+  // level 1: PT/16 partial sums of 16 columns for each digit
+  constexpr int NP = PT / 16;
+  for (int u = t; u < NDIG * NP; u += PT) {
+    const int dg = u / NP, part = u % NP;
     uint64_t acc = 0;
-    for (int i = 0; i < PT; ++i) acc += sh.digits[t * PT + i];
-    sh.digits[t * PT] = acc;  // column total parked in slot 0
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += sh.digits[dg * PT + part * 16 + i];
+    sh.partial[dg * NP + part] = acc;
   }
   __syncthreads();
-  if (t == 0) {
+  if (t < NDIG) {  // level 2: one thread per digit
+    uint64_t acc = 0;
+    for (int k = 0; k < NP; ++k) acc += sh.partial[t * NP + k];
+    sh.partial[t * NP] = acc;
+  }
+  __syncthreads();
+  if (t == 0) {  // carry propagation
     uint64_t carry = 0;
     for (int i = 0; i < NDIG; ++i) {
-      const uint64_t x2 = sh.digits[i * PT] + carry;
-      sh.total[i] = x2 & 0xffffffffull;
-      carry = x2 >> 32;
+      const uint64_t acc = sh.partial[i * NP] + carry;
+      sh.total[i] = acc & 0xffffffffull;
+      carry = acc >> 32;
     }
     sh.total[NDIG] = carry;
   }
@@ -203,18 +253,18 @@ __device__ double digits_to_double(const uint64_t *dig) {
       break;
     }
   if (top < 0) return 0.0;
+  // 128-bit window of the four highest digits; its lowest bit has weight 2^base
+  unsigned __int128 w = 0;
+  for (int i = top; i >= top - 3; --i) w = (w << 32) | (unsigned __int128)(i >= 0 ? dig[i] : 0u);
+  const int base = 32 * (top - 3);
+  bool low_nz = false;  // any set bit below the window
+  for (int i = top - 4; i >= 0; --i) low_nz |= dig[i] != 0;
   const int p = 32 * top + 31 - __builtin_clz((unsigned)dig[top]);  // highest set bit
-  auto bit = [&](int k) -> uint64_t { return k < 0 ? 0ull : ((dig[k >> 5] >> (k & 31)) & 1ull); };
-  if (p <= 52) {
-    uint64_t m = 0;
-    for (int k = p; k >= 0; --k) m = (m << 1) | bit(k);
-    return ldexp((double)m, -149);
-  }
-  uint64_t m = 0;
-  for (int k = p; k >= p - 52; --k) m = (m << 1) | bit(k);
-  const uint64_t rnd = bit(p - 53);
-  bool sticky = false;
-  for (int k = p - 54; k >= 0 && !sticky; --k) sticky = bit(k) != 0;
+  const int sh_m = p - 52 - base;  // window bit of the mantissa's lowest bit (>= 43)
+  uint64_t m = (uint64_t)(w >> sh_m) & ((1ull << 53) - 1);
+  if (p <= 52) return ldexp((double)m, base + sh_m - 149);  // exact (never below 53 bits here)
+  const bool rnd = (w >> (sh_m - 1)) & 1;
+  const bool sticky = low_nz || (w & (((unsigned __int128)1 << (sh_m - 1)) - 1)) != 0;
   int ex = p - 52;
   if (rnd && (sticky || (m & 1ull))) {
     ++m;
@@ -253,41 +303,29 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Shared &sh = *reinterpret_cast<Shared *>(smem_raw);
   float *srow = reinterpret_cast<float *>(smem_raw + ((sizeof(Shared) + 15) & ~(size_t)15));
-
   const int t = threadIdx.x;
   const size_t r = blockIdx.x;
   const int M = a.M, s = a.budget;
-  const float *grow = a.scores + r * (size_t)M;
-  const float *row = IN_LDS ? srow : grow;
   int32_t *out_idx = a.idx + r * (size_t)s;
   float *out_bias = a.bias ? a.bias + r * (size_t)s : nullptr;
-
-  if (IN_LDS) {
-    for (int j = t; j < M; j += PT) srow[j] = grow[j];
-    __syncthreads();
-  }
-  const int chunk = (M + PT - 1) / PT;
-  const int lo = min(M, t * chunk), hi = min(M, lo + chunk);
+  RowView<IN_LDS> row;
+  row.init(a.scores + r * (size_t)M, srow, M);
 
   // ---- phase 0: validity, positives, extremes, approximate total
   long long npos = 0, nbad = 0;
   unsigned mx = 0, mnpos = 0x7f800000u;
   double tot = 0.0;
-  for (int j = lo; j < hi; ++j) {
-    const float v = row[j];
+  row.each([&](int, float v) {
     const unsigned b = __builtin_bit_cast(unsigned, v);
-    if (!(v >= 0.f) || b >= 0x7f800000u) {
+    if (!(v >= 0.f) || (b & 0x7fffffffu) >= 0x7f800000u) {
       ++nbad;
-      continue;
-    }
-    if (b != 0u) {  // +0 only (-0 has the sign bit and is >= 0 but b != 0)
-      if (b & 0x80000000u) continue;
+    } else if (v > 0.f) {
       ++npos;
       mx = max(mx, b);
       mnpos = min(mnpos, b);
       tot += (double)v;
     }
-  }
+  });
   nbad = block_sum_l(sh, nbad);
   npos = block_sum_l(sh, npos);
   tot = block_sum_d(sh, tot);
@@ -316,17 +354,16 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
       const unsigned mid = blo + (bhi - blo) / 2;
       const float xm = __builtin_bit_cast(float, mid);
       long long c = 0;
-      for (int j = lo; j < hi; ++j) c += row[j] >= xm ? 1 : 0;
+      row.each([&](int, float v) { c += v >= xm ? 1 : 0; });
       c = block_sum_l(sh, c);
       if (c >= s) blo = mid; else bhi = mid;
     }
     const float v = __builtin_bit_cast(float, blo);
-    // values are >= 0 here; -0 equals +0 and is treated as 0
     long long ngt = 0, ntie = 0;
-    for (int j = lo; j < hi; ++j) {
-      ngt += row[j] > v ? 1 : 0;
-      ntie += row[j] == v ? 1 : 0;
-    }
+    row.each([&](int, float x) {
+      ngt += x > v ? 1 : 0;
+      ntie += x == v ? 1 : 0;
+    });
     ngt = block_sum_l(sh, ngt);
     const long long need = s - ngt;
     uint64_t tie_total;
@@ -334,22 +371,20 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
     long long nsel = 0;
     {
       uint64_t tr = tie_base;
-      for (int j = lo; j < hi; ++j) {
-        const float x = row[j];
+      row.each([&](int, float x) {
         bool sel = x > v;
         if (x == v) {
           sel = (long long)tr < need;
           ++tr;
         }
         nsel += sel ? 1 : 0;
-      }
+      });
     }
     uint64_t sel_total;
     uint64_t pos = block_exscan_u64(sh, (uint64_t)nsel, sel_total);
     {
       uint64_t tr = tie_base;
-      for (int j = lo; j < hi; ++j) {
-        const float x = row[j];
+      row.each([&](int j, float x) {
         bool sel = x > v;
         if (x == v) {
           sel = (long long)tr < need;
@@ -360,7 +395,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
           if (out_bias) out_bias[pos] = 0.f;
           ++pos;
         }
-      }
+      });
     }
     if (t == 0) {
       a.count[r] = s;
@@ -373,14 +408,15 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   if (npos <= s) {
     uint64_t total;
     long long mine = 0;
-    for (int j = lo; j < hi; ++j) mine += row[j] > 0.f ? 1 : 0;
+    row.each([&](int, float x) { mine += x > 0.f ? 1 : 0; });
     uint64_t pos = block_exscan_u64(sh, (uint64_t)mine, total);
-    for (int j = lo; j < hi; ++j)
-      if (row[j] > 0.f) {
+    row.each([&](int j, float x) {
+      if (x > 0.f) {
         out_idx[pos] = j;
         if (out_bias) out_bias[pos] = 0.f;
         ++pos;
       }
+    });
     fill_rest((int)npos);
     if (t == 0) {
       a.count[r] = (int)npos;
@@ -390,82 +426,160 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   }
 
   // cond(x): (s - #{S >= x}) x <= sum_{S < x} S, decided with a certified
-  // fp64 margin or, inside the margin, exactly.
-  const double err_bound = ldexp((double)(M + 2 * PT), -50) * tot;
-  auto cond = [&](float x) -> bool {
-    long long nge = 0;
-    double slt = 0.0;
-    for (int j = lo; j < hi; ++j) {
-      const float v = row[j];
-      if (v >= x) ++nge;
-      else slt += (double)v;
-    }
-    nge = block_sum_l(sh, nge);
-    slt = block_sum_d(sh, slt);
-    const long long mult = (long long)s - nge;
-    if (mult <= 0) return true;
-    const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
-    const double diff = lhs - slt;
-    if (diff > err_bound) return false;
-    if (diff < -err_bound) return true;
-    exact_sum(sh, row, lo, hi, x, true);
-    uint64_t ldig[NDIG + 1];
-    scaled_to_digits((unsigned long long)mult, x, ldig);
-    return digits_ge(sh.total, ldig);
-  };
-
+  // fp64 margin or, inside the margin, exactly.  The search below visits
+  // one point per iteration (a single evaluation site keeps the register
+  // footprint of the unrolled row passes small):
+  //   stage 0  x = max S           (true: no saturated block)
+  //   stage 1  secant steps down from T / s towards the threshold
+  //   stage 2  bisection of [blo, bhi) until no row value lies inside
+  //   stage 3  exact sum T_r = sum_{S <= x*}
+  // per-thread fp32 partial sums (chunk terms) then an fp64 reduction
+  const int chunk = ((M + PT - 1) / PT + 3) & ~3;
+  const double err_bound = (ldexp((double)(chunk + 2), -23) + ldexp((double)(M + 2 * PT), -50)) * tot;
+  const float fmx = __builtin_bit_cast(float, mx);
   unsigned blo = mnpos, bhi = mx;
-  float xstar;
-  if (cond(__builtin_bit_cast(float, mx))) {
-    xstar = __builtin_bit_cast(float, mx);  // no saturated block
-  } else {
-    // x > T/s can never satisfy cond: tighten the upper end when possible.
-    const double up = tot / (double)s * (1.0 + 0x1p-20);
-    const float upf = (float)up;
-    if (upf < __builtin_bit_cast(float, mx)) {
-      const unsigned ub = __builtin_bit_cast(unsigned, upf) + 1u;
-      if (ub > blo && ub < bhi && !cond(__builtin_bit_cast(float, ub))) bhi = ub;
+  long long ngt_lo = npos, nge_hi = 0;
+  float x = fmx;
+  int stage = 0, secant_left = 12;
+  float xstar = fmx;
+  while (true) {
+    // ---- one pass at x (stage 3: non-strict exact sum only)
+    bool holds = true;
+    long long nge = 0, ngt = 0;
+    double slt = 0.0;
+    bool need_exact = stage == 3;
+    long long mult = 0;
+    if (stage != 3) {
+      int cge = 0, cgt = 0;
+      float sf = 0.f;
+      row.each([&](int, float v) {
+        const bool ge = v >= x;
+        cge += ge ? 1 : 0;
+        cgt += v > x ? 1 : 0;
+        sf += ge ? 0.f : v;
+      });
+      const long long cnt = block_sum_l(sh, ((long long)cge << 32) | (long long)cgt);
+      slt = block_sum_d(sh, (double)sf);
+      nge = cnt >> 32;
+      ngt = cnt & 0xffffffffll;
+      mult = (long long)s - nge;
+      if (mult > 0) {
+        const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
+        const double diff = lhs - slt;
+        if (diff > err_bound) holds = false;
+        else if (!(diff < -err_bound)) need_exact = true;
+      }
     }
-    while (bhi - blo > 1) {
-      const unsigned mid = blo + (bhi - blo) / 2;
-      if (cond(__builtin_bit_cast(float, mid))) blo = mid; else bhi = mid;
+    if (need_exact) {
+      exact_sum(sh, row, x, stage != 3);
+      if (stage == 3) break;
+      uint64_t ldig[NDIG + 1];
+      scaled_to_digits((unsigned long long)mult, x, ldig);
+      holds = digits_ge(sh.total, ldig);
+    }
+    // ---- advance the search
+    const unsigned xb = __builtin_bit_cast(unsigned, x);
+    if (stage == 0) {
+      if (holds) {  // no saturated block: x* = max S
+        xstar = x;
+        stage = 3;
+        continue;
+      }
+      nge_hi = nge;
+      stage = 1;
+      x = fminf(fmx, (float)(tot / (double)s * (1.0 + 0x1p-20)));  // x > T/s never holds
+      if (!(__builtin_bit_cast(unsigned, x) > blo && __builtin_bit_cast(unsigned, x) < bhi)) stage = 2;
+      else continue;
+    } else if (stage == 1) {
+      if (holds) {
+        blo = xb;
+        ngt_lo = ngt;
+        stage = 2;
+      } else {
+        bhi = xb;
+        nge_hi = nge;
+        // secant step x' = sum_{S<x} / (s - #{S >= x}), aimed 2^-12 low so
+        // that the test at x' is decided by the fp64 margin
+        const float xn = (float)(slt / (double)mult * (1.0 - 0x1p-12));
+        unsigned xnb = xn < x ? __builtin_bit_cast(unsigned, xn) : xb - 1u;
+        xnb = max(blo + 1u, xnb);
+        if (--secant_left > 0 && xnb > blo && xnb < bhi) {
+          x = __builtin_bit_cast(float, xnb);
+          continue;
+        }
+        stage = 2;
+      }
+    } else {  // stage 2: x was a bisection point
+      if (holds) {
+        blo = xb;
+        ngt_lo = ngt;
+      } else {
+        bhi = xb;
+        nge_hi = nge;
+      }
+    }
+    // stage 2: next bisection point, or done
+    if (bhi - blo > 1 && ngt_lo > nge_hi) {
+      x = __builtin_bit_cast(float, blo + (bhi - blo) / 2);
+      continue;
     }
     xstar = __builtin_bit_cast(float, blo);
+    x = xstar;
+    stage = 3;
   }
 
-  long long nsat = 0;
-  for (int j = lo; j < hi; ++j) nsat += row[j] > xstar ? 1 : 0;
-  nsat = block_sum_l(sh, nsat);
-  exact_sum(sh, row, lo, hi, xstar, false);
+  long long nsat;
+  {
+    long long c = 0;
+    row.each([&](int, float v) { c += v > xstar ? 1 : 0; });
+    nsat = block_sum_l(sh, c);
+  }
   if (t == 0) sh.bcast_d = digits_to_double(sh.total);
   __syncthreads();
   const double Tr = sh.bcast_d;
   const double lam = (double)(s - nsat) / Tr;
 
   const uint64_t U = a.offsets ? a.offsets[r] : offset_of_row(a.seed, r);
+  // Pi_j = floor(min(1, lam S_j) 2^44) = floor(min(2^44, lam' S_j)) with
+  // lam' = lam 2^44 (exact: power-of-two scaling commutes with rounding);
+  // floor, then + 2^52 puts the integer in the low mantissa bits.
+  const double lam44 = lam * (double)UNIT;
+  auto fixed_pi = [&](float v) -> uint64_t {
+    const double y = __builtin_floor(fmin((double)UNIT, lam44 * (double)v)) + 0x1p52;
+    return __builtin_bit_cast(uint64_t, y) & ((1ull << 52) - 1);
+  };
   uint64_t mine = 0;
-  for (int j = lo; j < hi; ++j) {
-    const double pi = fmin(1.0, lam * (double)row[j]);
-    mine += (uint64_t)(pi * (double)UNIT);
-  }
+  row.each([&](int, float v) { mine += fixed_pi(v); });
   uint64_t csum_total;
-  uint64_t C = block_exscan_u64(sh, mine, csum_total);
+  const uint64_t C0 = block_exscan_u64(sh, mine, csum_total);
+  // With D = C - U, the number of points U + k 2^44 (k >= 0) below C is
+  // ((D - 1) >> 44) + 1 (arithmetic shift; 0 while D <= 0).  Block j holds
+  // a point exactly when that number grows across it.
+  long long qprev = (((long long)C0 - (long long)U) - 1) >> 44;  // points below C, minus 1
+  long long D = (long long)C0 - (long long)U;
+  row.each([&](int j, float v) {
+    const uint64_t Pi = fixed_pi(v);
+    D += (long long)Pi;
+    const long long q = (D - 1) >> 44;
+    if (q > qprev && qprev + 1 < (long long)s) out_idx[qprev + 1] = j;
+    qprev = q;
+  });
   auto below = [&](uint64_t c) -> uint64_t {  // points U + k 2^44 (k < s) below c
     if (c <= U) return 0;
     const uint64_t n = ((c - U - 1) >> 44) + 1;
     return n < (uint64_t)s ? n : (uint64_t)s;
   };
-  for (int j = lo; j < hi; ++j) {
-    const double pi = fmin(1.0, lam * (double)row[j]);
-    const uint64_t Pi = (uint64_t)(pi * (double)UNIT);
-    const uint64_t p0 = below(C), p1 = below(C + Pi);
-    if (p1 > p0) {
-      out_idx[p0] = j;
-      if (out_bias) out_bias[p0] = (float)(-log(pi));
-    }
-    C += Pi;
-  }
   const int drawn = (int)below(csum_total);
+  if (out_bias) {
+    // shifts -ln pi of the drawn blocks, one slot per thread (the indices
+    // were written by this workgroup before the barrier)
+    __syncthreads();
+    for (int e = t; e < drawn; e += PT) {
+      const int j = out_idx[e];
+      const double pi = fmin(1.0, lam * (double)row.p[j]);
+      out_bias[e] = (float)(-log(pi));
+    }
+  }
   fill_rest(drawn);
   if (t == 0) {
     a.count[r] = drawn;
@@ -486,12 +600,11 @@ int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, i
       hipSuccess)
     return BSA_ERR_HIP;
   const size_t base = (sizeof(Shared) + 15) & ~(size_t)15;
-  const size_t with_row = base + (size_t)M * sizeof(float);
-  if (with_row <= (size_t)max_lds) {
+  const size_t with_row = base + (size_t)(M + 4) * sizeof(float);
+  if (with_row <= (size_t)max_lds)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(rows), dim3(PT), with_row, stream, a);
-  } else {
+  else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(rows), dim3(PT), base, stream, a);
-  }
   return status_of(hipGetLastError());
 }
 
