@@ -100,23 +100,32 @@ __global__ __launch_bounds__(256) void pool_split_kernel(SelArgs a) {
 }
 
 // ---------------------------------------------------------------- k-means
+// One workgroup per query block.  Member sums follow the stated order
+// exactly: a stable counting sort lists each cluster's rows in ascending
+// order, and one thread per (dim, cluster) adds them in that order.
 template <int D>
 __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
-  constexpr int QS = D + 1;  // padded fp32 row stride
-  __shared__ float qf[128 * QS];
-  __shared__ float mu[16 * D];
-  __shared__ float acc[16 * D];
+  constexpr int QS = D + 8;  // padded bf16 row stride (16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint16_t qb16[128 * QS];
+  __shared__ __attribute__((aligned(16))) float mu[16 * D];
   __shared__ int asg[128];
-  __shared__ int cnt[16];
+  __shared__ int order[128];  // rows sorted by cluster, ascending within
+  __shared__ int cnt[16], off[16];
   __shared__ int active[16];
+  __shared__ unsigned long long masks[2][16];
 
   const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
   const int qb = blockIdx.x, bh = blockIdx.y;
   const int C = a.C;
   const int n = min(128, a.N - qb * 128);
   const uint16_t *qp = a.q + ((size_t)bh * a.N + (size_t)qb * 128) * D;
 
-  for (int e = t; e < n * D; e += 256) qf[(e / D) * QS + (e % D)] = bf16_to_f32(qp[e]);
+  // 16-byte loads of the block into padded rows
+  for (int e = t; e < n * (D / 8); e += 256) {
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    st16(&qb16[r * QS + c8 * 8], ld16(qp + (size_t)r * D + c8 * 8));
+  }
   for (int e = t; e < 16 * D; e += 256) mu[e] = 0.f;
   if (t < 16) active[t] = (t < C) && (((t + 1) * n) / C > (t * n) / C);
   if (t < n) {
@@ -126,27 +135,50 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
   }
   __syncthreads();
 
-  // Member means in ascending row order (one thread per (dim, cluster parity)).
+  auto q_at = [&](int r, int k) -> float { return bf16_to_f32(qb16[r * QS + k]); };
+
+  // counts, offsets and the stable order of rows by cluster, then means
   auto update_means = [&]() {
-    for (int e = t; e < 16 * D; e += 256) acc[e] = 0.f;
-    if (t < 16) cnt[t] = 0;
-    __syncthreads();
-    if (t < 2 * D) {
-      const int dim = t % D, par = t / D;
-      for (int r = 0; r < n; ++r) {
-        const int c = asg[r];
-        if ((c & 1) == par) acc[c * D + dim] = __fadd_rn(acc[c * D + dim], qf[r * QS + dim]);
+    if (w < 2) {
+      const int r = w * 64 + lane;
+      const int c = r < n ? asg[r] : -1;
+      for (int k = 0; k < C; ++k) {
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(c == k);
+        if (lane == 0) masks[w][k] = m;
       }
     }
-    if (t < C) {
-      int m = 0;
-      for (int r = 0; r < n; ++r) m += asg[r] == t ? 1 : 0;
-      cnt[t] = m;
+    __syncthreads();
+    if (t == 0) {
+      int o = 0;
+      for (int k = 0; k < C; ++k) {
+        const int c0 = __builtin_popcountll(masks[0][k]), c1 = __builtin_popcountll(masks[1][k]);
+        cnt[k] = c0 + c1;
+        off[k] = o;
+        o += c0 + c1;
+      }
     }
     __syncthreads();
-    for (int e = t; e < C * D; e += 256) {
-      const int c = e / D;
-      if (cnt[c] > 0) mu[e] = __fdiv_rn(acc[e], (float)cnt[c]);
+    if (w < 2) {
+      const int r = w * 64 + lane;
+      if (r < n) {
+        const int c = asg[r];
+        const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        int rank = __builtin_popcountll(masks[w][c] & below);
+        if (w == 1) rank += __builtin_popcountll(masks[0][c]);
+        order[off[c] + rank] = r;
+      }
+    }
+    __syncthreads();
+    // thread (dim, cluster group): clusters g, g + G, ... for G = 256 / D
+    constexpr int G = 256 / D;
+    const int dim = t % D, g = t / D;
+    for (int c = g; c < C; c += G) {
+      const int m = cnt[c];
+      if (m == 0) continue;  // empty cluster keeps its centroid
+      float acc = 0.f;
+      const int o = off[c];
+      for (int i = 0; i < m; ++i) acc = __fadd_rn(acc, q_at(order[o + i], dim));
+      mu[c * D + dim] = __fdiv_rn(acc, (float)m);
     }
     __syncthreads();
   };
@@ -161,9 +193,17 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
       for (int c = par; c < C; c += 2) {
         if (!active[c]) continue;
         float dd = 0.f;
-        for (int k = 0; k < D; ++k) {
-          const float df = __fsub_rn(qf[r * QS + k], mu[c * D + k]);
-          dd = __fadd_rn(dd, __fmul_rn(df, df));
+        for (int k0 = 0; k0 < D; k0 += 8) {
+          const u32x4 qv = *(const u32x4 *)&qb16[r * QS + k0];
+          const f32x4 m0 = *(const f32x4 *)&mu[c * D + k0];
+          const f32x4 m1 = *(const f32x4 *)&mu[c * D + k0 + 4];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const unsigned word = qv[e >> 1];
+            const float qx = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
+            const float df = __fsub_rn(qx, e < 4 ? m0[e] : m1[e - 4]);
+            dd = __fadd_rn(dd, __fmul_rn(df, df));
+          }
         }
         if (dd < best) {
           best = dd;
@@ -189,7 +229,6 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
   if (a.centroids)
     for (int e = t; e < C * D; e += 256) a.centroids[rbase * D + e] = mu[e];
   // one wave per cluster row for the split
-  const int lane = t & 63, w = t >> 6;
   constexpr int PER = D / 64;
   for (int c = w; c < C; c += 4) {
     float amax = 0.f;
