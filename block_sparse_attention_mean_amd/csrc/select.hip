@@ -9,8 +9,9 @@
 // selector scores many query/KV blocks in one batched matrix operation.
 //
 // Kernels:
-//   pool_split  one wave per KV block: fp32 mean of its keys, then a split
-//               into two fp16 halves with a per-row power-of-two scale
+//   pool_split  one workgroup per 32 KV blocks (one key tile of the GEMM):
+//               fp32 mean of each block's keys, then a split into two fp16
+//               halves at one power-of-two scale per tile
 //               (x 2^e = hi + lo 2^-11, |x 2^e| < 2^11) so the GEMM below is
 //               fp32-accurate on fp16 matrix cores;
 //   kmeans      one workgroup per query block; fp32 in a fixed operation
@@ -18,13 +19,15 @@
 //               summed over ascending dims without fused multiply-add) --
 //               its assignments are discrete decisions and must be
 //               reproducible bit for bit;
-//   score<0>    sweep 1 of centroids x pooled keys (3 fp16 MFMA per product:
+//   score<0>    sweep 1 of pooled keys x centroids (3 fp16 MFMA per product:
 //               hi.hi + (hi.lo + lo.hi) 2^-11): per-row running max and sum
 //               of 2^(logit log2 e), per column chunk;
 //   score<1>    sweep 2: merges the chunk statistics into a per-row offset
 //               beta = max + log2(sum) - log2(share), recomputes the same
 //               logits bit for bit and writes S_ij = sum_c 2^(t_cj - beta_c)
-//               with the cluster sum done in registers.
+//               with the cluster sum done across lanes.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bsa {
@@ -35,12 +38,11 @@ typedef _Float16 half_t;
 
 struct SelArgs {
   const uint16_t *q, *k;
-  int N, M, nqb, C, iters, kv_shift, R, nchunk, chunk_cols, tiles;
+  int N, M, nqb, C, iters, kv_shift, R, nchunk, chunk_cols, tiles, ktiles;
   float *scores, *centroids, *weights;
   half_t *kb_hi, *kb_lo;
   float *kb_cs;
-  half_t *ce_hi, *ce_lo;
-  float *ce_rs, *ce_w;
+  float *ce_f, *ce_w;
   float2 *stats;
   float scale_log2;
 };
@@ -67,36 +69,51 @@ __device__ __forceinline__ float wave_max_f(float v) {
 }
 
 // ---------------------------------------------------------------- pooling
+// One workgroup per key tile of 32 KV blocks; wave w pools blocks 8 w .. 8 w + 7
+// of the tile, lane l holding dims l PER .. l PER + PER - 1.
 template <int D>
 __global__ __launch_bounds__(256) void pool_split_kernel(SelArgs a) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int bh = blockIdx.y;
-  if (j >= a.M) return;
+  __shared__ float wmax[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tile = blockIdx.x, bh = blockIdx.y;
   const int kvb = 1 << a.kv_shift;
-  const int r0 = j * kvb;
-  const int rows = min(kvb, a.N - r0);
-  const uint16_t *kp = a.k + ((size_t)bh * a.N + r0) * D + lane * PER;
-  float acc[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) acc[p] = 0.f;
-  for (int t = 0; t < rows; ++t) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) acc[p] = __fadd_rn(acc[p], bf16_to_f32(kp[(size_t)t * D + p]));
-  }
+  float acc[8][PER];
   float amax = 0.f;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    acc[p] = rows == kvb ? acc[p] * (1.0f / (float)kvb) : __fdiv_rn(acc[p], (float)rows);
-    amax = fmaxf(amax, fabsf(acc[p]));
+  for (int i = 0; i < 8; ++i) {
+    const int j = tile * 32 + w * 8 + i;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[i][p] = 0.f;
+    if (j < a.M) {
+      const int r0 = j * kvb;
+      const int rows = min(kvb, a.N - r0);
+      const uint16_t *kp = a.k + ((size_t)bh * a.N + r0) * D + lane * PER;
+      for (int t = 0; t < rows; ++t) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[i][p] = __fadd_rn(acc[i][p], bf16_to_f32(kp[(size_t)t * D + p]));
+      }
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        acc[i][p] = rows == kvb ? acc[i][p] * (1.0f / (float)kvb) : __fdiv_rn(acc[i][p], (float)rows);
+        amax = fmaxf(amax, fabsf(acc[i][p]));
+      }
+    }
   }
   amax = wave_max_f(amax);
-  const int e = row_exponent(amax);
-  const size_t o = ((size_t)bh * a.M + j) * D + lane * PER;
+  if (lane == 0) wmax[w] = amax;
+  __syncthreads();
+  const int e = row_exponent(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 #pragma unroll
-  for (int p = 0; p < PER; ++p) split_f16(acc[p], e, a.kb_hi[o + p], a.kb_lo[o + p]);
-  if (lane == 0) a.kb_cs[(size_t)bh * a.M + j] = ldexpf(1.f, -e);
+  for (int i = 0; i < 8; ++i) {
+    const int j = tile * 32 + w * 8 + i;
+    if (j < a.M) {
+      const size_t o = ((size_t)bh * a.M + j) * D + lane * PER;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) split_f16(acc[i][p], e, a.kb_hi[o + p], a.kb_lo[o + p]);
+    }
+  }
+  if (threadIdx.x == 0) a.kb_cs[(size_t)bh * a.ktiles + tile] = ldexpf(1.f, -e);
 }
 
 // ---------------------------------------------------------------- k-means
@@ -223,210 +240,319 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
     update_means();
   }
 
-  // outputs: fp32 centroids / shares (optional) and the fp16 split for the GEMM
+  // outputs: fp32 centroids and shares for the score GEMM (and the caller)
   const size_t rbase = ((size_t)bh * a.nqb + qb) * C;
-  if (a.weights && t < C) a.weights[rbase + t] = __fdiv_rn((float)cnt[t], (float)n);
-  if (a.centroids)
-    for (int e = t; e < C * D; e += 256) a.centroids[rbase * D + e] = mu[e];
-  // one wave per cluster row for the split
-  constexpr int PER = D / 64;
-  for (int c = w; c < C; c += 4) {
-    float amax = 0.f;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) amax = fmaxf(amax, fabsf(mu[c * D + lane * PER + p]));
-    amax = wave_max_f(amax);
-    const int e = row_exponent(amax);
-    const size_t o = (rbase + c) * D + lane * PER;
-#pragma unroll
-    for (int p = 0; p < PER; ++p) split_f16(mu[c * D + lane * PER + p], e, a.ce_hi[o + p], a.ce_lo[o + p]);
-    if (lane == 0) {
-      a.ce_rs[rbase + c] = ldexpf(a.scale_log2, -e);
-      a.ce_w[rbase + c] = __fdiv_rn((float)cnt[c], (float)n);
-    }
+  if (t < C) {
+    const float share = __fdiv_rn((float)cnt[t], (float)n);
+    a.ce_w[rbase + t] = share;
+    if (a.weights) a.weights[rbase + t] = share;
+  }
+  for (int e = t; e < C * D; e += 256) {
+    a.ce_f[rbase * D + e] = mu[e];
+    if (a.centroids) a.centroids[rbase * D + e] = mu[e];
   }
 }
 
 // ---------------------------------------------------------------- scores
-// MFMA row i of a 32-row sub-tile -> local row so that lane half h,
-// register r holds local row 16 h + r.
-__device__ __forceinline__ int local_row(int i) {
-  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte-chunk XOR swizzle of the pooled-key tiles: the operand read
+// (32 rows x one chunk per half-wave) is bank-conflict free.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+template <int N>
+__device__ __forceinline__ void sc_ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// x + (x of the lane n below, inside each row of 16 lanes)
+template <int N>
+__device__ __forceinline__ float add_shr(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, false);
+  return x + __builtin_bit_cast(float, y);
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; renumber them so that a
+// contiguous range of logical ids (the row tiles sharing one key chunk) runs
+// on one XCD and its L2.
+__device__ __forceinline__ int xcd_order(int L, int total) {
+  const int q = total >> 3, rem = total & 7, x = L & 7;
+  return x * q + min(x, rem) + (L >> 3);
+}
+
+// One workgroup = 256 centroid rows (4 waves x 64) x one column chunk.  The
+// product is taken transposed, D[key][centroid] = K_tile . C^T: the pooled-key
+// split tiles (32 keys, hi and lo) stream through a four-slot LDS ring filled
+// by direct global->LDS loads and feed the A operand, while each wave keeps
+// its 64 centroid rows (two 32-row sub-tiles) split in registers as the B
+// operand.  Lane l then owns centroid row l % 32 of each sub-tile and 16 of
+// the 32 keys of a step, so the row statistics are two registers.
 template <int D, int PASS>
-__global__ __launch_bounds__(256) void score_kernel(SelArgs a) {
+__global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   constexpr int KS = D / 16;
-  constexpr int BSTR = D + 8;  // LDS row stride (halves)
-  constexpr int CT = 64;       // columns per step
-  __shared__ __attribute__((aligned(16))) half_t bhi[CT * BSTR];
-  __shared__ __attribute__((aligned(16))) half_t blo[CT * BSTR];
-  __shared__ float bcs[CT];
+  constexpr int CT = 32;               // keys per step
+  constexpr int NB = 4;                // ring slots
+  constexpr int ROWB = D * 2;          // bytes of one fp16 row
+  constexpr int TB = CT * ROWB;        // bytes of one hi (or lo) tile
+  constexpr int NCH = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / NCH;        // rows per 1 KB wave load
+  constexpr int LOADS = 2 * CT / RPI;  // wave loads per step (hi + lo)
+  constexpr int LPW = LOADS / 4;       // per wave
+  static_assert(LPW >= 1 && LOADS % 4 == 0, "step shape");
+  __shared__ __attribute__((aligned(16))) unsigned char h0[TB], l0[TB], h1[TB], l1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char h2[TB], l2[TB], h3[TB], l3[TB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int tile = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
-  const int bh = blockIdx.y;
+  const int id = xcd_order(blockIdx.x, gridDim.x);
+  const int tile = id % a.tiles;
+  const int rest = id / a.tiles;
+  const int chunk = rest % a.nchunk, bh = rest / a.nchunk;
   const int R = a.R, M = a.M, C = a.C;
-  const int rho0 = tile * 128 + wave * 32;
+  const int rho0 = tile * 256 + wave * 64;
+  const int cbeg = chunk * a.chunk_cols;
+  const int cend = min(M, cbeg + a.chunk_cols);
+  const int nsteps = (cend - cbeg + CT - 1) / CT;
+  const unsigned char *khi = (const unsigned char *)(a.kb_hi + (size_t)bh * M * D);
+  const unsigned char *klo = (const unsigned char *)(a.kb_lo + (size_t)bh * M * D);
+  // key-tile scales, read through the constant address space so that the
+  // uniform per-step read is a scalar load: a vector load here would have to
+  // wait for the ring's outstanding tile loads
+  typedef const __attribute__((address_space(4))) float cfloat_t;
+  cfloat_t *kcs = (cfloat_t *)(a.kb_cs + (size_t)bh * a.ktiles + cbeg / CT);
 
-  // A operand: centroid rows (hi, lo)
-  f16x8 ahi[KS], alo[KS];
-  {
-    const int rho = rho0 + local_row(l32);
+  auto hslot = [&](auto c) -> unsigned char * {
+    constexpr int S = decltype(c)::value;
+    return S == 0 ? h0 : S == 1 ? h1 : S == 2 ? h2 : h3;
+  };
+  auto lslot = [&](auto c) -> unsigned char * {
+    constexpr int S = decltype(c)::value;
+    return S == 0 ? l0 : S == 1 ? l1 : S == 2 ? l2 : l3;
+  };
+
+  // gather of step k into slot S: wave loads u = wave * LPW + j, each lane
+  // one 16-byte chunk at a fixed offset inside the 32-key tile.  Keys past
+  // the chunk end (ragged last step) read the next rows or the 32-row pad
+  // after the split arrays and are masked in the epilogue.
+  unsigned koff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int u = wave * LPW + j;
+    const int r = (u % (LOADS / 2)) * RPI + lane / NCH;  // tile row
+    koff[j] = (unsigned)(r * ROWB + (((lane % NCH) ^ swz_k<D>(r)) << 4));
+  }
+  auto issue = [&](auto slot_c, int k) {
+    unsigned char *ht = hslot(slot_c);
+    unsigned char *lt = lslot(slot_c);
+    const size_t tile_off = (size_t)(cbeg + k * CT) * ROWB;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int u = wave * LPW + j;
+      const bool hi = u < LOADS / 2;
+      const int dst = (u % (LOADS / 2)) * RPI * ROWB;  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const void *)((hi ? khi : klo) + tile_off + koff[j]),
+                                       (lds_void_t *)((hi ? ht : lt) + dst), 16, 0, 0);
+    }
+  };
+
+  // B operand: centroid rows rho0 + 32 u + l32, dims 16 ks + 8 hh + e, split
+  // into fp16 halves at one power-of-two scale per 32-row sub-tile (its
+  // largest magnitude lands in [2^10, 2^11))
+  f16x8 chi[2][KS], clo[2][KS];
+  float rs[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rho = rho0 + 32 * u + l32;
     const bool ok = rho < R;
-    const size_t o = ((size_t)bh * R + (ok ? rho : 0)) * D + hh * 8;
+    const float *src = a.ce_f + ((size_t)bh * R + (ok ? rho : 0)) * D + hh * 8;
+    f32x4 x[KS][2];
+    float amax = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-      if (ok) {
-        vh = ld16(a.ce_hi + o + ks * 16);
-        vl = ld16(a.ce_lo + o + ks * 16);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        x[ks][hf] = ok ? *(const f32x4 *)(src + ks * 16 + hf * 4) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[ks][hf][e]));
       }
-      ahi[ks] = as_f16x8(vh);
-      alo[ks] = as_f16x8(vl);
+    }
+    const int ex = row_exponent(wave_max_f(amax));
+    rs[u] = ldexpf(a.scale_log2, -ex);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        half_t hi, lo;
+        split_f16(x[ks][e >> 2][e & 3], ex, hi, lo);
+        chi[u][ks][e] = hi;
+        clo[u][ks][e] = lo;
+      }
     }
   }
-  // per-lane rows 16 hh + r
-  float rs[16];
-  float stA[16], stB[16];  // PASS 0: running max / sum ; PASS 1: beta
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rho = rho0 + 16 * hh + r;
-    rs[r] = rho < R ? a.ce_rs[(size_t)bh * R + rho] : 0.f;
-    stA[r] = -__builtin_inff();
-    stB[r] = 0.f;
-  }
+
+  // row statistics of this lane's two centroid rows; a finite floor for the
+  // running maximum keeps 2^(t - m) free of inf - inf
+  constexpr float kFloor = -0x1p100f;
+  float st_m[2] = {kFloor, kFloor}, st_z[2] = {0.f, 0.f};
   if (PASS == 1) {
+    // merge the chunk statistics: beta = max + log2(sum) - log2(share)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rho = rho0 + 16 * hh + r;
+    for (int u = 0; u < 2; ++u) {
+      const int rho = rho0 + 32 * u + l32;
       float beta = __builtin_inff();
       if (rho < R) {
-        float m = -__builtin_inff();
-        for (int c = 0; c < a.nchunk; ++c)
-          m = fmaxf(m, a.stats[((size_t)bh * a.nchunk + c) * R + rho].x);
+        float m = kFloor;
+        for (int c = 0; c < a.nchunk; ++c) m = fmaxf(m, a.stats[((size_t)bh * a.nchunk + c) * R + rho].x);
         float z = 0.f;
         for (int c = 0; c < a.nchunk; ++c) {
           const float2 p = a.stats[((size_t)bh * a.nchunk + c) * R + rho];
-          if (p.x != -__builtin_inff()) z += p.y * __builtin_amdgcn_exp2f(p.x - m);
+          z += p.y * __builtin_amdgcn_exp2f(p.x - m);
         }
         const float w = a.ce_w[(size_t)bh * R + rho];
         if (w > 0.f && z > 0.f) beta = m + __builtin_log2f(z) - __builtin_log2f(w);
       }
-      stA[r] = beta;
+      st_m[u] = beta;
     }
   }
 
-  const int c0 = chunk * a.chunk_cols;
-  const int c1 = min(M, c0 + a.chunk_cols);
-  for (int cb = c0; cb < c1; cb += CT) {
-    __syncthreads();
-    // stage CT columns of the pooled-key split into LDS
-    constexpr int CH = D / 8;
-    for (int e = tid; e < CT * CH; e += 256) {
-      const int col = e / CH, ch = e % CH;
-      const int j = cb + col;
-      u32x4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-      if (j < c1) {
-        const size_t o = ((size_t)bh * M + j) * D + ch * 8;
-        vh = ld16(a.kb_hi + o);
-        vl = ld16(a.kb_lo + o);
-      }
-      st16(&bhi[col * BSTR + ch * 8], vh);
-      st16(&blo[col * BSTR + ch * 8], vl);
+  // logits of sub-tile u at step k -> statistics (sweep 1) or scores (sweep 2).
+  // Register r holds key 8 (r / 4) + 4 hh + r % 4 of the step.
+  auto epilogue = [&](const f32x16 &acc0, const f32x16 &acc1, float f, int k, int u) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = __builtin_fmaf(acc1[r], 0x1p-11f, acc0[r]);
+    const int c0 = cbeg + k * CT + 4 * hh;  // key of register 0
+    if (cbeg + k * CT + CT > cend) {       // ragged last step of the chunk
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = c0 + 8 * (r >> 2) + (r & 3) < cend ? v[r] : -__builtin_inff();
     }
-    if (tid < CT) bcs[tid] = (cb + tid < c1) ? a.kb_cs[(size_t)bh * M + cb + tid] : 0.f;
-    __syncthreads();
-
-    float tv[2][16];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      f32x16 acc0, acc1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc0[r] = 0.f;
-        acc1[r] = 0.f;
-      }
-      const int col = tt * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 bh16 = as_f16x8(ld16(&bhi[col * BSTR + ks * 16 + hh * 8]));
-        const f16x8 bl16 = as_f16x8(ld16(&blo[col * BSTR + ks * 16 + hh * 8]));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bh16, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bl16, acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[ks], bh16, acc1, 0, 0, 0);
-      }
-      const bool valid = cb + col < c1;
-      const float cs = bcs[col];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = __builtin_fmaf(acc1[r], 0x1p-11f, acc0[r]);
-        tv[tt][r] = valid ? (v * rs[r]) * cs : -__builtin_inff();
-      }
-    }
-
     if (PASS == 0) {
+      float mx = v[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float mt = fmaxf(tv[0][r], tv[1][r]);
-        const float mn = fmaxf(stA[r], mt);
-        if (mn != -__builtin_inff()) {
-          stB[r] = stB[r] * __builtin_amdgcn_exp2f(stA[r] - mn) +
-                   __builtin_amdgcn_exp2f(tv[0][r] - mn) + __builtin_amdgcn_exp2f(tv[1][r] - mn);
-          stA[r] = mn;
-        }
-      }
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, v[r]);
+      const float mnew = fmaxf(st_m[u], mx * f);  // f > 0
+      float z = st_z[u] * __builtin_amdgcn_exp2f(st_m[u] - mnew);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], f, -mnew));
+      st_m[u] = mnew;
+      st_z[u] = z;
     } else {
+      float e[16];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int j = cb + tt * 32 + l32;
-        const bool valid = j < c1;
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], f, -st_m[u]));
+      // a query block's C clusters are C consecutive lanes: prefix sums
+      // inside rows of 16 lanes leave each block's total in its last lane
+      if (C >= 2) {
 #pragma unroll
-        for (int g = 0; g < 16; g += 1) {
-          if (g % C) continue;  // groups of C registers = one query block
-          float sacc = 0.f;
-          for (int q2 = 0; q2 < C; ++q2) sacc += __builtin_amdgcn_exp2f(tv[tt][g + q2] - stA[g + q2]);
-          const int rho = rho0 + 16 * hh + g;
-          const int qbk = rho / C;
-          if (valid && rho < R) a.scores[((size_t)bh * a.nqb + qbk) * M + j] = sacc;
+        for (int r = 0; r < 16; ++r) e[r] = add_shr<1>(e[r]);
+      }
+      if (C >= 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = add_shr<2>(e[r]);
+      }
+      if (C >= 8) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = add_shr<4>(e[r]);
+      }
+      if (C >= 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = add_shr<8>(e[r]);
+      }
+      const int rho = rho0 + 32 * u + l32;
+      if ((l32 & (C - 1)) == C - 1 && rho < R) {
+        float *dst = a.scores + ((size_t)bh * a.nqb + rho / C) * M;
+        if (c0 - 4 * hh + CT <= cend && (M & 3) == 0) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4 *)(dst + c0 + 8 * g) = (f32x4){e[4 * g], e[4 * g + 1], e[4 * g + 2], e[4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int col = c0 + 8 * (r >> 2) + (r & 3);
+            if (col < cend) dst[col] = e[r];
+          }
         }
       }
     }
+  };
+
+  // one step: wait for its slot, prefetch NB - 1 steps ahead, compute
+  auto step = [&](auto slot_c, int k) {
+    constexpr int S = decltype(slot_c)::value;
+    constexpr int SN = (S + NB - 1) % NB;
+    const int ahead = min(NB - 2, nsteps - 1 - k);  // steps after k already requested
+    if (ahead >= 2) sc_ring_barrier<2 * LPW>();
+    else if (ahead == 1) sc_ring_barrier<LPW>();
+    else sc_ring_barrier<0>();
+    if (k + NB - 1 < nsteps) issue(std::integral_constant<int, SN>(), k + NB - 1);
+    const unsigned char *ht = hslot(slot_c);
+    const unsigned char *lt = lslot(slot_c);
+    const float cs = kcs[k];  // key-tile scale (a power of two)
+    f32x16 acc0[2], acc1[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[u][r] = 0.f;
+        acc1[u][r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = ((2 * ks + hh) ^ swz_k<D>(l32)) << 4;
+      const f16x8 kh = as_f16x8(*(const u32x4 *)(ht + l32 * ROWB + ch));
+      const f16x8 kl = as_f16x8(*(const u32x4 *)(lt + l32 * ROWB + ch));
+      // the two updates of each acc1 are kept apart in the issue order
+      acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, clo[0][ks], acc1[0], 0, 0, 0);
+      acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, clo[1][ks], acc1[1], 0, 0, 0);
+      acc0[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, chi[0][ks], acc0[0], 0, 0, 0);
+      acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, chi[1][ks], acc0[1], 0, 0, 0);
+      acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, chi[0][ks], acc1[0], 0, 0, 0);
+      acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, chi[1][ks], acc1[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) epilogue(acc0[u], acc1[u], rs[u] * cs, k, u);
+  };
+
+  for (int k = 0; k < NB - 1 && k < nsteps; ++k) {
+    switch (k) {
+      case 0: issue(std::integral_constant<int, 0>(), 0); break;
+      case 1: issue(std::integral_constant<int, 1>(), 1); break;
+      default: issue(std::integral_constant<int, 2>(), 2); break;
+    }
+  }
+  for (int k = 0; k < nsteps; k += NB) {
+    step(std::integral_constant<int, 0>(), k);
+    if (k + 1 < nsteps) step(std::integral_constant<int, 1>(), k + 1);
+    if (k + 2 < nsteps) step(std::integral_constant<int, 2>(), k + 2);
+    if (k + 3 < nsteps) step(std::integral_constant<int, 3>(), k + 3);
   }
 
   if (PASS == 0) {
-    // merge the 32 lanes of each half (same rows, different columns)
+    // lanes l and l + 32 hold the same rows (different keys): merge, store
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float m = stA[r], z = stB[r];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        const float m2 = __shfl_xor(m, o, 64);
-        const float z2 = __shfl_xor(z, o, 64);
-        const float mn = fmaxf(m, m2);
-        if (mn != -__builtin_inff()) {
-          const float za = m == -__builtin_inff() ? 0.f : z * __builtin_amdgcn_exp2f(m - mn);
-          const float zb = m2 == -__builtin_inff() ? 0.f : z2 * __builtin_amdgcn_exp2f(m2 - mn);
-          z = za + zb;
-          m = mn;
-        }
-      }
-      stA[r] = m;
-      stB[r] = z;
-    }
-    if (l32 == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rho = rho0 + 16 * hh + r;
-        if (rho < R) a.stats[((size_t)bh * a.nchunk + chunk) * R + rho] = make_float2(stA[r], stB[r]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const float m = st_m[u], z = st_z[u];
+      const float m2 = xor32(m), z2 = xor32(z);
+      const float mn = fmaxf(m, m2);
+      const float zz = z * __builtin_amdgcn_exp2f(m - mn) + z2 * __builtin_amdgcn_exp2f(m2 - mn);
+      const int rho = rho0 + 32 * u + l32;
+      if (hh == 0 && rho < R) a.stats[((size_t)bh * a.nchunk + chunk) * R + rho] = make_float2(mn, zz);
     }
   }
 }
 
 struct Layout {
-  size_t kb_hi, kb_lo, kb_cs, ce_hi, ce_lo, ce_rs, ce_w, stats, total;
-  int nqb, M, R, nchunk, chunk_cols, tiles;
+  size_t kb_hi, kb_lo, kb_cs, ce_f, ce_w, stats, total;
+  int nqb, M, R, nchunk, chunk_cols, tiles, ktiles;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -437,23 +563,28 @@ Layout make_layout(int B, int H, int N, int d, int kv_block, int C) {
   L.nqb = (N + 127) / 128;
   L.M = (N + kv_block - 1) / kv_block;
   L.R = L.nqb * C;
-  L.tiles = (L.R + 127) / 128;
-  // column chunks: enough workgroups to fill the chip, whole 64-column steps
+  L.tiles = (L.R + 255) / 256;
+  L.ktiles = (L.M + 31) / 32;
+  // column chunks of whole 32-key steps: at least two rounds of the 512
+  // resident workgroups (2 per CU), preferring a nearly full last round
   const long long wg = (long long)L.tiles * (long long)BH;
-  int nchunk = (int)((2048 + wg - 1) / wg);
-  const int steps = (L.M + 63) / 64;
-  if (nchunk < 1) nchunk = 1;
-  if (nchunk > steps) nchunk = steps;
-  if (nchunk > 64) nchunk = 64;
-  L.chunk_cols = ((steps + nchunk - 1) / nchunk) * 64;
+  const int steps = L.ktiles;
+  int nchunk = 1;
+  for (int n = 1; n <= 64 && n <= steps; ++n) {
+    nchunk = n;
+    const long long tot = wg * n;
+    if (tot < 1024) continue;
+    const long long rounds = (tot + 511) / 512;
+    if (tot * 10 >= rounds * 512 * 9) break;  // rounds at least 90 % occupied
+  }
+  L.chunk_cols = ((steps + nchunk - 1) / nchunk) * 32;
   L.nchunk = (L.M + L.chunk_cols - 1) / L.chunk_cols;
   size_t off = 0;
-  L.kb_hi = off; off += al256(BH * L.M * d * 2);
-  L.kb_lo = off; off += al256(BH * L.M * d * 2);
-  L.kb_cs = off; off += al256(BH * L.M * 4);
-  L.ce_hi = off; off += al256(BH * L.R * d * 2);
-  L.ce_lo = off; off += al256(BH * L.R * d * 2);
-  L.ce_rs = off; off += al256(BH * L.R * 4);
+  // split keys, each array padded by one 32-key tile (ragged-step reads)
+  L.kb_hi = off; off += al256((BH * L.M + 32) * d * 2);
+  L.kb_lo = off; off += al256((BH * L.M + 32) * d * 2);
+  L.kb_cs = off; off += al256(BH * L.ktiles * 4);
+  L.ce_f = off; off += al256(BH * L.R * d * 4);
   L.ce_w = off; off += al256(BH * L.R * 4);
   L.stats = off; off += al256(BH * (size_t)L.nchunk * L.R * 8);
   L.total = off;
@@ -485,20 +616,21 @@ int launch_select_scores(const void *q, const void *k, int B, int H, int N, int 
   a.nchunk = L.nchunk;
   a.chunk_cols = L.chunk_cols;
   a.tiles = L.tiles;
+  a.ktiles = L.ktiles;
   a.scores = scores;
   a.centroids = centroids;
   a.weights = weights;
   a.kb_hi = (half_t *)(ws + L.kb_hi);
   a.kb_lo = (half_t *)(ws + L.kb_lo);
   a.kb_cs = (float *)(ws + L.kb_cs);
-  a.ce_hi = (half_t *)(ws + L.ce_hi);
-  a.ce_lo = (half_t *)(ws + L.ce_lo);
-  a.ce_rs = (float *)(ws + L.ce_rs);
+  a.ce_f = (float *)(ws + L.ce_f);
   a.ce_w = (float *)(ws + L.ce_w);
   a.stats = (float2 *)(ws + L.stats);
   a.scale_log2 = kLog2e / sqrtf((float)d);
   const unsigned BH = (unsigned)(B * H);
-  const dim3 gpool((L.M + 3) / 4, BH), gkm(L.nqb, BH), gsc(L.tiles * L.nchunk, BH);
+  const long long nsc = (long long)L.tiles * L.nchunk * BH;
+  if (nsc > 0x7fffffffLL) return BSA_ERR_UNSUPPORTED;
+  const dim3 gpool(L.ktiles, BH), gkm(L.nqb, BH), gsc((unsigned)nsc);
   if (d == 128) {
     hipLaunchKernelGGL(pool_split_kernel<128>, gpool, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(kmeans_kernel<128>, gkm, dim3(256), 0, stream, a);
