@@ -46,7 +46,7 @@ lib.bsa_sip_plan.argtypes = [_p, _i, _i, _i, _i, _i, _i, _u64, _p, _p, _p, _p, _
 lib.bsa_attn_fwd.restype = _i
 lib.bsa_attn_fwd.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _f, _p, _p, _p]
 lib.bsa_basa_layout.restype = _i
-lib.bsa_basa_layout.argtypes = [_i] * 12 + [_pi] * 5 + [_psz]
+lib.bsa_basa_layout.argtypes = [_i] * 12 + [_pi] * 4 + [_psz]
 lib.bsa_basa_plan.restype = _i
 lib.bsa_basa_plan.argtypes = [_p, _p, _p] + [_i] * 14 + [_p] * 6 + [_p, _sz, _p]
 lib.bsa_window_unpermute.restype = _i
@@ -180,12 +180,12 @@ def bsa_attn_fwd(q, k, v, idx, bias, count, q_block=128, kv_block=4, softmax_sca
 
 
 def bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block=4, B=1, H=1):
-    vals = [ctypes.c_int(0) for _ in range(5)]
+    vals = [ctypes.c_int(0) for _ in range(4)]
     ws = ctypes.c_size_t(0)
     _check(lib.bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H,
                                *[ctypes.byref(x) for x in vals], ctypes.byref(ws)),
            "bsa_basa_layout")
-    keys = ["nwin", "Nq_pad", "Nk_valid", "Nk_alloc", "max_blocks"]
+    keys = ["nwin", "Nq_pad", "Nk", "max_blocks"]
     out = {k: v.value for k, v in zip(keys, vals)}
     out["workspace"] = ws.value
     return out
@@ -201,7 +201,7 @@ def bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
     lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
     dev = q.device
     qp = torch.empty((B, H, lay["Nq_pad"], d), dtype=torch.bfloat16, device=dev)
-    kp = torch.empty((B, H, lay["Nk_alloc"], d), dtype=torch.bfloat16, device=dev)
+    kp = torch.empty((B, H, lay["Nk"], d), dtype=torch.bfloat16, device=dev)
     vp = torch.empty_like(kp)
     nqb = lay["Nq_pad"] // 128
     idx = torch.empty((B, H, nqb, lay["max_blocks"]), dtype=torch.int32, device=dev)

@@ -23,8 +23,8 @@ int launch_select_scores(const void *q, const void *k, int B, int H, int N, int 
                          float *weights, void *workspace, hipStream_t stream);
 size_t select_workspace_bytes(int B, int H, int N, int d, int kv_block, int n_clusters);
 int basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
-                int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
-                int *Nk_alloc, int *max_blocks, size_t *workspace);
+                int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk, int *max_blocks,
+                size_t *workspace);
 int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
                      int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
                      int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
@@ -136,17 +136,16 @@ int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d, 
 }
 
 int bsa_basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
-                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
-                    int *Nk_alloc, int *max_blocks, size_t *workspace) {
-  if (!nwin || !Nq_pad || !Nk_valid || !Nk_alloc || !max_blocks || !workspace)
-    return BSA_ERR_ARG;
+                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk,
+                    int *max_blocks, size_t *workspace) {
+  if (!nwin || !Nq_pad || !Nk || !max_blocks || !workspace) return BSA_ERR_ARG;
   if (T < 1 || Hg < 1 || Wg < 1 || wh < 1 || ww < 1 || ph < 1 || pw < 1 || topk < 0 || B < 1 ||
       H < 1)
     return BSA_ERR_ARG;
   if (wh > Hg || ww > Wg) return BSA_ERR_ARG;
   if (!head_dim_ok(d) || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
-  return bsa::basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, nwin, Nq_pad,
-                          Nk_valid, Nk_alloc, max_blocks, workspace);
+  return bsa::basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, nwin, Nq_pad, Nk,
+                          max_blocks, workspace);
 }
 
 int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
@@ -154,10 +153,10 @@ int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int
                   int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
                   int32_t *routes, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !qp || !kp || !vp || !idx || !count) return BSA_ERR_ARG;
-  int nwin, nqp, nkv, nka, mb;
+  int nwin, nqp, nk, mb;
   size_t ws;
-  int st = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, &nwin, &nqp, &nkv,
-                           &nka, &mb, &ws);
+  int st = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, &nwin, &nqp, &nk,
+                           &mb, &ws);
   if (st != BSA_OK) return st;
   if (topk > nwin - 1) return BSA_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||

@@ -188,7 +188,9 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
  * multiple of 128, windows in row-major window order.  The pooled memory G
  * (per-frame non-overlapping ph x pw spatial means of K and V on the
  * unshifted grid, T * ceil(Hg/ph) * ceil(Wg/pw) tokens, raster order) is
- * appended after the last window in the key/value buffers.  Every query
+ * appended after the last window in the key/value buffers (one KV block may
+ * straddle the end: the attention kernel masks keys at or past Nk and reads
+ * no row there).  Every query
  * window routes to the `topk` other windows with the largest
  * mean(Q_w) . mean(K_w') (fp32, fixed order: window-local token order sums,
  * one IEEE division, ascending-dim dot product without fused multiply-add;
@@ -199,22 +201,23 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
  * bsa_basa_layout (host, no GPU) reports the sizes:
  *   nwin         number of windows;
  *   Nq_pad       padded query rows (= padded window-major rows);
- *   Nk_valid     Nq_pad + pooled tokens (keys at or beyond are masked);
- *   Nk_alloc     rows to allocate for kp/vp (Nk_valid rounded up to kv_block);
+ *   Nk           key/value rows: Nq_pad + pooled tokens;
  *   max_blocks   list stride;
  *   workspace    bytes of device scratch bsa_basa_plan needs.
  * kv_block must divide every window's token count and 128.
  *
  * bsa_basa_plan: q,k,v [B,H,N,d] bf16 -> qp [B,H,Nq_pad,d], kp, vp
- * [B,H,Nk_alloc,d] bf16 (caller-allocated), idx [B,H,Nq_pad/128,max_blocks]
- * int32, count [B,H,Nq_pad/128] int32, routes optional [B,H,nwin,topk] int32.
- * Then bsa_attn_fwd(qp, kp, vp, B, H, Nq_pad, Nk_valid, d, 128, kv_block,
+ * [B,H,Nk,d] bf16 (caller-allocated), idx [B,H,Nq_pad/128,max_blocks]
+ * int32 (unused tail entries -1), count [B,H,Nq_pad/128] int32, routes
+ * optional [B,H,nwin,topk] int32 (rank order, best first).  Pad rows of qp,
+ * kp and vp are zero.  topk <= min(64, nwin - 1).
+ * Then bsa_attn_fwd(qp, kp, vp, B, H, Nq_pad, Nk, d, 128, kv_block,
  * idx, NULL, count, max_blocks, ...) and bsa_window_unpermute() give the
  * output in raster order.
  * --------------------------------------------------------------------- */
 int bsa_basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
-                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk_valid,
-                    int *Nk_alloc, int *max_blocks, size_t *workspace /* all host out */);
+                    int kv_block, int B, int H, int *nwin, int *Nq_pad, int *Nk,
+                    int *max_blocks, size_t *workspace /* all host out */);
 
 int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
                   int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,

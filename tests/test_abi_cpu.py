@@ -113,8 +113,7 @@ def test_basa_layout_of_the_1664x960_grid(bsa):
     lay = bsa.bsa_basa_layout(21, 60, 104, 128, 10, 10, 4, 4, 2, 4, 1, 12)
     assert lay["nwin"] == 66
     assert lay["Nq_pad"] == 135936          # 60 windows of 2176 rows + 6 of 896
-    assert lay["Nk_valid"] == 135936 + 8190
-    assert lay["Nk_alloc"] == 135936 + 8192
+    assert lay["Nk"] == 135936 + 8190        # + 21 x 15 x 26 pooled tokens
     assert lay["max_blocks"] == 3 * 525 + 2048
 
 

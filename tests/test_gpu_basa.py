@@ -1,0 +1,157 @@
+"""GPU parity of the BASA path (bsa_basa_plan -> bsa_attn_fwd ->
+bsa_window_unpermute) against the definition-based oracle (oracle/basa.py),
+which builds no lists: windows of the rolled grid, routed windows and the
+pooled memory are gathered directly and attended in fp64.
+
+Bit-exact: routes (fp32 routing in the stated order on both sides), the
+window-major copies of Q/K/V and their zero pad rows, the block lists.
+Pooled K/V rows: the device stores the fp32 cell mean rounded to bf16; they
+are checked against the oracle's fp64 cell mean within one bf16 step.
+Attention output: within the attention tolerances."""
+import numpy as np
+import pytest
+
+from oracle import basa as obasa
+from synth import CONFIGS, bf16_bits_to_f32, bf16_bits_to_f64, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_mean_amd as bsa
+    from tests import _gpu
+    return bsa, _gpu, torch
+
+
+def _window_rows(T, Hg, Wg, wh, ww):
+    """(first padded row, token count) of every window, window-major order."""
+    nwy, nwx = obasa.window_grid(Hg, Wg, wh, ww)
+    out, off = [], 0
+    for a in range(nwy):
+        for b in range(nwx):
+            n = T * (min(Hg, (a + 1) * wh) - a * wh) * (min(Wg, (b + 1) * ww) - b * ww)
+            out.append((off, n))
+            off += -(-n // 128) * 128
+    return out, off
+
+
+def _expected_lists(T, Hg, Wg, wh, ww, routes, npool, kvb, nq_pad):
+    wins, _ = _window_rows(T, Hg, Wg, wh, ww)
+    lists = []
+    for w, (off, n) in enumerate(wins):
+        blocks = list(range(off // kvb, (off + n) // kvb))
+        for j in sorted(routes[w]):
+            o2, n2 = wins[j]
+            blocks += range(o2 // kvb, (o2 + n2) // kvb)
+        blocks += range(nq_pad // kvb, nq_pad // kvb + -(-npool // kvb))
+        for _ in range(-(-n // 128)):
+            lists.append(blocks)
+    return lists
+
+
+def _run_basa(env, qb, kb, vb, geo):
+    bsa, g, torch = env
+    T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kvb = (geo[x] for x in
+                                                    ("T", "Hg", "Wg", "wh", "ww", "dy", "dx", "ph",
+                                                     "pw", "topk", "kvb"))
+    q, k, v = g.to_dev_bf16(qb), g.to_dev_bf16(kb), g.to_dev_bf16(vb)
+    plan = bsa.bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=kvb,
+                             want_routes=True)
+    outp, _ = bsa.bsa_attn_fwd(plan["qp"], plan["kp"], plan["vp"], plan["idx"], None,
+                               plan["count"], 128, kvb)
+    out = bsa.bsa_window_unpermute(outp, T, Hg, Wg, wh, ww, dy, dx)
+    torch.cuda.synchronize()
+    return plan, out
+
+
+SMALL = [
+    dict(T=2, Hg=12, Wg=20, wh=4, ww=6, dy=1, dx=3, ph=5, pw=4, topk=2, kvb=4, d=64, H=2),
+    dict(T=2, Hg=12, Wg=20, wh=4, ww=6, dy=-5, dx=17, ph=5, pw=4, topk=2, kvb=8, d=128, H=2),
+    dict(T=3, Hg=10, Wg=16, wh=5, ww=8, dy=2, dx=0, ph=2, pw=3, topk=0, kvb=4, d=128, H=1),
+    dict(T=1, Hg=16, Wg=16, wh=4, ww=4, dy=3, dx=1, ph=4, pw=4, topk=5, kvb=16, d=64, H=2),
+]
+
+
+@pytest.mark.parametrize("geo", SMALL, ids=lambda x: f"{x['Hg']}x{x['Wg']}w{x['wh']}x{x['ww']}"
+                         f"k{x['topk']}d{x['d']}kv{x['kvb']}")
+def test_basa_small_matches_oracle(env, geo):
+    bsa, g, torch = env
+    g.say(f"case basa small {geo}")
+    T, Hg, Wg, wh, ww, dy, dx = (geo[x] for x in ("T", "Hg", "Wg", "wh", "ww", "dy", "dx"))
+    ph, pw, topk, kvb, d, H = (geo[x] for x in ("ph", "pw", "topk", "kvb", "d", "H"))
+    qb, kb, vb = make_qkv(T, Hg, Wg, H, d, seed=Hg * 7 + d + topk)
+    plan, out = _run_basa(env, qb, kb, vb, geo)
+    N = T * Hg * Wg
+    members = obasa.window_members(T, Hg, Wg, wh, ww, dy % Hg, dx % Wg)
+    wins, nq_pad = _window_rows(T, Hg, Wg, wh, ww)
+    assert plan["Nq_pad"] == nq_pad and plan["nwin"] == len(members)
+    qp = plan["qp"].view(torch.int16).cpu().numpy().view(np.uint16)
+    kp = plan["kp"].view(torch.int16).cpu().numpy().view(np.uint16)
+    vp = plan["vp"].view(torch.int16).cpu().numpy().view(np.uint16)
+    idx = plan["idx"].cpu().numpy()
+    cnt = plan["count"].cpu().numpy()
+    routes = plan["routes"].cpu().numpy() if topk else None
+    got = g.from_dev_bf16(out)
+    for h in range(H):
+        q32, k32 = bf16_bits_to_f32(qb[0, h]), bf16_bits_to_f32(kb[0, h])
+        want_routes = obasa.route(q32, k32, members, topk) if topk else np.zeros((len(members), 0), int)
+        if topk:
+            np.testing.assert_array_equal(routes[0, h], want_routes)
+        # window-major copies and zero pad rows
+        for w, (off, n) in enumerate(wins):
+            pad = -(-n // 128) * 128
+            for src, dst in ((qb, qp), (kb, kp), (vb, vp)):
+                np.testing.assert_array_equal(dst[0, h, off:off + n], src[0, h, members[w]])
+                assert not dst[0, h, off + n:off + pad].any()
+        # pooled memory within one bf16 step (8 significant bits) of the fp64 cell means
+        npool = T * -(-Hg // ph) * -(-Wg // pw)
+        for src, dst in ((kb, kp), (vb, vp)):
+            gm = obasa.pooled_memory(bf16_bits_to_f64(src[0, h]), T, Hg, Wg, ph, pw)
+            dev = bf16_bits_to_f64(dst[0, h, nq_pad:])
+            assert dev.shape == gm.shape == (npool, d)
+            ulp = np.ldexp(1.0, np.frexp(gm)[1] - 8)
+            assert (np.abs(dev - gm) <= ulp).all()
+        # block lists
+        lists = _expected_lists(T, Hg, Wg, wh, ww, want_routes, npool, kvb, nq_pad)
+        assert len(lists) == idx.shape[2]
+        for i, blocks in enumerate(lists):
+            assert cnt[0, h, i] == len(blocks)
+            np.testing.assert_array_equal(idx[0, h, i, :len(blocks)], blocks)
+            assert (idx[0, h, i, len(blocks):] == -1).all()
+        want, _ = obasa.basa_attn(qb[0, h], kb[0, h], vb[0, h], T, Hg, Wg, wh, ww, dy % Hg,
+                                  dx % Wg, ph, pw, topk, routes=want_routes)
+        assert not np.isnan(want).any()
+        g.assert_attn_close(got[0, h], want, f"basa small head {h}")
+    assert got.shape == (1, H, N, d)
+
+
+def test_basa_full_size_sampled_windows(env):
+    """The 1664x960 / 81-frame latent (21 x 60 x 104), one head, w = (10, 10),
+    Delta = (3, 7), pooled 4 x 4, top-2: routes of every window exact, output
+    rows of sampled windows (full, ragged last column, last) against the
+    oracle."""
+    bsa, g, torch = env
+    c = CONFIGS["basa_1664x960"]
+    geo = dict(T=c["T"], Hg=c["Hg"], Wg=c["Wg"], wh=c["wh"], ww=c["ww"], dy=c["dy"], dx=c["dx"],
+               ph=c["ph"], pw=c["pw"], topk=c["topk"], kvb=c["kv_block"])
+    g.say(f"case basa full size {geo}")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=11)
+    plan, out = _run_basa(env, qb, kb, vb, geo)
+    assert plan["nwin"] == 66 and plan["Nq_pad"] == 135936
+    cnt = plan["count"].cpu().numpy()
+    assert cnt.max() <= plan["max_blocks"]
+    members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
+    want_routes = obasa.route(bf16_bits_to_f32(qb[0, 0]), bf16_bits_to_f32(kb[0, 0]), members,
+                              c["topk"])
+    np.testing.assert_array_equal(plan["routes"].cpu().numpy()[0, 0], want_routes)
+    got = g.from_dev_bf16(out)[0, 0]
+    wins = [0, 10, 37, 65]
+    want, _ = obasa.basa_attn(qb[0, 0], kb[0, 0], vb[0, 0], c["T"], c["Hg"], c["Wg"], c["wh"],
+                              c["ww"], c["dy"], c["dx"], c["ph"], c["pw"], c["topk"],
+                              windows=wins, routes=want_routes)
+    rows = np.concatenate([members[w] for w in wins])
+    g.assert_attn_close(got[rows], want[rows], "basa full size sampled windows")
