@@ -16,13 +16,16 @@
 //     the largest x with cond(x) is bracketed by secant steps down from
 //     T / s and a bisection over fp32 bit patterns that stops once no row
 //     value lies inside the bracket; then r = #{S > x}, T_r = sum_{S <= x} S;
-//   * each bisection step decides cond from an fp64 sum whose rounding
-//     error is bounded; only when the margin is inside that bound is the
-//     sum recomputed exactly (integer superaccumulator, 320 bits in units
-//     of 2^-149, which holds every fp32 value and 2^20 of them);
-//   * T_r is always taken from the superaccumulator and rounded once to
-//     fp64 (round to nearest even); lambda = (s - r) / T_r is one IEEE
-//     division and pi_j = min(1, lambda S_j) one IEEE multiply;
+//   * each search step decides cond from an fp64 sum whose rounding error
+//     is bounded; inside that bound the sum is retaken as a double-double
+//     (error below 2^-90 of the sum), and only when even that cannot
+//     decide, exactly (integer digits, 352 bits in units of 2^-149, which
+//     hold every fp32 value and 2^20 of them);
+//   * T_r is the correctly rounded (nearest even) fp64 value of the exact
+//     sum: read off the double-double when its error interval lies inside
+//     one rounding interval, else from the exact digits; lambda =
+//     (s - r) / T_r is one IEEE division and pi_j = min(1, lambda S_j) one
+//     IEEE multiply;
 //   * Pi_j = floor(pi_j 2^44) and their prefix sums are exact 64-bit
 //     integers; points U + k 2^44 (k < s) pick the blocks, in index order.
 #include "common.h"
@@ -62,15 +65,17 @@ struct PlanArgs {
   double *lambda;
 };
 
+// Small on purpose: with the row (M floats) this stays under half of a
+// CU's LDS, so two rows run per CU.
 struct Shared {
-  uint64_t digits[NDIG * PT];   // per-thread carry-save digits [digit][thread]
-  uint64_t partial[NDIG * (PT / 16)];  // first-level column sums
+  uint64_t wdig[NW][NDIG + 1];  // per-wave digit sums of an exact sum
   uint64_t total[NDIG + 1];     // normalised digits of the last exact sum
   double red_d[NW];
   long long red_l[NW];
   unsigned red_u[NW];
   unsigned red_u2[NW];
-  int flag;
+  long long cl[2][NW];          // alternating buffers of the one-barrier reductions
+  double chi[2][NW], clo[2][NW];
   double bcast_d;
 };
 
@@ -159,6 +164,73 @@ __device__ uint64_t block_exscan_u64(Shared &sh, uint64_t v, uint64_t &total) {
   return base + inc - v;
 }
 
+// One-barrier block reduction of a packed count and a double-double (hi,
+// lo); every thread gets the same result (symmetric butterflies, then the
+// waves in order).  The two buffers alternate with `ph`, so a reduction may
+// write before the barrier: the previous reader of that buffer has passed
+// the barrier of the reduction in between.
+__device__ __forceinline__ void two_sum(double a, double b, double &s, double &e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+// (hi, lo) += (bhi, blo) for non-negative double-doubles (symmetric in the
+// two operands, relative error below 6 u^2 per call).
+__device__ __forceinline__ void dd_add(double &hi, double &lo, double bhi, double blo) {
+  double s, e;
+  two_sum(hi, bhi, s, e);
+  e += lo + blo;
+  hi = s + e;
+  lo = e - (hi - s);
+}
+// The same for a packed count and a plain fp64 sum.
+__device__ void block_reduce(Shared &sh, long long &cnt, double &sum, int &ph) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    cnt += __shfl_xor(cnt, o, 64);
+    sum += __shfl_xor(sum, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh.cl[ph][w] = cnt;
+    sh.chi[ph][w] = sum;
+  }
+  __syncthreads();
+  cnt = sh.cl[ph][0];
+  sum = sh.chi[ph][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    cnt += sh.cl[ph][i];
+    sum += sh.chi[ph][i];
+  }
+  ph ^= 1;
+}
+__device__ void block_reduce(Shared &sh, long long &cnt, double &hi, double &lo, int &ph) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const long long c2 = __shfl_xor(cnt, o, 64);
+    const double h2 = __shfl_xor(hi, o, 64), l2 = __shfl_xor(lo, o, 64);
+    cnt += c2;
+    dd_add(hi, lo, h2, l2);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh.cl[ph][w] = cnt;
+    sh.chi[ph][w] = hi;
+    sh.clo[ph][w] = lo;
+  }
+  __syncthreads();
+  cnt = sh.cl[ph][0];
+  hi = sh.chi[ph][0];
+  lo = sh.clo[ph][0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    cnt += sh.cl[ph][i];
+    dd_add(hi, lo, sh.chi[ph][i], sh.clo[ph][i]);
+  }
+  ph ^= 1;
+}
+
 // Row access: thread t owns the contiguous chunk [lo, hi) (a multiple of
 // 4 long, so LDS reads are 16 bytes wide); the row sits in LDS when it
 // fits, else it is re-read from global memory on every pass.
@@ -195,53 +267,83 @@ struct RowView {
   }
 };
 
-// Exact sum of {S_j : S_j < x} (strict) or {S_j <= x} (!strict) into
-// sh.total as 11 normalised 32-bit digits (units of 2^-149).  Each thread
-// accumulates carry-save digits in its own LDS column (no contention); the
-// columns are reduced in two levels.
+// Double-double sum of {S_j < x} (strict) or {S_j <= x} (!strict), with
+// the count of S_j > x.  Per thread: exact two-sums into (hi, lo); then the
+// block reduction.  The result's error is below (chunk^2 + 64) 2^-104 of the
+// sum (chunk = values per thread).
 template <typename Row>
-__device__ __forceinline__ void exact_sum(Shared &sh, const Row &row, float x, bool strict) {
-  const int t = threadIdx.x;
+__device__ void dd_sum(Shared &sh, const Row &row, float x, bool strict, double &hi, double &lo,
+                       long long &ngt, int &ph) {
+  double h = 0.0, l = 0.0;
+  long long c = 0;
+  row.each([&](int, float v) {
+    const bool in = strict ? v < x : v <= x;
+    c += v > x ? 1 : 0;
+    double s2, e;
+    two_sum(h, in ? (double)v : 0.0, s2, e);
+    h = s2;
+    l += e;
+  });
+  const double n = h + l;  // normalise: |l| <= ulp(h) / 2
+  l = l - (n - h);
+  h = n;
+  block_reduce(sh, c, h, l, ph);
+  hi = h;
+  lo = l;
+  ngt = c;
+}
+
+// Exact sum of {S_j < x} (strict) or {S_j <= x} (!strict) into sh.total as
+// 11 normalised 32-bit digits (units of 2^-149).  Only digits dlo..dhi can
+// receive a value (the row's exponent range); each thread accumulates them
+// in registers, then waves and workgroup add them up.
+template <typename Row>
+__device__ void exact_sum(Shared &sh, const Row &row, float x, bool strict, int dlo, int dhi) {
+  uint64_t acc[NDIG + 1];
 #pragma unroll
-  for (int i = 0; i < NDIG; ++i) sh.digits[i * PT + t] = 0ull;
-  row.each([&](int, float s) {
-    if (strict ? !(s < x) : !(s <= x)) return;
-    const unsigned b = __builtin_bit_cast(unsigned, s);
+  for (int i = 0; i <= NDIG; ++i) acc[i] = 0ull;
+  row.each([&](int, float v) {
+    const bool in = strict ? v < x : v <= x;
+    const unsigned b = in ? __builtin_bit_cast(unsigned, v) : 0u;
     const unsigned e = b >> 23;
     const uint64_t mant = e ? ((b & 0x7fffffu) | 0x800000u) : (b & 0x7fffffu);
     const unsigned shift = e ? e - 1 : 0;
-    const uint64_t v = mant << (shift & 31);
-    const unsigned d = shift >> 5;
-    atomicAdd((unsigned long long *)&sh.digits[d * PT + t], (unsigned long long)(v & 0xffffffffull));
-    atomicAdd((unsigned long long *)&sh.digits[(d + 1) * PT + t], (unsigned long long)(v >> 32));
-  });
-  __syncthreads();
-  // level 1: PT/16 partial sums of 16 columns for each digit
-  constexpr int NP = PT / 16;
-  for (int u = t; u < NDIG * NP; u += PT) {
-    const int dg = u / NP, part = u % NP;
-    uint64_t acc = 0;
+    const uint64_t w = mant << (shift & 31);
+    const int d = (int)(shift >> 5);
+    const uint64_t wlo = w & 0xffffffffull, whi = w >> 32;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc += sh.digits[dg * PT + part * 16 + i];
-    sh.partial[dg * NP + part] = acc;
-  }
-  __syncthreads();
-  if (t < NDIG) {  // level 2: one thread per digit
-    uint64_t acc = 0;
-    for (int k = 0; k < NP; ++k) acc += sh.partial[t * NP + k];
-    sh.partial[t * NP] = acc;
-  }
-  __syncthreads();
-  if (t == 0) {  // carry propagation
-    uint64_t carry = 0;
-    for (int i = 0; i < NDIG; ++i) {
-      const uint64_t acc = sh.partial[i * NP] + carry;
-      sh.total[i] = acc & 0xffffffffull;
-      carry = acc >> 32;
+    for (int i = 0; i <= NDIG; ++i) {
+      if (i < dlo || i > dhi) continue;  // uniform
+      acc[i] += (d == i ? wlo : 0ull) + (d + 1 == i ? whi : 0ull);
     }
-    sh.total[NDIG] = carry;
+  });
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i <= NDIG; ++i) {
+    if (i < dlo || i > dhi) continue;
+    long long a = (long long)acc[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+    if ((threadIdx.x & 63) == 0) sh.wdig[wv][i] = (uint64_t)a;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {  // carry propagation
+    uint64_t carry = 0;
+    for (int i = 0; i <= NDIG; ++i) {
+      uint64_t a = carry;
+      if (i >= dlo && i <= dhi)
+        for (int k = 0; k < NW; ++k) a += sh.wdig[k][i];
+      sh.total[i] = a & 0xffffffffull;
+      carry = a >> 32;
+    }
+  }
+  __syncthreads();
+}
+
+// Digit index (32-bit digits, units 2^-149) of the low word of an fp32 value.
+__device__ __forceinline__ int digit_of(unsigned b) {
+  const unsigned e = b >> 23;
+  return (int)((e ? e - 1 : 0) >> 5);
 }
 
 // Correct rounding (nearest even) of the integer held in `dig` (units 2^-149).
@@ -426,30 +528,38 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   }
 
   // cond(x): (s - #{S >= x}) x <= sum_{S < x} S, decided with a certified
-  // fp64 margin or, inside the margin, exactly.  The search below visits
-  // one point per iteration (a single evaluation site keeps the register
-  // footprint of the unrolled row passes small):
-  //   stage 0  x = max S           (true: no saturated block)
+  // fp64 margin or, inside the margin, from a double-double sum and, if
+  // even that cannot decide, exactly.  The search visits one point per
+  // iteration (a single evaluation site keeps the register footprint of
+  // the unrolled row passes small):
+  //   stage 0  x = max S           (true: no saturated block); needed only
+  //            when max S <= T / s, since cond(x) fails for every x > T / s
   //   stage 1  secant steps down from T / s towards the threshold
   //   stage 2  bisection of [blo, bhi) until no row value lies inside
-  //   stage 3  exact sum T_r = sum_{S <= x*}
   // per-thread fp32 partial sums (chunk terms) then an fp64 reduction
   const int chunk = ((M + PT - 1) / PT + 3) & ~3;
   const double err_bound = (ldexp((double)(chunk + 2), -23) + ldexp((double)(M + 2 * PT), -50)) * tot;
+  const double dd_rel = ldexp((double)chunk * (double)chunk + 64.0, -104) * 2.0;  // safety x2
+  const int dlo = digit_of(mnpos), dhi = digit_of(mx) + 1;
   const float fmx = __builtin_bit_cast(float, mx);
   unsigned blo = mnpos, bhi = mx;
   long long ngt_lo = npos, nge_hi = 0;
   float x = fmx;
-  int stage = 0, secant_left = 12;
+  int stage = 0, secant_left = 12, ph = 0;
   float xstar = fmx;
-  while (true) {
-    // ---- one pass at x (stage 3: non-strict exact sum only)
+  {
+    const float x0 = (float)(tot / (double)s * (1.0 + 0x1p-20));  // above T / s
+    if (x0 < fmx && __builtin_bit_cast(unsigned, x0) > blo) {
+      x = x0;
+      stage = 1;
+    }
+  }
+  while (stage != 3) {
+    // ---- one pass at x
     bool holds = true;
-    long long nge = 0, ngt = 0;
+    long long cnt = 0;
     double slt = 0.0;
-    bool need_exact = stage == 3;
-    long long mult = 0;
-    if (stage != 3) {
+    {
       int cge = 0, cgt = 0;
       float sf = 0.f;
       row.each([&](int, float v) {
@@ -458,24 +568,35 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
         cgt += v > x ? 1 : 0;
         sf += ge ? 0.f : v;
       });
-      const long long cnt = block_sum_l(sh, ((long long)cge << 32) | (long long)cgt);
-      slt = block_sum_d(sh, (double)sf);
-      nge = cnt >> 32;
-      ngt = cnt & 0xffffffffll;
-      mult = (long long)s - nge;
-      if (mult > 0) {
-        const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
-        const double diff = lhs - slt;
-        if (diff > err_bound) holds = false;
-        else if (!(diff < -err_bound)) need_exact = true;
-      }
+      cnt = ((long long)cge << 32) | (long long)cgt;
+      slt = (double)sf;
+      block_reduce(sh, cnt, slt, ph);
     }
-    if (need_exact) {
-      exact_sum(sh, row, x, stage != 3);
-      if (stage == 3) break;
-      uint64_t ldig[NDIG + 1];
-      scaled_to_digits((unsigned long long)mult, x, ldig);
-      holds = digits_ge(sh.total, ldig);
+    const long long nge = cnt >> 32, ngt = cnt & 0xffffffffll;
+    const long long mult = (long long)s - nge;
+    if (mult > 0) {
+      const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
+      const double diff = lhs - slt;
+      if (diff > err_bound) {
+        holds = false;
+      } else if (!(diff < -err_bound)) {
+        // inside the margin: double-double sum of {S < x}
+        double thi, tlo;
+        long long unused;
+        dd_sum(sh, row, x, true, thi, tlo, unused, ph);
+        double p, q;
+        two_sum(lhs, -thi, p, q);  // lhs - thi = p + q exactly
+        const double d = p + (q - tlo);
+        const double margin = dd_rel * thi + 0x1p-100 * (lhs + thi);
+        if (d > margin) {
+          holds = false;
+        } else if (!(d < -margin)) {
+          exact_sum(sh, row, x, true, dlo, dhi);
+          uint64_t ldig[NDIG + 1];
+          scaled_to_digits((unsigned long long)mult, x, ldig);
+          holds = digits_ge(sh.total, ldig);
+        }
+      }
     }
     // ---- advance the search
     const unsigned xb = __builtin_bit_cast(unsigned, x);
@@ -524,19 +645,31 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
       continue;
     }
     xstar = __builtin_bit_cast(float, blo);
-    x = xstar;
     stage = 3;
   }
 
+  // T_r = sum_{S <= x*} correctly rounded, r = #{S > x*}
   long long nsat;
+  double Tr;
   {
-    long long c = 0;
-    row.each([&](int, float v) { c += v > xstar ? 1 : 0; });
-    nsat = block_sum_l(sh, c);
+    double thi, tlo;
+    dd_sum(sh, row, xstar, false, thi, tlo, nsat, ph);
+    // thi = RN(thi + tlo); the exact sum lies within E of thi + tlo.  It
+    // rounds to thi when that interval stays strictly inside thi's rounding
+    // interval (half an ulp above, half the ulp below under it).
+    const double E = dd_rel * thi;
+    const unsigned long long tb = __builtin_bit_cast(unsigned long long, thi);
+    const double up = __builtin_bit_cast(double, tb + 1ull) - thi;
+    const double down = thi > 0.0 ? thi - __builtin_bit_cast(double, tb - 1ull) : up;
+    if (tlo + E < 0.5 * up && tlo - E > -0.5 * down) {
+      Tr = thi;
+    } else {
+      exact_sum(sh, row, xstar, false, dlo, dhi);
+      if (t == 0) sh.bcast_d = digits_to_double(sh.total);
+      __syncthreads();
+      Tr = sh.bcast_d;
+    }
   }
-  if (t == 0) sh.bcast_d = digits_to_double(sh.total);
-  __syncthreads();
-  const double Tr = sh.bcast_d;
   const double lam = (double)(s - nsat) / Tr;
 
   const uint64_t U = a.offsets ? a.offsets[r] : offset_of_row(a.seed, r);

@@ -115,6 +115,29 @@ def test_plan_exact_ties_and_special_rows(env):
         assert np.all(gc == -1) and np.all(gi == -1)
 
 
+def test_plan_sum_on_rounding_midpoints(env):
+    """Rows whose T_r lies exactly on, or just off, a midpoint between two
+    fp64 values: lambda = 1 / RN(T_r) must still match the oracle's
+    correctly rounded sum bit for bit (ties to even)."""
+    bsa, g, torch = env
+    g.say("case plan T_r on fp64 midpoints")
+    M = 8
+    rows = []
+    for tail in ([2.0 ** -53], [3 * 2.0 ** -53], [2.0 ** -53, 2.0 ** -80], [2.0 ** -53, 2.0 ** -100],
+                 [2.0 ** -24, 2.0 ** -77], [5 * 2.0 ** -53]):
+        r = np.zeros(M)
+        r[0] = 1.0
+        r[1:1 + len(tail)] = tail
+        rows.append(r)
+    S = np.stack(rows).astype(np.float32)
+    assert np.array_equal(S.astype(np.float64), np.stack(rows))   # every value is an fp32
+    S = S.reshape(1, 1, len(rows), M)
+    got = _gpu_plan(env, S, 1, opl.SIP, seed=3)
+    want = opl.plan(S, 1, opl.SIP, seed=3)
+    _compare(S, got, want, "midpoint rows")
+    assert got[3][0, 0, 0] == 1.0 and got[3][0, 0, 1] == 1.0 / (1.0 + 2.0 ** -51)
+
+
 def test_plan_on_selector_scores_full_rows(env):
     """Rows of real selector output (oracle scores of one Wan2.1-14B 720p
     head, rounded to fp32): 48 rows of M = 18,900 at budget 2048."""
