@@ -220,7 +220,7 @@ def main():
         "plan_ms": round(float(np.mean(pln)), 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": "bsa::attn_fwd_kernel<128>",
+            "kernel": "bsa::attn_fwd_kernel<128, true>",
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,

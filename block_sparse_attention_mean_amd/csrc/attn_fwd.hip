@@ -27,7 +27,9 @@
 //   * base-2 softmax (scale and shift pre-multiplied by log2 e) against a
 //     lazy reference maximum folded into the logit fma: O and the row sum
 //     are rescaled only when a tile exceeds the reference by more than 8
-//     (a wave-uniform test).
+//     (a wave-uniform test).  With KV blocks of 4 or more tokens (and Nk a
+//     multiple of 4) every aligned group of 4 keys shares one shift, so a
+//     lane's 16 logits need 4 shifts (one 16-byte LDS read).
 #include <type_traits>
 
 #include "common.h"
@@ -84,7 +86,15 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-template <int D>
+// Position of 4-key group q (0..7) of a tile in the shift ring when the
+// shift is uniform per group: [0 1 4 5 | 2 3 6 7], so that lane half h
+// finds its four groups (keys 8h + 0..7 and 16 + 8h + 0..7) in one 16-byte
+// read at 4 h.
+__device__ __forceinline__ int quad_pos(int q) {
+  return (q & 1) | (((q >> 2) & 1) << 1) | (((q >> 1) & 1) << 2);
+}
+
+template <int D, bool QUAD>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 4;              // waves: one 32-query quarter each
   constexpr int KT = 32;             // keys per tile
@@ -199,7 +209,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       const int dst = (wave * RPW + j * RPI) * ROWB;  // wave-uniform
       __builtin_amdgcn_global_load_lds((const void *)(kbase + src + g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(vbase + src + g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
-      if (lane % NCH == 0) bring[S * KT + g_row[j]] = ok ? bias_s[e] : -__builtin_inff();
+      if (QUAD) {
+        // rows 4 q .. 4 q + 3 share entry e (blocks of >= 4 keys, tiles
+        // start on block boundaries); row 4 q writes the group's shift
+        if (lane % NCH == 0 && (g_row[j] & 3) == 0)
+          bring[S * KT + quad_pos(g_row[j] >> 2)] = ok ? bias_s[e] : -__builtin_inff();
+      } else if (lane % NCH == 0) {
+        bring[S * KT + g_row[j]] = ok ? bias_s[e] : -__builtin_inff();
+      }
     }
   };
 
@@ -231,14 +248,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // lane halves (different keys of the same query) then agree on the new
     // reference through one exchange.
     const float *bt = bring + S * KT;
+    if (QUAD) {
+      const f32x4 bq = *(const f32x4 *)&bt[4 * hh];  // groups (m, half): (0,0) (0,1) (1,0) (1,1)
+      f32x4 bm;
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const f32x4 b0 = *(const f32x4 *)&bt[m2 * 16 + hh * 8];
-      const f32x4 b1 = *(const f32x4 *)&bt[m2 * 16 + hh * 8 + 4];
+      for (int i = 0; i < 4; ++i) bm[i] = bq[i] - m_run;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sacc[m2 * 8 + e] = __builtin_fmaf(sacc[m2 * 8 + e], a.scale_log2, b0[e] - m_run);
-        sacc[m2 * 8 + 4 + e] = __builtin_fmaf(sacc[m2 * 8 + 4 + e], a.scale_log2, b1[e] - m_run);
+      for (int r = 0; r < 16; ++r) sacc[r] = __builtin_fmaf(sacc[r], a.scale_log2, bm[r >> 2]);
+    } else {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const f32x4 b0 = *(const f32x4 *)&bt[m2 * 16 + hh * 8];
+        const f32x4 b1 = *(const f32x4 *)&bt[m2 * 16 + hh * 8 + 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[m2 * 8 + e] = __builtin_fmaf(sacc[m2 * 8 + e], a.scale_log2, b0[e] - m_run);
+          sacc[m2 * 8 + 4 + e] = __builtin_fmaf(sacc[m2 * 8 + 4 + e], a.scale_log2, b1[e] - m_run);
+        }
       }
     }
     float mx = sacc[0];
@@ -261,21 +287,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     }
     bf16x8 pf[2];
     {
-      float rs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[r]);
-        sacc[r] = pv;
-        rs += pv;
-      }
-      l_run += rs;
+      for (int r = 0; r < 16; ++r) sacc[r] = __builtin_amdgcn_exp2f(sacc[r]);
+      float rs[2] = {0.f, 0.f};  // two shorter add chains
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(sacc[8 * m + 2 * e], sacc[8 * m + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          w[e] = pack_bf16x2(sacc[8 * m + 2 * e], sacc[8 * m + 2 * e + 1]);
+          rs[m] += sacc[8 * m + 2 * e] + sacc[8 * m + 2 * e + 1];
+        }
         pf[m] = as_bf16x8(w);
       }
+      l_run += rs[0] + rs[1];
     }
     // V^T fragments through the transposing LDS read
 #pragma unroll
@@ -384,10 +409,16 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   const long long total = (long long)B * H * a.nqb;
   a.total_wg = (int)total;
   dim3 grid((unsigned)total), block(256);
-  if (d == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, stream, a);
+  // group shifts need every aligned group of 4 keys inside one block and
+  // either wholly below Nk or wholly masked
+  const bool quad = a.kv_shift >= 2 && (Nk & 3) == 0;
+  if (d == 128) {
+    if (quad) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, a);
+  } else {
+    if (quad) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, stream, a);
+  }
   return status_of(hipGetLastError());
 }
 
