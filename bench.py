@@ -12,7 +12,13 @@ attention kernel alone, the selector and the planner are reported beside it,
 with the roofline of the attention kernel (timed with HIP events on the
 stream it runs on) and the CPU oracle on a bounded sample.
 
+With ``--workload basa_1664x960`` the step is instead the BASA-structured
+path at the 1664x960 / 81-frame latent (21 x 60 x 104, 12 heads, 10 x 10
+windows, 4 x 4 pooled memory, top-2 routing): bsa_basa_plan ->
+bsa_attn_fwd -> bsa_window_unpermute, reported the same way.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload wan14b_720p|basa_1664x960]
 """
 from __future__ import annotations
 
@@ -110,6 +116,178 @@ def cpu_baseline(c, seed, heads):
     }
 
 
+def basa_window_rows(T, Hg, Wg, wh, ww):
+    """(first padded row, token count) of every window, window-major order."""
+    nwy, nwx = -(-Hg // wh), -(-Wg // ww)
+    out, off = [], 0
+    for a in range(nwy):
+        for b in range(nwx):
+            n = T * (min(Hg, (a + 1) * wh) - a * wh) * (min(Wg, (b + 1) * ww) - b * ww)
+            out.append((off, n))
+            off += -(-n // 128) * 128
+    return out, off
+
+
+def basa_cpu_baseline(c, seed, heads):
+    """The oracle's definition-based BASA attention of whole heads 0..heads-1
+    (window routing and every window's output rows), in the same TFLOP/s
+    unit."""
+    import numpy as np
+    from oracle import basa as obasa
+    from synth import bf16_bits_to_f32, head_qkv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
+    npool = c["T"] * -(-c["Hg"] // c["ph"]) * -(-c["Wg"] // c["pw"])
+    sec, flops = 0.0, 0.0
+    for h in range(heads):
+        qb, kb, vb = head_qkv(c["T"], c["Hg"], c["Wg"], c["d"], seed, h)
+        t0 = time.perf_counter()
+        routes = obasa.route(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), members, c["topk"])
+        obasa.basa_attn(qb, kb, vb, c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"],
+                        c["ph"], c["pw"], c["topk"], routes=routes)
+        sec += time.perf_counter() - t0
+        flops += sum(4.0 * c["d"] * len(members[w]) *
+                     (len(members[w]) + sum(len(members[j]) for j in routes[w]) + npool)
+                     for w in range(len(members)))
+    return {
+        "value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"heads 0..{heads - 1} of {c['name']}, all {len(members)} windows: routing and "
+                   f"attention, fp64 numpy (routing in its stated fp32 order)"),
+        "seconds": round(sec, 3), "host_cpus": os.cpu_count(),
+    }
+
+
+def run_basa(args):
+    import numpy as np
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    from synth import CONFIGS, make_qkv
+
+    c = dict(CONFIGS[args.workload])
+    c["name"] = args.workload
+    T, Hg, Wg, H, d, kvb = c["T"], c["Hg"], c["Wg"], c["H"], c["d"], c["kv_block"]
+    wh, ww, dy, dx, ph, pw, topk = (c[x] for x in ("wh", "ww", "dy", "dx", "ph", "pw", "topk"))
+    N = T * Hg * Wg
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {args.workload}: H={H} N={N} d={d}")
+    qb, kb, vb = make_qkv(T, Hg, Wg, H, d, seed=args.seed, workers=min(16, os.cpu_count() or 1))
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    del qb, kb, vb
+    lay = bsa.bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kvb, 1, H)
+    nq, nk, mb = lay["Nq_pad"], lay["Nk"], lay["max_blocks"]
+    nqb = nq // 128
+    qp = torch.empty((1, H, nq, d), dtype=torch.bfloat16, device=dev)
+    kp = torch.empty((1, H, nk, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    idx = torch.empty((1, H, nqb, mb), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, H, nqb), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(lay["workspace"], 256), dtype=torch.uint8, device=dev)
+    outp = torch.empty_like(qp)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    L = bsa.lib
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        bsa._check(L.bsa_basa_plan(q.data_ptr(), k.data_ptr(), v.data_ptr(), 1, H, T, Hg, Wg, d,
+                                   wh, ww, dy, dx, ph, pw, topk, kvb, qp.data_ptr(), kp.data_ptr(),
+                                   vp.data_ptr(), idx.data_ptr(), cnt.data_ptr(), None,
+                                   ws.data_ptr(), ws.numel(), st), "bsa_basa_plan")
+        if marks is not None:
+            marks[1].record(stream)
+        bsa._check(L.bsa_attn_fwd(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), 1, H, nq, nk, d,
+                                  128, kvb, idx.data_ptr(), None, cnt.data_ptr(), mb, 0.0,
+                                  outp.data_ptr(), None, st), "bsa_attn_fwd")
+        if marks is not None:
+            marks[2].record(stream)
+        bsa._check(L.bsa_window_unpermute(outp.data_ptr(), out.data_ptr(), 1, H, T, Hg, Wg, d, wh,
+                                          ww, dy, dx, st), "bsa_window_unpermute")
+        if marks is not None:
+            marks[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    g0, g1 = ev(), ev()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = g0.elapsed_time(g1) / args.steps
+    prep = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    att = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    unp = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    # algorithmic work: real (unpadded) queries x valid keys of their lists
+    wins, _ = basa_window_rows(T, Hg, Wg, wh, ww)
+    qvalid = np.zeros(nqb, np.int64)
+    for off, n in wins:
+        for i in range(off // 128, (off + n + 127) // 128):
+            qvalid[i] = min(128, off + n - 128 * i)
+    idx_h = idx.cpu().numpy().astype(np.int64)
+    cnt_h = cnt.cpu().numpy().astype(np.int64)
+    e = np.arange(mb)[None, None, None, :]
+    keys = np.where(e < cnt_h[..., None], np.minimum(kvb, nk - idx_h * kvb), 0).sum(axis=-1)
+    flops = 4.0 * d * float((keys * qvalid[None, None, :]).sum())
+    if not torch.isfinite(out.float()).all():
+        raise SystemExit("non-finite attention output")
+    attn_tf = flops / att / 1e9
+    npool = T * -(-Hg // ph) * -(-Wg // pw)
+    dense_keys = N
+    rec = {
+        "metric": "BASA-structured block-sparse attention effective TFLOP/s, 1664x960x81 latent",
+        "value": round(flops / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
+                        f"windows {wh}x{ww} rolled by ({dy},{dx}), pooled {ph}x{pw} ({npool} tokens), "
+                        f"top-{topk} routing, KV block {kvb}",
+            "B": 1, "H": H, "N": N, "d": d, "kv_block": kvb, "Nq_pad": nq, "Nk": nk,
+            "max_blocks": mb, "sparsity": round(1 - float(keys.mean()) / dense_keys, 5),
+            "seed": args.seed,
+            "step": "bsa_basa_plan + bsa_attn_fwd + bsa_window_unpermute",
+        },
+        "attn_ms_per_call": round(att, 4),
+        "attn_tflops": round(attn_tf, 2),
+        "basa_plan_ms": round(prep, 4),
+        "unpermute_ms": round(unp, 4),
+        "attn_flop_per_call": flops,
+        "roofline": {
+            "kernel": "bsa::attn_fwd_kernel<128, false>",
+            "bound": "mfma",
+            "achieved": round(attn_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        rec["cpu_baseline"] = basa_cpu_baseline(c, args.seed, 2)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -117,6 +295,8 @@ def main():
               "measured on a single MI355X; heads shard across GPUs with no communication.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("basa"):
+        return run_basa(args)
     import numpy as np
     import torch
     import block_sparse_attention_mean_amd as bsa

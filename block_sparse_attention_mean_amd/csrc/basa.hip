@@ -135,24 +135,49 @@ struct BasaArgs {
 };
 
 // ---------------------------------------------------------------- descriptors
+// One thread per dim; the window's tokens in window-local order (frame,
+// rolled row, rolled column), their raster index stepped incrementally.
+// The adds stay in that order; loads run UN tokens ahead of them.
 __global__ __launch_bounds__(128) void desc_kernel(BasaArgs a) {
+  constexpr int UN = 16;
   const Geo &g = a.g;
   const int wid = blockIdx.x, which = blockIdx.y, bh = blockIdx.z;
   const int dim = threadIdx.x;
   if (dim >= a.d) return;
   const Win w = window_at(g, wid / g.nwx, wid % g.nwx);
   const uint16_t *x = (which ? a.k : a.q) + (size_t)bh * a.N * a.d + dim;
+  // cursor: frame t, local row yy, local column xx -> raster token
+  int t = 0, yy = 0, xx = 0;
+  int y = w.a * g.wh + g.dy;
+  if (y >= g.Hg) y -= g.Hg;
+  const int x0 = w.b * g.ww + g.dx;
+  auto next_token = [&]() -> int {
+    int xc = x0 + xx;
+    if (xc >= g.Wg) xc -= g.Wg;
+    const int tok = (t * g.Hg + y) * g.Wg + xc;
+    if (++xx == w.w) {
+      xx = 0;
+      if (++yy == w.h) {
+        yy = 0;
+        ++t;
+        y = w.a * g.wh + g.dy;
+      } else {
+        ++y;
+      }
+      if (y >= g.Hg) y -= g.Hg;
+    }
+    return tok;
+  };
   float acc = 0.f;
-  // the adds stay in order; the token loads run ahead of them
   int r = 0;
-  for (; r + 8 <= w.n; r += 8) {
-    float v8[8];
+  for (; r + UN <= w.n; r += UN) {
+    float vu[UN];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v8[u] = bf16_to_f32(x[(size_t)token_of(g, w, r + u) * a.d]);
+    for (int u = 0; u < UN; ++u) vu[u] = bf16_to_f32(x[(size_t)next_token() * a.d]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __fadd_rn(acc, v8[u]);
+    for (int u = 0; u < UN; ++u) acc = __fadd_rn(acc, vu[u]);
   }
-  for (; r < w.n; ++r) acc = __fadd_rn(acc, bf16_to_f32(x[(size_t)token_of(g, w, r) * a.d]));
+  for (; r < w.n; ++r) acc = __fadd_rn(acc, bf16_to_f32(x[(size_t)next_token() * a.d]));
   a.desc[(((size_t)bh * 2 + which) * g.nwin + wid) * a.d + dim] = __fdiv_rn(acc, (float)w.n);
 }
 
@@ -163,29 +188,46 @@ __device__ inline float desc_dot(const float *qd, const float *kd, int d) {
   return acc;
 }
 
+// One wave per (head, query window i): lane l scores candidate windows
+// l, l + 64, .. (each dot product in the stated order); the top-k are then
+// taken one rank at a time by a wave-wide (score desc, id asc) maximum.
+__device__ __forceinline__ bool ranks_before(float s1, int j1, float s2, int j2) {
+  return s1 > s2 || (s1 == s2 && j1 < j2);
+}
+
 __global__ __launch_bounds__(64) void route_kernel(BasaArgs a) {
   const Geo &g = a.g;
-  const int i = blockIdx.x * 64 + threadIdx.x, bh = blockIdx.y;
-  if (i >= g.nwin) return;
+  const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
   const float *qd = a.desc + (((size_t)bh * 2 + 0) * g.nwin + i) * a.d;
   const float *kd0 = a.desc + ((size_t)bh * 2 + 1) * g.nwin * a.d;
-  // rank p: the best window ranked after pick p-1 in (score desc, id asc)
+  // rank p: the best window ranked after pick p-1
   float ps = __builtin_inff();
   int pj = -1;
   for (int p = 0; p < a.topk; ++p) {
     float bs = -__builtin_inff();
-    int bj = -1;
-    for (int j = 0; j < g.nwin; ++j) {
+    int bj = 0x7fffffff;
+    for (int j = lane; j < g.nwin; j += 64) {
       if (j == i) continue;
       const float s = desc_dot(qd, kd0 + (size_t)j * a.d, a.d);
-      const bool after = s < ps || (s == ps && j > pj);
-      if (after && (bj < 0 || s > bs)) {  // ascending j keeps the lowest id on ties
+      const bool after = ranks_before(ps, pj, s, j);
+      if (after && (bj == 0x7fffffff || ranks_before(s, j, bs, bj))) {
         bs = s;
         bj = j;
       }
     }
-    a.rank[((size_t)bh * g.nwin + i) * a.topk + p] = bj;
-    if (a.routes) a.routes[((size_t)bh * g.nwin + i) * a.topk + p] = bj;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float s2 = __shfl_xor(bs, o, 64);
+      const int j2 = __shfl_xor(bj, o, 64);
+      if (j2 != 0x7fffffff && (bj == 0x7fffffff || ranks_before(s2, j2, bs, bj))) {
+        bs = s2;
+        bj = j2;
+      }
+    }
+    if (lane == 0) {
+      a.rank[((size_t)bh * g.nwin + i) * a.topk + p] = bj;
+      if (a.routes) a.routes[((size_t)bh * g.nwin + i) * a.topk + p] = bj;
+    }
     ps = bs;
     pj = bj;
   }
@@ -374,7 +416,7 @@ int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, 
   const unsigned bh = (unsigned)BH;
   if (topk > 0) {
     hipLaunchKernelGGL(desc_kernel, dim3(nwin, 2, bh), dim3(128), 0, stream, a);
-    hipLaunchKernelGGL(route_kernel, dim3((nwin + 63) / 64, bh), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(route_kernel, dim3(nwin, bh), dim3(64), 0, stream, a);
   }
   const long long pe = (long long)nqp * (d / 8);
   hipLaunchKernelGGL(permute_kernel, dim3((unsigned)((pe + 255) / 256), bh), dim3(256), 0, stream, a);
