@@ -51,7 +51,7 @@ namespace {
 
 constexpr int PT = 512;               // threads per row
 constexpr int NW = PT / 64;           // waves
-constexpr int NDIG = 10;              // 32-bit digits of the superaccumulator
+constexpr int NDIG = 10;              // exact sums use 32-bit digits 0..NDIG (units 2^-149)
 constexpr uint64_t UNIT = 1ull << 44;  // fixed-point 1.0 of pi
 
 struct PlanArgs {
