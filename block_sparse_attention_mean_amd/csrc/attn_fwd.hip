@@ -7,15 +7,16 @@
 // and no reordered copy of the sequence in memory.  The shift itself is the
 // 1/pi weighting of section "어떻게 쓰나".
 //
-// Design (one workgroup = one 128-query block of one (b, h), 4 waves; two
-// workgroups share a CU, so a stall at one workgroup's barrier is covered
-// by the other):
+// Design (one workgroup = one 128-query block of one (b, h), 4 waves; three
+// workgroups share a CU, so each SIMD interleaves three waves' matrix and
+// vector work and a stall at one workgroup's barrier is covered by the
+// others):
 //   * wave w owns queries 32 w .. +32 and computes every key of every tile;
 //   * the block list and shifts of the query block are staged in LDS, so
 //     gather addresses never wait on global memory;
 //   * listed blocks are gathered with direct global->LDS 16-byte loads into
-//     a ring of four 32-key K/V tiles (tile t+3 is requested while tile t is
-//     consumed); K and V stay row-major with 16-byte-chunk XOR swizzles
+//     a ring of three 32-key K/V tiles (tile t+2 is requested while tile t
+//     is consumed); K and V stay row-major with 16-byte-chunk XOR swizzles
 //     (bank-conflict free for their MFMA operand reads) realised by each
 //     lane's choice of source address;
 //   * S^T = K Q^T (bf16 MFMA 32x32x16; Q stays in registers as the B
@@ -95,10 +96,10 @@ __device__ __forceinline__ int quad_pos(int q) {
 }
 
 template <int D, bool QUAD>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 4;              // waves: one 32-query quarter each
   constexpr int KT = 32;             // keys per tile
-  constexpr int NBUF = 4;            // ring slots
+  constexpr int NBUF = 3;            // ring slots
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int ROWB = D * 2;        // row bytes
   constexpr int TILEB = KT * ROWB;   // bytes of one K (or V) tile
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int LPT = 2 * LPW;       // vector-memory ops per wave per tile
   constexpr int DS = D / 16;         // k-steps of QK^T
   constexpr int DT = D / 32;         // dim tiles of O^T
-  constexpr int CAP = 1920;          // list entries staged per phase
+  constexpr int CAP = 512;           // list entries staged per phase
   static_assert(LPW >= 1 && RPW % RPI == 0, "tile too small for the gather split");
 
   // Ring of K/V tiles.  Separate arrays let the compiler see that a gather
@@ -117,7 +118,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char k0[TILEB], v0[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k1[TILEB], v1[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k2[TILEB], v2[TILEB];
-  __shared__ __attribute__((aligned(16))) unsigned char k3[TILEB], v3[TILEB];
   __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
   __shared__ __attribute__((aligned(16))) float bias_s[CAP];
   __shared__ __attribute__((aligned(16))) float bring[NBUF * KT];
@@ -185,11 +185,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   auto kslot = [&](auto c) -> unsigned char * {
     constexpr int S = decltype(c)::value;
-    return S == 0 ? k0 : (S == 1 ? k1 : (S == 2 ? k2 : k3));
+    return S == 0 ? k0 : (S == 1 ? k1 : k2);
   };
   auto vslot = [&](auto c) -> unsigned char * {
     constexpr int S = decltype(c)::value;
-    return S == 0 ? v0 : (S == 1 ? v1 : (S == 2 ? v2 : v3));
+    return S == 0 ? v0 : (S == 1 ? v1 : v2);
   };
 
   // Gather tile t into slot S: this wave loads rows [RPW w, RPW w + RPW).
@@ -224,6 +224,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int gi = lane & 15;  // index inside a 16-lane group
   const int gg = lane >> 4;  // group 0..3
 
+  // LDS byte offsets of this lane's MFMA operand reads inside a K tile and
+  // (for rows 0..3 of each 16-row group) inside a V tile.  The empty asm at
+  // each use hides the value from the optimiser, so it adds the slot base
+  // per read instead of keeping one full address per slot and read live,
+  // which at three workgroups per CU would spill.
+  int koff[DS], voff[DT];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) koff[ds] = krow * ROWB + (((2 * ds + hh) ^ swz_k<D>(krow)) << 4);
+  {
+    const int r0 = 8 * (gg >> 1) + (gi >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int n0 = dt * 32 + 16 * (gg & 1) + 4 * (gi & 3);
+      voff[dt] = r0 * ROWB + (((n0 >> 3) ^ swz_v<D>(r0)) << 4) + ((n0 >> 2) & 1) * 8;
+    }
+  }
   // S^T of the tile in slot S (32 keys x this wave's 32 queries).
   auto qk = [&](auto slot_c, f32x16 &sacc) {
     const unsigned char *kt = kslot(slot_c);
@@ -231,8 +247,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const int ch = (2 * ds + hh) ^ swz_k<D>(krow);
-      const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + krow * ROWB + ch * 16));
+      int o = koff[ds];
+      asm volatile("" : "+v"(o));
+      const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + o));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ds], sacc, 0, 0, 0);
     }
   };
@@ -305,16 +322,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // V^T fragments through the transposing LDS read
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int n0 = dt * 32 + 16 * (gg & 1) + 4 * (gi & 3);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         s16x4 part[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int row = 16 * m + 8 * (gg >> 1) + 4 * p + (gi >> 2);
-          const int ch = (n0 >> 3) ^ swz_v<D>(row);
-          const unsigned char *addr = vt + row * ROWB + ch * 16 + ((n0 >> 2) & 1) * 8;
-          part[p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)addr);
+          int o = voff[dt];
+          asm volatile("" : "+v"(o));
+          part[p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(vt + o + (16 * m + 4 * p) * ROWB));
         }
         const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
         const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
@@ -324,16 +340,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // One tile in slot S: wait for it, prefetch tile t+3 into the slot of
-  // tile t-1, compute.
+  // One tile in slot S: wait for it (tile t+1 may still be in flight; the
+  // barrier also means every wave is done with tile t-1), prefetch tile t+2
+  // into the slot of tile t-1, compute.
   f32x16 sA;
   auto step = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
-    constexpr int S3 = (S + 3) % NBUF;
-    if (t + 2 < ntiles) ring_barrier<2 * LPT>();
-    else if (t + 1 < ntiles) ring_barrier<LPT>();
+    constexpr int SN = (S + 2) % NBUF;
+    if (t + 1 < ntiles) ring_barrier<LPT>();
     else ring_barrier<0>();
-    if (t + 3 < ntiles) issue(std::integral_constant<int, S3>(), t + 3);
+    if (t + 2 < ntiles) issue(std::integral_constant<int, SN>(), t + 2);
     qk(slot_c, sA);
     softmax_pv(slot_c, sA);
   };
@@ -358,12 +374,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
     if (ntiles > 0) issue(std::integral_constant<int, 0>(), 0);
     if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
-    if (ntiles > 2) issue(std::integral_constant<int, 2>(), 2);
-    for (int t = 0; t < ntiles; t += 4) {
+    for (int t = 0; t < ntiles; t += 3) {
       step(std::integral_constant<int, 0>(), t);
       if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
       if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
-      if (t + 3 < ntiles) step(std::integral_constant<int, 3>(), t + 3);
     }
   }
 
