@@ -225,10 +225,11 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   const int gg = lane >> 4;  // group 0..3
 
   // LDS byte offsets of this lane's MFMA operand reads inside a K tile and
-  // (for rows 0..3 of each 16-row group) inside a V tile.  The empty asm at
-  // each use hides the value from the optimiser, so it adds the slot base
-  // per read instead of keeping one full address per slot and read live,
-  // which at three workgroups per CU would spill.
+  // (for rows 0..3 of each 16-row group) inside a V tile.  The empty asm
+  // before each use makes the value opaque to the optimiser, so the slot
+  // base goes into the read's immediate offset instead of one full address
+  // per slot and read being kept live, which at three workgroups per CU
+  // would spill; updating in place costs no copy.
   int koff[DS], voff[DT];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) koff[ds] = krow * ROWB + (((2 * ds + hh) ^ swz_k<D>(krow)) << 4);
@@ -247,9 +248,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      int o = koff[ds];
-      asm volatile("" : "+v"(o));
-      const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + o));
+      asm volatile("" : "+v"(koff[ds]));
+      const bf16x8 af = as_bf16x8(*(const u32x4 *)(kt + koff[ds]));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ds], sacc, 0, 0, 0);
     }
   };
@@ -306,14 +306,15 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = __builtin_amdgcn_exp2f(sacc[r]);
-      float rs[2] = {0.f, 0.f};  // two shorter add chains
+      float rs[2];  // two shorter add chains
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           w[e] = pack_bf16x2(sacc[8 * m + 2 * e], sacc[8 * m + 2 * e + 1]);
-          rs[m] += sacc[8 * m + 2 * e] + sacc[8 * m + 2 * e + 1];
+          const float pr = sacc[8 * m + 2 * e] + sacc[8 * m + 2 * e + 1];
+          rs[m] = e == 0 ? pr : rs[m] + pr;
         }
         pf[m] = as_bf16x8(w);
       }
@@ -322,15 +323,14 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     // V^T fragments through the transposing LDS read
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      asm volatile("" : "+v"(voff[dt]));
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         s16x4 part[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          int o = voff[dt];
-          asm volatile("" : "+v"(o));
           part[p] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(vt + o + (16 * m + 4 * p) * ROWB));
+              (lds_s16x4 *)(vt + voff[dt] + (16 * m + 4 * p) * ROWB));
         }
         const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
         const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
