@@ -28,9 +28,14 @@
 //   * base-2 softmax (scale and shift pre-multiplied by log2 e) against a
 //     lazy reference maximum folded into the logit fma: O and the row sum
 //     are rescaled only when a tile exceeds the reference by more than 8
-//     (a wave-uniform test).  With KV blocks of 4 or more tokens (and Nk a
-//     multiple of 4) every aligned group of 4 keys shares one shift, so a
-//     lane's 16 logits need 4 shifts (one 16-byte LDS read).
+//     (a wave-uniform test);
+//   * group-shift path, taken when each wave load (4 rows at d = 128, 8 at
+//     d = 64) lies inside one KV block and Nk is a whole number of loads:
+//     every aligned group of 4 keys shares one shift, staged once per
+//     phase in the order the softmax reads it, so a lane's 16 logits need 4
+//     shifts (one 16-byte LDS read); the block index of a load is
+//     wave-uniform, so it comes from a scalar load and the row address
+//     from scalar arithmetic, leaving one vector add per gather.
 #include <type_traits>
 
 #include "common.h"
@@ -109,7 +114,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   constexpr int LPT = 2 * LPW;       // vector-memory ops per wave per tile
   constexpr int DS = D / 16;         // k-steps of QK^T
   constexpr int DT = D / 32;         // dim tiles of O^T
-  constexpr int CAP = 512;           // list entries staged per phase
+  constexpr int CAP = 512;           // list entries staged per phase (per-key shifts)
+  constexpr int CAPG = 1024;         // 4-key groups staged per phase (group shifts)
   static_assert(LPW >= 1 && RPW % RPI == 0, "tile too small for the gather split");
 
   // Ring of K/V tiles.  Separate arrays let the compiler see that a gather
@@ -118,9 +124,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char k0[TILEB], v0[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k1[TILEB], v1[TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char k2[TILEB], v2[TILEB];
-  __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
-  __shared__ __attribute__((aligned(16))) float bias_s[CAP];
-  __shared__ __attribute__((aligned(16))) float bring[NBUF * KT];
+  // Per-key shifts: the phase's list in LDS and a shift ring beside the
+  // tiles.  Group shifts: one shift per 4-key group of the phase, stored
+  // per tile in the order the softmax reads them.
+  __shared__ __attribute__((aligned(16))) int32_t idx_s[QUAD ? 1 : CAP];
+  __shared__ __attribute__((aligned(16))) float bias_s[QUAD ? 1 : CAP];
+  __shared__ __attribute__((aligned(16))) float bring[QUAD ? 1 : NBUF * KT];
+  __shared__ __attribute__((aligned(16))) float gb_s[QUAD ? CAPG : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,18 +179,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   float l_run = 0.f;
   bool fresh = true;    // no key of this query seen yet (same in both halves)
 
-  int nkeys = 0, ntiles = 0;
+  int nkeys = 0, ntiles = 0, pbase = 0, pcnt = 0;
 
   // Per-lane constants of the gather: tile row of load j and the swizzled
-  // source chunk offsets of that row in K and V.
+  // source chunk offsets of that row in K and V (with group shifts, the
+  // offsets include the row's distance from the first row of the load).
   int g_row[LPW], g_koff[LPW], g_voff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int r = wave * RPW + j * RPI + lane / NCH;
     const int cl = lane % NCH;
+    const int rel = QUAD ? (lane / NCH) * ROWB : 0;
     g_row[j] = r;
-    g_koff[j] = (cl ^ swz_k<D>(r)) << 4;
-    g_voff[j] = (cl ^ swz_v<D>(r)) << 4;
+    g_koff[j] = rel + ((cl ^ swz_k<D>(r)) << 4);
+    g_voff[j] = rel + ((cl ^ swz_v<D>(r)) << 4);
   }
 
   auto kslot = [&](auto c) -> unsigned char * {
@@ -192,9 +204,45 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     return S == 0 ? v0 : (S == 1 ? v1 : v2);
   };
 
-  // Gather tile t into slot S: this wave loads rows [RPW w, RPW w + RPW).
-  // Masked keys (invalid or padded list entries, rows past Nk) load row 0
-  // and get a -inf shift.
+  // Group shifts: the RPI rows of each wave load lie in one KV block
+  // (blocks of at least RPI keys, tiles starting on block boundaries), so
+  // the block index is wave-uniform.  It is read with a scalar load before
+  // the ring barrier (its latency hides behind the wait) and the key row of
+  // the load becomes a scalar base; each lane adds its 32-bit offset.
+  // Masked loads (padded or invalid entries, rows past Nk) read row 0.
+  typedef const __attribute__((address_space(4))) int32_t cint_t;
+  auto rows_of = [&](int t, int (&row)[LPW]) {
+    int blk[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {  // all loads first (one wait); entry 0 stands in past the list
+      const int e = (t * KT + wave * RPW + j * RPI) >> a.kv_shift;
+      blk[j] = ((cint_t *)idx_row)[pbase + (e < pcnt ? e : 0)];
+    }
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {  // branch-free, so both loads issue before the wait
+      const int pos = t * KT + wave * RPW + j * RPI;
+      const unsigned b = (unsigned)blk[j];
+      const unsigned kk = (b << a.kv_shift) + (unsigned)(pos & (kvb - 1));
+      // (the load's rows are all below Nk or all past it)
+      const bool ok = ((pos >> a.kv_shift) < pcnt) & (b < (unsigned)a.M) & (kk < (unsigned)a.Nk);
+      row[j] = ok ? (int)kk : 0;
+    }
+  };
+  auto issue_rows = [&](auto slot_c, const int (&row)[LPW]) {
+    unsigned char *kt = kslot(slot_c);
+    unsigned char *vt = vslot(slot_c);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const size_t src = (size_t)row[j] * ROWB;
+      const int dst = (wave * RPW + j * RPI) * ROWB;
+      __builtin_amdgcn_global_load_lds((const void *)(kbase + src + (unsigned)g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vbase + src + (unsigned)g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
+    }
+  };
+
+  // Per-key shifts: gather tile t into slot S; this wave loads rows
+  // [RPW w, RPW w + RPW).  Masked keys (invalid or padded list entries, rows
+  // past Nk) load row 0 and get a -inf shift.
   auto issue = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
     unsigned char *kt = kslot(slot_c);
@@ -209,14 +257,16 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
       const int dst = (wave * RPW + j * RPI) * ROWB;  // wave-uniform
       __builtin_amdgcn_global_load_lds((const void *)(kbase + src + g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(vbase + src + g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
-      if (QUAD) {
-        // rows 4 q .. 4 q + 3 share entry e (blocks of >= 4 keys, tiles
-        // start on block boundaries); row 4 q writes the group's shift
-        if (lane % NCH == 0 && (g_row[j] & 3) == 0)
-          bring[S * KT + quad_pos(g_row[j] >> 2)] = ok ? bias_s[e] : -__builtin_inff();
-      } else if (lane % NCH == 0) {
-        bring[S * KT + g_row[j]] = ok ? bias_s[e] : -__builtin_inff();
-      }
+      if (lane % NCH == 0) bring[S * KT + g_row[j]] = ok ? bias_s[e] : -__builtin_inff();
+    }
+  };
+  auto issue_any = [&](auto slot_c, int t) {
+    if constexpr (QUAD) {
+      int row[LPW];
+      rows_of(t, row);
+      issue_rows(slot_c, row);
+    } else {
+      issue(slot_c, t);
     }
   };
 
@@ -254,8 +304,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
-  // Softmax of the tile in slot S (logits in sacc) and O^T += V^T P^T.
-  auto softmax_pv = [&](auto slot_c, f32x16 &sacc) {
+  // Softmax of tile t of the phase, in slot S (logits in sacc), and
+  // O^T += V^T P^T.
+  auto softmax_pv = [&](auto slot_c, f32x16 &sacc, int t) {
     constexpr int S = decltype(slot_c)::value;
     const unsigned char *vt = vslot(slot_c);
     // Base-2 logits relative to the running reference m_run of each query:
@@ -266,7 +317,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     // reference through one exchange.
     const float *bt = bring + S * KT;
     if (QUAD) {
-      const f32x4 bq = *(const f32x4 *)&bt[4 * hh];  // groups (m, half): (0,0) (0,1) (1,0) (1,1)
+      // groups (m, half): (0,0) (0,1) (1,0) (1,1)
+      const f32x4 bq = *(const f32x4 *)&gb_s[t * (KT / 4) + 4 * hh];
       f32x4 bm;
 #pragma unroll
       for (int i = 0; i < 4; ++i) bm[i] = bq[i] - m_run;
@@ -347,33 +399,60 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   auto step = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
     constexpr int SN = (S + 2) % NBUF;
+    const bool more = t + 2 < ntiles;
+    int row[LPW];
+    if (QUAD && more) rows_of(t + 2, row);
     if (t + 1 < ntiles) ring_barrier<LPT>();
     else ring_barrier<0>();
-    if (t + 2 < ntiles) issue(std::integral_constant<int, SN>(), t + 2);
+    if (more) {
+      if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row);
+      else issue(std::integral_constant<int, SN>(), t + 2);
+    }
     qk(slot_c, sA);
-    softmax_pv(slot_c, sA);
+    softmax_pv(slot_c, sA, t);
   };
 
-  for (int base = 0; base < cnt; base += CAP) {
-    const int pc = min(CAP, cnt - base);
+  // A phase covers CAP list entries (per-key shifts) or CAPG 4-key groups
+  // (group shifts).
+  const int per_phase = QUAD ? (CAPG * 4) >> a.kv_shift : CAP;
+  for (int base = 0; base < cnt; base += per_phase) {
+    const int pc = min(per_phase, cnt - base);
+    pbase = base;
+    pcnt = pc;
     nkeys = pc << a.kv_shift;
     ntiles = (nkeys + KT - 1) / KT;
-    // entries covering whole tiles (list tail padded with masked entries)
-    const int padded = min(CAP, ((ntiles * KT) >> a.kv_shift) + 1);
     __syncthreads();
-    for (int e = tid; e < padded; e += NW * 64) {
-      int blk = e < pc ? idx_row[base + e] : -1;
-      float bv = (e < pc && bias_row) ? bias_row[base + e] * kLog2e : 0.f;
-      if (blk < 0 || blk >= a.M) {
-        blk = 0;
-        bv = -__builtin_inff();
+    if constexpr (QUAD) {
+      // shift of every 4-key group of the phase's tiles, -inf for groups of
+      // padded or invalid entries and past Nk
+      const int ng = ntiles * (KT / 4);
+      for (int g = tid; g < ng; g += NW * 64) {
+        const int e = (4 * g) >> a.kv_shift;
+        float bv = -__builtin_inff();
+        if (e < pc) {
+          const int blk = idx_row[base + e];
+          if (blk >= 0 && blk < a.M && (blk << a.kv_shift) + ((4 * g) & (kvb - 1)) < a.Nk)
+            bv = bias_row ? bias_row[base + e] * kLog2e : 0.f;
+        }
+        gb_s[(g & ~7) | quad_pos(g & 7)] = bv;
       }
-      idx_s[e] = blk;
-      bias_s[e] = bv;
+    } else {
+      // entries covering whole tiles (list tail padded with masked entries)
+      const int padded = min(CAP, ((ntiles * KT) >> a.kv_shift) + 1);
+      for (int e = tid; e < padded; e += NW * 64) {
+        int blk = e < pc ? idx_row[base + e] : -1;
+        float bv = (e < pc && bias_row) ? bias_row[base + e] * kLog2e : 0.f;
+        if (blk < 0 || blk >= a.M) {
+          blk = 0;
+          bv = -__builtin_inff();
+        }
+        idx_s[e] = blk;
+        bias_s[e] = bv;
+      }
     }
     __syncthreads();
-    if (ntiles > 0) issue(std::integral_constant<int, 0>(), 0);
-    if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
+    if (ntiles > 0) issue_any(std::integral_constant<int, 0>(), 0);
+    if (ntiles > 1) issue_any(std::integral_constant<int, 1>(), 1);
     for (int t = 0; t < ntiles; t += 3) {
       step(std::integral_constant<int, 0>(), t);
       if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
@@ -423,9 +502,11 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   const long long total = (long long)B * H * a.nqb;
   a.total_wg = (int)total;
   dim3 grid((unsigned)total), block(256);
-  // group shifts need every aligned group of 4 keys inside one block and
-  // either wholly below Nk or wholly masked
-  const bool quad = a.kv_shift >= 2 && (Nk & 3) == 0;
+  // Group shifts and the scalar gather need every wave load (4 rows at
+  // d = 128, 8 at d = 64) inside one KV block and wholly below Nk or wholly
+  // past it: blocks of at least that many keys and Nk a multiple of it.
+  const int rows_per_load = d == 128 ? 4 : 8;
+  const bool quad = kv_block >= rows_per_load && Nk % rows_per_load == 0;
   if (d == 128) {
     if (quad) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, a);

@@ -121,6 +121,65 @@ def test_attn_edge_rows(env):
     g.assert_attn_close(O[0, 0, 256:], ref2, "row with partial block")
 
 
+def _valid_entries(idx_row, bias_row, c, M):
+    """The listed entries the kernel keeps: the first c, with 0 <= idx < M."""
+    bl, b = np.asarray(idx_row[:c]), np.asarray(bias_row[:c])
+    keep = (bl >= 0) & (bl < M)
+    return bl[keep], b[keep]
+
+
+@pytest.mark.parametrize("d,Nk,kvb", [(128, 132, 8), (128, 260, 4), (64, 136, 16)])
+def test_attn_group_shift_edges(env, d, Nk, kvb):
+    """The group-shift path (every wave load inside one KV block, Nk a whole
+    number of loads): a row with count 0, invalid indices (-1, M, 1000) among
+    valid ones, entries past the count, and the partial last block whose
+    tail groups lie past Nk."""
+    bsa, g, torch = env
+    g.say(f"case attn group-shift edges d={d} Nk={Nk} kv_block={kvb}")
+    qb, kb, vb = make_qkv(1, 1, 384, 1, d, seed=Nk + kvb)
+    kb2, vb2 = kb[:, :, :Nk], vb[:, :, :Nk]
+    M = -(-Nk // kvb)
+    idx = np.full((1, 1, 3, 12), M + 5, np.int32)
+    cnt = np.array([[[0, 12, 9]]], np.int32)
+    idx[0, 0, 1] = [0, 5 % M, -1, M - 1, M, 2, 3, 1000, 4 % M, 1, M - 2, 6 % M]
+    idx[0, 0, 2, :9] = [M - 1, M - 2, 0, 1, 2, 3, 4 % M, 5 % M, 6 % M]
+    bias = np.random.default_rng(1).random((1, 1, 3, 12)).astype(np.float32)
+    O, lse = _run(env, qb, kb2, vb2, kvb, idx, bias, cnt)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb2, vb2))
+    assert np.all(O[0, 0, :128] == 0) and np.all(np.isneginf(lse[0, 0, :128]))
+    for i in (1, 2):
+        bl, b = _valid_entries(idx[0, 0, i], bias[0, 0, i], cnt[0, 0, i], M)
+        ref, rlse = oat.attn_fwd(q[128 * i:128 * i + 128], k, v, 128, kvb, bl[None], b[None],
+                                 [len(bl)])
+        g.assert_attn_close(O[0, 0, 128 * i:128 * i + 128], ref, f"row {i}")
+        np.testing.assert_allclose(lse[0, 0, 128 * i:128 * i + 128], rlse, rtol=0, atol=2e-3)
+
+
+def test_attn_multi_phase_lists(env):
+    """Lists longer than one staging phase (4096 keys of group shifts; 512
+    entries of per-key shifts), with ragged counts: exactly one phase, one
+    entry more, a ragged second phase, and the full list; sampled query
+    blocks against the oracle, for both shift paths (Nk a multiple of 4 or
+    not)."""
+    bsa, g, torch = env
+    for N in (12000, 11999):
+        g.say(f"case attn multi-phase N={N} d=128 kv_block=4")
+        qb, kb, vb = make_qkv(1, 1, N, 1, 128, seed=N)
+        M = -(-N // 4)
+        nqb = -(-N // 128)
+        s = 1500
+        i_, b_, c_, _ = _random_plan(nqb, M, s, opl.SIP, seed=N)
+        c_ = c_.copy()
+        c_[0], c_[1], c_[2], c_[3] = 1024, 1025, 1200, 511
+        O, _ = _run(env, qb, kb, vb, 4, i_[None, None], b_[None, None], c_[None, None],
+                    want_lse=False)
+        q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+        blocks = [0, 1, 2, 3, 40, nqb - 1]
+        ref, _ = oat.attn_fwd(q, k, v, 128, 4, i_, b_, c_, blocks=blocks)
+        rows = np.concatenate([np.arange(i * 128, min(N, i * 128 + 128)) for i in blocks])
+        g.assert_attn_close(O[0, 0][rows], ref[rows], f"N={N} sampled blocks")
+
+
 def test_attn_deterministic(env):
     bsa, g, torch = env
     g.say("case attn determinism")
