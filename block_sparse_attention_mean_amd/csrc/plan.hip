@@ -243,7 +243,18 @@ struct RowView {
     lo = min(M, (int)threadIdx.x * chunk);
     hi = min(M, lo + chunk);
     if (IN_LDS) {
-      for (int j = threadIdx.x; j < M; j += PT) srow[j] = grow[j];
+      // batches of U independent loads per thread, so the copy waits for
+      // memory once per batch rather than once per value
+      constexpr int U = 16;
+      for (int j0 = threadIdx.x; j0 < M; j0 += U * PT) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j0 + u * PT < M) v[u] = grow[j0 + u * PT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j0 + u * PT < M) srow[j0 + u * PT] = v[u];
+      }
       __syncthreads();
       p = srow;
     } else {
@@ -707,10 +718,17 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
     // shifts -ln pi of the drawn blocks, one slot per thread (the indices
     // were written by this workgroup before the barrier)
     __syncthreads();
-    for (int e = t; e < drawn; e += PT) {
-      const int j = out_idx[e];
-      const double pi = fmin(1.0, lam * (double)row.p[j]);
-      out_bias[e] = (float)(-log(pi));
+    constexpr int U = 4;  // independent index loads before the first wait
+    for (int e0 = t; e0 < drawn; e0 += U * PT) {
+      int jj[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) jj[u] = e0 + u * PT < drawn ? out_idx[e0 + u * PT] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (e0 + u * PT < drawn) {
+          const double pi = fmin(1.0, lam * (double)row.p[jj[u]]);
+          out_bias[e0 + u * PT] = (float)(-log(pi));
+        }
     }
   }
   fill_rest(drawn);
