@@ -79,23 +79,47 @@ __global__ __launch_bounds__(256) void pool_split_kernel(SelArgs a) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int kvb = 1 << a.kv_shift;
   float acc[8][PER];
-  float amax = 0.f;
+  int rows[8];
+  const uint16_t *kp[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = tile * 32 + w * 8 + i;
+    const int r0 = j * kvb;
+    rows[i] = j < a.M ? min(kvb, a.N - r0) : 0;
+    kp[i] = a.k + ((size_t)bh * a.N + (j < a.M ? r0 : 0)) * D + lane * PER;
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[i][p] = 0.f;
-    if (j < a.M) {
-      const int r0 = j * kvb;
-      const int rows = min(kvb, a.N - r0);
-      const uint16_t *kp = a.k + ((size_t)bh * a.N + r0) * D + lane * PER;
-      for (int t = 0; t < rows; ++t) {
+  }
+  // rows t0 .. t0 + 3 of all 8 blocks are loaded before any is added, so
+  // a wave waits for memory once per batch; the sums keep ascending row
+  // order.  Loads past a block's rows re-read its row 0 (always present)
+  // and are not added.
+  for (int t0 = 0; t0 < kvb; t0 += 4) {
+    uint16_t v[8][4][PER];
 #pragma unroll
-        for (int p = 0; p < PER; ++p) acc[i][p] = __fadd_rn(acc[i][p], bf16_to_f32(kp[(size_t)t * D + p]));
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tt = t0 + u < rows[i] ? t0 + u : 0;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) v[i][u][p] = kp[i][(size_t)tt * D + p];
       }
 #pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (t0 + u < rows[i]) {
+#pragma unroll
+          for (int p = 0; p < PER; ++p) acc[i][p] = __fadd_rn(acc[i][p], bf16_to_f32(v[i][u][p]));
+        }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (rows[i] > 0) {
+#pragma unroll
       for (int p = 0; p < PER; ++p) {
-        acc[i][p] = rows == kvb ? acc[i][p] * (1.0f / (float)kvb) : __fdiv_rn(acc[i][p], (float)rows);
+        acc[i][p] = rows[i] == kvb ? acc[i][p] * (1.0f / (float)kvb) : __fdiv_rn(acc[i][p], (float)rows[i]);
         amax = fmaxf(amax, fabsf(acc[i][p]));
       }
     }
@@ -138,10 +162,21 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
   const int n = min(128, a.N - qb * 128);
   const uint16_t *qp = a.q + ((size_t)bh * a.N + (size_t)qb * 128) * D;
 
-  // 16-byte loads of the block into padded rows
-  for (int e = t; e < n * (D / 8); e += 256) {
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    st16(&qb16[r * QS + c8 * 8], ld16(qp + (size_t)r * D + c8 * 8));
+  // 16-byte loads of the block into padded rows, all issued before the
+  // first LDS store
+  {
+    constexpr int PER = 128 * (D / 8) / 256;  // chunks per thread
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {  // rows past n re-read row n - 1 and are not stored
+      const int e = t + i * 256, r = min(e / (D / 8), n - 1), c8 = e % (D / 8);
+      v[i] = ld16(qp + (size_t)r * D + c8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = t + i * 256, r = e / (D / 8), c8 = e % (D / 8);
+      if (r < n) st16(&qb16[r * QS + c8 * 8], v[i]);
+    }
   }
   for (int e = t; e < 16 * D; e += 256) mu[e] = 0.f;
   if (t < 16) active[t] = (t < C) && (((t + 1) * n) / C > (t * n) / C);
