@@ -14,8 +14,10 @@
 //     (s - r) S_(r+1) <= T_r.  Over the row values v this reads
 //     cond(v): (s - #{S >= v}) v <= sum_{S < v} S, which is monotone in v;
 //     the largest x with cond(x) is bracketed by secant steps down from
-//     T / s and a bisection over fp32 bit patterns that stops once no row
-//     value lies inside the bracket; then r = #{S > x}, T_r = sum_{S <= x} S;
+//     T / s, then either (at most 64 row values inside the bracket) those
+//     values are collected in one pass and cond is taken at each, or a
+//     bisection over fp32 bit patterns runs until no row value lies inside
+//     the bracket; then r = #{S > x}, T_r = sum_{S <= x} S;
 //   * each search step decides cond from an fp64 sum whose rounding error
 //     is bounded; inside that bound the sum is retaken as a double-double
 //     (error below 2^-90 of the sum), and only when even that cannot
@@ -53,6 +55,7 @@ constexpr int PT = 512;               // threads per row
 constexpr int NW = PT / 64;           // waves
 constexpr int NDIG = 10;              // exact sums use 32-bit digits 0..NDIG (units 2^-149)
 constexpr uint64_t UNIT = 1ull << 44;  // fixed-point 1.0 of pi
+constexpr int MCAP = 64;              // bracket values resolved without bisection
 
 struct PlanArgs {
   const float *scores;
@@ -77,6 +80,9 @@ struct Shared {
   long long cl[2][NW];          // alternating buffers of the one-barrier reductions
   double chi[2][NW], clo[2][NW];
   double bcast_d;
+  float col[MCAP];  // row values inside the final search bracket
+  int cstat[MCAP];  // the condition at each: 1 holds, 0 fails, 2 undecided
+  int ncol;
 };
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -302,6 +308,33 @@ __device__ void dd_sum(Shared &sh, const Row &row, float x, bool strict, double 
   hi = h;
   lo = l;
   ngt = c;
+}
+
+// Double-double sum of {S_j <= lo_x} (as dd_sum, same error bound) that also
+// collects the row values in (lo_x, hi_x) into sh.col; the caller knows
+// there are at most MCAP of them and has cleared sh.ncol.
+template <typename Row>
+__device__ void dd_sum_collect(Shared &sh, const Row &row, float lo_x, float hi_x, double &hi,
+                               double &lo, int &ph) {
+  double h = 0.0, l = 0.0;
+  long long c = 0;
+  row.each([&](int, float v) {
+    const bool in = v <= lo_x;
+    double s2, e;
+    two_sum(h, in ? (double)v : 0.0, s2, e);
+    h = s2;
+    l += e;
+    if (!in && v < hi_x) {
+      const int slot = atomicAdd(&sh.ncol, 1);
+      if (slot < MCAP) sh.col[slot] = v;
+    }
+  });
+  const double n = h + l;
+  l = l - (n - h);
+  h = n;
+  block_reduce(sh, c, h, l, ph);  // its barrier also publishes sh.col
+  hi = h;
+  lo = l;
 }
 
 // Exact sum of {S_j < x} (strict) or {S_j <= x} (!strict) into sh.total as
@@ -565,6 +598,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
       stage = 1;
     }
   }
+  bool collect = false;
   while (stage != 3) {
     // ---- one pass at x
     bool holds = true;
@@ -650,7 +684,13 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
         nge_hi = nge;
       }
     }
-    // stage 2: next bisection point, or done
+    // stage 2: few enough values left inside the bracket to resolve them
+    // directly (below), else the next bisection point, or done
+    if (stage == 2 && ngt_lo > nge_hi && ngt_lo - nge_hi <= MCAP) {
+      collect = true;
+      stage = 3;
+      continue;
+    }
     if (bhi - blo > 1 && ngt_lo > nge_hi) {
       x = __builtin_bit_cast(float, blo + (bhi - blo) / 2);
       continue;
@@ -662,13 +702,110 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   // T_r = sum_{S <= x*} correctly rounded, r = #{S > x*}
   long long nsat;
   double Tr;
-  {
-    double thi, tlo;
+  double thi, tlo;
+  double E;  // bound on |exact sum - (thi + tlo)|
+  if (collect) {
+    // The bracket (blo, bhi) holds m <= MCAP row values.  One pass sums
+    // {S <= blo} and collects them; cond is then taken at each collected
+    // value v (nge(v) = nge_hi + #{collected >= v}, slt(v) = sum_{S <= blo}
+    // + sum of collected values below v) with the certified double-double
+    // margin, and x* is the largest value where it holds (blo if none).
+    // cond is monotone, so this is the partition the bisection would find.
+    const float flo = __builtin_bit_cast(float, blo), fhi = __builtin_bit_cast(float, bhi);
+    const int m = (int)(ngt_lo - nge_hi);
+    if (t == 0) sh.ncol = 0;
+    __syncthreads();
+    double shi, slo;
+    dd_sum_collect(sh, row, flo, fhi, shi, slo, ph);
+    const double mrel = dd_rel + 0x1p-90;  // the sum plus up to MCAP exact-rounded terms
+    if (t < 64) {
+      const float v = t < m ? sh.col[t] : 0.f;
+      double bh = 0.0, bl = 0.0;  // collected values below v
+      long long ge = 0;           // collected values >= v
+      for (int j = 0; j < m; ++j) {
+        const float u = sh.col[j];
+        if (u < v) {
+          double s2, e;
+          two_sum(bh, (double)u, s2, e);
+          bh = s2;
+          bl += e;
+        } else {
+          ++ge;
+        }
+      }
+      if (t < m) {
+        int st = 1;
+        const long long mult = (long long)s - nge_hi - ge;
+        if (mult > 0) {
+          double rh = shi, rl = slo;
+          dd_add(rh, rl, bh, bl);
+          const double lhs = (double)mult * (double)v;  // exact
+          double p, q;
+          two_sum(lhs, -rh, p, q);
+          const double d = p + (q - rl);
+          const double margin = mrel * rh + 0x1p-100 * (lhs + rh);
+          st = d > margin ? 0 : (d < -margin ? 1 : 2);
+        }
+        sh.cstat[t] = st;
+      }
+    }
+    __syncthreads();
+    // certain bounds, then any undecided values between them in ascending
+    // order, each decided exactly (every thread takes the same steps)
+    float vt = flo, vf = fhi;
+    for (int j = 0; j < m; ++j) {
+      const float u = sh.col[j];
+      const int st = sh.cstat[j];
+      if (st == 1 && u > vt) vt = u;
+      if (st == 0 && u < vf) vf = u;
+    }
+    for (;;) {
+      float nxt = vf;
+      for (int j = 0; j < m; ++j) {
+        const float u = sh.col[j];
+        if (sh.cstat[j] == 2 && u > vt && u < nxt) nxt = u;
+      }
+      if (!(nxt < vf)) break;
+      long long ge = nge_hi;
+      for (int j = 0; j < m; ++j) ge += sh.col[j] >= nxt ? 1 : 0;
+      const long long mult = (long long)s - ge;
+      bool holds = true;
+      if (mult > 0) {
+        exact_sum(sh, row, nxt, true, dlo, dhi);
+        uint64_t ldig[NDIG + 1];
+        scaled_to_digits((unsigned long long)mult, nxt, ldig);
+        holds = digits_ge(sh.total, ldig);
+      }
+      if (!holds) break;
+      vt = nxt;
+    }
+    xstar = vt;
+    nsat = nge_hi;
+    thi = shi;
+    tlo = slo;
+    for (int j = 0; j < m; ++j) {
+      const float u = sh.col[j];
+      if (u > xstar) {
+        ++nsat;
+      } else {
+        double s2, e;
+        two_sum(thi, (double)u, s2, e);
+        thi = s2;
+        tlo += e;
+      }
+    }
+    const double n2 = thi + tlo;
+    tlo = tlo - (n2 - thi);
+    thi = n2;
+    E = mrel * thi;
+  } else {
     dd_sum(sh, row, xstar, false, thi, tlo, nsat, ph);
+    E = dd_rel * thi;
+  }
+  {
     // thi = RN(thi + tlo); the exact sum lies within E of thi + tlo.  It
     // rounds to thi when that interval stays strictly inside thi's rounding
     // interval (half an ulp above, half the ulp below under it).
-    const double E = dd_rel * thi;
     const unsigned long long tb = __builtin_bit_cast(unsigned long long, thi);
     const double up = __builtin_bit_cast(double, tb + 1ull) - thi;
     const double down = thi > 0.0 ? thi - __builtin_bit_cast(double, tb - 1ull) : up;

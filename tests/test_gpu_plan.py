@@ -115,6 +115,35 @@ def test_plan_exact_ties_and_special_rows(env):
         assert np.all(gc == -1) and np.all(gi == -1)
 
 
+def test_plan_threshold_inside_the_final_bracket(env):
+    """Rows whose threshold x* is a row value strictly below the maximum, so
+    the search ends with row values inside its bracket and resolves them
+    one by one: cond holding with equality at x* = c (undecided under the
+    double-double margin, decided exactly), the same with x* repeated, and
+    200 distinct values packed within 2e-4 of each other around x* (more
+    values in the bracket than are resolved directly, so bisection narrows
+    it first)."""
+    bsa, g, torch = env
+    g.say("case plan threshold inside the final bracket")
+    c, y, b = 2.0 ** -6, 3 * 2.0 ** -12, 10 * 2.0 ** -6   # 3c = 64 y: equality at x* = c
+    cases = [(np.array([b, c] + [y] * 64), 5),             # r = 1, T_r = 4c
+             (np.array([b, c, c] + [y] * 64 + [0.0]), 6)]  # r = 1, x* = c twice
+    clus = 2.0 ** -8 * (1 + np.arange(200) * 2.0 ** -20)
+    w = np.frombuffer(np.uint32(964319093).tobytes(), np.float32)[0]  # 109 of the 200 saturate
+    cases.append((np.concatenate([clus, np.full(1800, w)]), 310))
+    clus2 = 2.0 ** -8 * (1 + np.arange(200) * 2.0 ** -14)
+    cases.append((np.concatenate([clus2, np.full(1800, 2.0 ** -12)]), 312))
+    for row, s in cases:
+        S = row.astype(np.float32)
+        assert np.array_equal(S.astype(np.float64), row)   # every value is an fp32
+        S = S.reshape(1, 1, 1, -1)
+        got = _gpu_plan(env, S, s, opl.SIP, seed=4)
+        want = opl.plan(S, s, opl.SIP, seed=4)
+        _compare(S, got, want, f"bracket row M={S.shape[-1]} s={s}")
+    got = _gpu_plan(env, np.array([b, c] + [y] * 64, np.float32).reshape(1, 1, 1, -1), 5, opl.SIP)
+    assert got[3][0, 0, 0] == 64.0 and got[2][0, 0, 0] == 5   # lambda = (5 - 1) / (4c)
+
+
 def test_plan_sum_on_rounding_midpoints(env):
     """Rows whose T_r lies exactly on, or just off, a midpoint between two
     fp64 values: lambda = 1 / RN(T_r) must still match the oracle's
