@@ -30,6 +30,8 @@
 //             windows;
 //   lists     one workgroup per query block: own, routed (ascending), pooled;
 //   unpermute output rows back to raster token order.
+#include <type_traits>
+
 #include "common.h"
 
 namespace bsa {
@@ -137,9 +139,9 @@ struct BasaArgs {
 // ---------------------------------------------------------------- descriptors
 // One thread per dim; the window's tokens in window-local order (frame,
 // rolled row, rolled column), their raster index stepped incrementally.
-// The adds stay in that order; loads run UN tokens ahead of them.
+// The adds stay in that order; loads run up to UN tokens ahead of them.
 __global__ __launch_bounds__(128) void desc_kernel(BasaArgs a) {
-  constexpr int UN = 16;
+  constexpr int UN = 64;
   const Geo &g = a.g;
   const int wid = blockIdx.x, which = blockIdx.y, bh = blockIdx.z;
   const int dim = threadIdx.x;
@@ -170,13 +172,16 @@ __global__ __launch_bounds__(128) void desc_kernel(BasaArgs a) {
   };
   float acc = 0.f;
   int r = 0;
-  for (; r + UN <= w.n; r += UN) {
-    float vu[UN];
+  auto batch = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    float vu[n];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) vu[u] = bf16_to_f32(x[(size_t)next_token() * a.d]);
+    for (int u = 0; u < n; ++u) vu[u] = bf16_to_f32(x[(size_t)next_token() * a.d]);
 #pragma unroll
-    for (int u = 0; u < UN; ++u) acc = __fadd_rn(acc, vu[u]);
-  }
+    for (int u = 0; u < n; ++u) acc = __fadd_rn(acc, vu[u]);
+  };
+  for (; r + UN <= w.n; r += UN) batch(std::integral_constant<int, UN>());
+  for (; r + 8 <= w.n; r += 8) batch(std::integral_constant<int, 8>());
   for (; r < w.n; ++r) acc = __fadd_rn(acc, bf16_to_f32(x[(size_t)next_token() * a.d]));
   a.desc[(((size_t)bh * 2 + which) * g.nwin + wid) * a.d + dim] = __fdiv_rn(acc, (float)w.n);
 }
@@ -270,16 +275,31 @@ __global__ __launch_bounds__(256) void pool_kernel(BasaArgs a) {
   const int cells = g.pyc * g.pxc;
   const int t = (int)gi / cells, rem = (int)gi - t * cells;
   const int cy = rem / g.pxc, cx = rem - cy * g.pxc;
-  const int y1 = min(g.Hg, (cy + 1) * g.ph), x1 = min(g.Wg, (cx + 1) * g.pw);
+  const int y0 = cy * g.ph, x0 = cx * g.pw;
+  const int y1 = min(g.Hg, y0 + g.ph), x1 = min(g.Wg, x0 + g.pw);
+  const int wx = x1 - x0, cnt = (y1 - y0) * wx;
+  const size_t base = ((size_t)bh * a.N + (size_t)t * g.Hg * g.Wg) * a.d + dim;
   float sk = 0.f, sv = 0.f;
-  int cnt = 0;
-  for (int y = cy * g.ph; y < y1; ++y)
-    for (int x = cx * g.pw; x < x1; ++x) {
-      const size_t o = ((size_t)bh * a.N + ((size_t)t * g.Hg + y) * g.Wg + x) * a.d + dim;
-      sk = __fadd_rn(sk, bf16_to_f32(a.k[o]));
-      sv = __fadd_rn(sv, bf16_to_f32(a.v[o]));
-      ++cnt;
+  // the cells in row-major order, UP loads in flight before their adds
+  // (cells past the patch re-read its first cell and are not added)
+  constexpr int UP = 16;
+  for (int c0 = 0; c0 < cnt; c0 += UP) {
+    uint16_t kk[UP], vv[UP];
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const int c = c0 + u < cnt ? c0 + u : 0;
+      const int y = y0 + c / wx, x = x0 + c % wx;
+      const size_t o = base + ((size_t)y * g.Wg + x) * a.d;
+      kk[u] = a.k[o];
+      vv[u] = a.v[o];
     }
+#pragma unroll
+    for (int u = 0; u < UP; ++u)
+      if (c0 + u < cnt) {
+        sk = __fadd_rn(sk, bf16_to_f32(kk[u]));
+        sv = __fadd_rn(sv, bf16_to_f32(vv[u]));
+      }
+  }
   const size_t o = ((size_t)bh * a.Nk + g.Nq_pad + gi) * a.d + dim;
   a.kp[o] = (unsigned short)bf16_bits(__fdiv_rn(sk, (float)cnt));
   a.vp[o] = (unsigned short)bf16_bits(__fdiv_rn(sv, (float)cnt));
