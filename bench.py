@@ -57,14 +57,22 @@ def parse():
     return p.parse_args()
 
 
+def attn_build_sha():
+    """Hash of the attention kernel's source and its per-file build flags:
+    what the committed counter runs must have been taken on."""
+    from block_sparse_attention_mean_amd.build import FILE_FLAGS
+    h = hashlib.sha256(open(ATTN_SRC, "rb").read())
+    h.update(" ".join(FILE_FLAGS.get("attn_fwd.hip", [])).encode())
+    return h.hexdigest()
+
+
 def traffic_for_current_kernel():
     """HBM bytes per attention launch from committed counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel build; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_build_sha256") != attn_build_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
 
