@@ -705,18 +705,21 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   double thi, tlo;
   double E;  // bound on |exact sum - (thi + tlo)|
   if (collect) {
-    // The bracket (blo, bhi) holds m <= MCAP row values.  One pass sums
+    // The bracket (blo, bhi) holds m <= MCAP row values (at most
+    // ngt_lo - nge_hi).  One pass sums
     // {S <= blo} and collects them; cond is then taken at each collected
     // value v (nge(v) = nge_hi + #{collected >= v}, slt(v) = sum_{S <= blo}
     // + sum of collected values below v) with the certified double-double
     // margin, and x* is the largest value where it holds (blo if none).
     // cond is monotone, so this is the partition the bisection would find.
     const float flo = __builtin_bit_cast(float, blo), fhi = __builtin_bit_cast(float, bhi);
-    const int m = (int)(ngt_lo - nge_hi);
     if (t == 0) sh.ncol = 0;
     __syncthreads();
     double shi, slo;
     dd_sum_collect(sh, row, flo, fhi, shi, slo, ph);
+    // the values actually collected: ngt_lo - nge_hi can count more (its
+    // starting value counts the smallest positive values too)
+    const int m = min(sh.ncol, MCAP);
     const double mrel = dd_rel + 0x1p-90;  // the sum plus up to MCAP exact-rounded terms
     if (t < 64) {
       const float v = t < m ? sh.col[t] : 0.f;

@@ -133,6 +133,10 @@ def test_plan_threshold_inside_the_final_bracket(env):
     cases.append((np.concatenate([clus, np.full(1800, w)]), 310))
     clus2 = 2.0 ** -8 * (1 + np.arange(200) * 2.0 ** -14)
     cases.append((np.concatenate([clus2, np.full(1800, 2.0 ** -12)]), 312))
+    # max S just above T / s (within 2^-20): the test at the maximum fails and
+    # the bracket starts at the smallest positive value, which is repeated
+    cases.append((np.array([1.0, 1.0 - 2.0 ** -22] + [2.0 ** -40] * 3), 2))
+    cases.append((np.concatenate([[1.0], 1.0 - np.arange(1, 6) * 2.0 ** -22, np.full(20, 2.0 ** -40)]), 6))
     for row, s in cases:
         S = row.astype(np.float32)
         assert np.array_equal(S.astype(np.float64), row)   # every value is an fp32
