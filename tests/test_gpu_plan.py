@@ -70,6 +70,37 @@ def test_plan_matches_oracle_random_rows(env, M, s, mode):
     _compare(S, got, want, f"M={M} s={s}")
 
 
+@pytest.mark.parametrize("mode", [opl.SIP, opl.TOPK])
+def test_plan_structured_fuzz(env, mode):
+    """Many small rows built to sit on the search's edge cases: values from a
+    few powers of two (so sums and products are exact and equalities
+    happen), repeated values, zeros, one value nudged a few ulps off its
+    neighbour, and budgets from 1 up to the row length."""
+    bsa, g, torch = env
+    g.say(f"case plan structured fuzz mode={mode}")
+    for M in (5, 9, 17, 40, 96, 300):
+        H = max(1, M // 8)  # size of the head of large values (second family)
+        for s in sorted({1, 2, 3, H // 2 + 1, H, H + 1, H + 3, 2 * H, M // 4 + 1, M // 2, M - 1, M}):
+            rng = np.random.default_rng(M * 1009 + s * 7 + mode)
+            rows = []
+            for r in range(16):
+                if r % 2 == 0:  # spread powers of two
+                    v = 2.0 ** -rng.integers(1, 12, M).astype(np.float64)
+                else:           # a head of large values over a tail of small ones
+                    v = 2.0 ** -rng.integers(6, 15, M).astype(np.float64)
+                    v[rng.permutation(M)[:H]] = 2.0 ** -rng.integers(1, 4, H)
+                v[rng.random(M) < 0.1] = 0.0
+                k = rng.integers(0, M)  # one value a few ulps above another
+                if v[k] > 0:
+                    v[k] = np.float64(np.float32(v[rng.integers(0, M)]) *
+                                      np.float32(1 + rng.integers(1, 4) * 2.0 ** -23))
+                rows.append(v)
+            S = np.stack(rows).astype(np.float32).reshape(1, 2, 8, M)
+            got = _gpu_plan(env, S, s, mode, seed=M * 31 + s)
+            want = opl.plan(S, s, mode, seed=M * 31 + s)
+            _compare(S, got, want, f"fuzz M={M} s={s}")
+
+
 def test_plan_explicit_offsets(env):
     bsa, g, torch = env
     g.say("case plan explicit offsets")
