@@ -180,6 +180,41 @@ def test_attn_multi_phase_lists(env):
         g.assert_attn_close(O[0, 0][rows], ref[rows], f"N={N} sampled blocks")
 
 
+def test_attn_fuzz_geometries(env):
+    """Random small shapes through both shift paths (group shifts when the KV
+    block covers a wave load and Nk is a whole number of loads, per-key
+    shifts otherwise): lists with invalid entries, repeated blocks, counts
+    from 0 to the list length, shifts from 0 to 8."""
+    bsa, g, torch = env
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        d = int(rng.choice([64, 128]))
+        kvb = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        N = int(rng.integers(1, 400))
+        Nk = int(rng.integers(max(1, N // 2), N + 1))
+        M = -(-Nk // kvb)
+        nqb = -(-N // 128)
+        L = int(rng.integers(1, 2 * M + 3))
+        g.say(f"case attn fuzz {case}: N={N} Nk={Nk} d={d} kv_block={kvb} list={L}")
+        qb, kb, vb = make_qkv(1, 1, N, 1, d, seed=case)
+        kb, vb = kb[:, :, :Nk], vb[:, :, :Nk]
+        idx = rng.integers(-2, M + 3, (1, 1, nqb, L)).astype(np.int32)
+        bias = (rng.random((1, 1, nqb, L)) * 8).astype(np.float32)
+        bias[rng.random((1, 1, nqb, L)) < 0.3] = 0.0
+        cnt = rng.integers(0, L + 1, (1, 1, nqb)).astype(np.int32)
+        O, lse = _run(env, qb, kb, vb, kvb, idx, bias, cnt)
+        q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+        for i in range(nqb):
+            bl, b = _valid_entries(idx[0, 0, i], bias[0, 0, i], cnt[0, 0, i], M)
+            rows = slice(128 * i, min(N, 128 * i + 128))
+            if len(bl) == 0 or not np.any(bl * kvb < Nk):
+                assert np.all(O[0, 0, rows] == 0), f"case {case} block {i}: empty list not zero"
+                continue
+            ref, rlse = oat.attn_fwd(q[rows], k, v, 128, kvb, bl[None], b[None], [len(bl)])
+            g.assert_attn_close(O[0, 0, rows], ref, f"case {case} block {i}")
+            np.testing.assert_allclose(lse[0, 0, rows], rlse, rtol=0, atol=2e-3)
+
+
 def test_attn_deterministic(env):
     bsa, g, torch = env
     g.say("case attn determinism")
