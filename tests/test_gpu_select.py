@@ -52,6 +52,26 @@ def test_select_matches_oracle_small(env, T, Hg, Wg, d, kvb, C, iters):
         _check_head(g, qb[0, h], kb[0, h], Sg[0, h], mug[0, h], wg[0, h], kvb, C, iters, f"head {h}")
 
 
+def test_select_fuzz_geometries(env):
+    """Random sequence lengths (ragged query blocks and ragged 32-block key
+    tiles), KV block sizes, cluster counts, head dims and iteration counts,
+    two heads each, every output checked."""
+    bsa, g, torch = env
+    rng = np.random.default_rng(99)
+    for case in range(12):
+        d = int(rng.choice([64, 128]))
+        kvb = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        C = int(rng.choice([1, 2, 4, 8, 16]))
+        iters = int(rng.integers(0, 3))
+        N = int(rng.integers(1, 2500))
+        g.say(f"case select fuzz {case}: N={N} d={d} kv={kvb} C={C} it={iters}")
+        qb, kb, _ = make_qkv(1, 1, N, 2, d, seed=1000 + case)
+        Sg, mug, wg = _gpu_select(env, qb, kb, kvb, C, iters)
+        for h in range(2):
+            _check_head(g, qb[0, h], kb[0, h], Sg[0, h], mug[0, h], wg[0, h], kvb, C, iters,
+                        f"fuzz {case} head {h}")
+
+
 def test_select_tiny_config_mean_pooled(env):
     bsa, g, torch = env
     c = CONFIGS["tiny_2x32x32"]
