@@ -79,6 +79,32 @@ SMALL = [
 @pytest.mark.parametrize("geo", SMALL, ids=lambda x: f"{x['Hg']}x{x['Wg']}w{x['wh']}x{x['ww']}"
                          f"k{x['topk']}d{x['d']}kv{x['kvb']}")
 def test_basa_small_matches_oracle(env, geo):
+    _check_small(env, geo)
+
+
+def test_basa_fuzz_geometries(env):
+    """Random grids, window sizes (ragged last windows), rolls, pool cells
+    and top-k; KV block the largest power of two (up to 16) dividing every
+    window's token count and 128."""
+    bsa, g, torch = env
+    rng = np.random.default_rng(55)
+    for case in range(8):
+        T = int(rng.integers(1, 4))
+        Hg, Wg = int(rng.integers(3, 17)), int(rng.integers(3, 25))
+        wh, ww = int(rng.integers(1, Hg + 1)), int(rng.integers(1, Wg + 1))
+        wins, _ = _window_rows(T, Hg, Wg, wh, ww)
+        kvb = 16
+        while any(n % kvb for _, n in wins):
+            kvb //= 2
+        nwin = len(wins)
+        geo = dict(T=T, Hg=Hg, Wg=Wg, wh=wh, ww=ww, dy=int(rng.integers(-Hg, 2 * Hg)),
+                   dx=int(rng.integers(-Wg, 2 * Wg)), ph=int(rng.integers(1, Hg + 1)),
+                   pw=int(rng.integers(1, Wg + 1)), topk=min(64, int(rng.integers(0, nwin))), kvb=kvb,
+                   d=int(rng.choice([64, 128])), H=2)
+        _check_small(env, geo)
+
+
+def _check_small(env, geo):
     bsa, g, torch = env
     g.say(f"case basa small {geo}")
     T, Hg, Wg, wh, ww, dy, dx = (geo[x] for x in ("T", "Hg", "Wg", "wh", "ww", "dy", "dx"))
