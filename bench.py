@@ -281,7 +281,7 @@ def run_basa(args):
         "unpermute_ms": round(unp, 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": "bsa::attn_fwd_kernel<128, false>",
+            "kernel": "bsa::attn_fwd_kernel<128, true, true>",
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -408,7 +408,7 @@ def main():
         "plan_ms": round(float(np.mean(pln)), 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": "bsa::attn_fwd_kernel<128, true>",
+            "kernel": "bsa::attn_fwd_kernel<128, true, false>",
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,

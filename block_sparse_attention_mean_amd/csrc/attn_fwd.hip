@@ -30,12 +30,15 @@
 //     are rescaled only when a tile exceeds the reference by more than 8
 //     (a wave-uniform test);
 //   * group-shift path, taken when each wave load (4 rows at d = 128, 8 at
-//     d = 64) lies inside one KV block and Nk is a whole number of loads:
-//     every aligned group of 4 keys shares one shift, staged once per
-//     phase in the order the softmax reads it, so a lane's 16 logits need 4
-//     shifts (one 16-byte LDS read); the block index of a load is
-//     wave-uniform, so it comes from a scalar load and the row address
-//     from scalar arithmetic, leaving one vector add per gather.
+//     d = 64) lies inside one KV block: every aligned group of 4 keys
+//     shares one shift, staged once per phase in the order the softmax
+//     reads it, so a lane's 16 logits need 4 shifts (one 16-byte LDS read);
+//     the block index of a load is wave-uniform, so it comes from a scalar
+//     load and the row address from scalar arithmetic, leaving one vector
+//     add per gather.  When Nk is not a whole number of loads, a separate
+//     instance also handles the load and the 4-key group crossing Nk: the
+//     load's lanes past Nk re-read its last valid row, and the tile's keys
+//     past Nk are masked before the exponentials.
 #include <type_traits>
 
 #include "common.h"
@@ -100,7 +103,10 @@ __device__ __forceinline__ int quad_pos(int q) {
   return (q & 1) | (((q >> 2) & 1) << 1) | (((q >> 1) & 1) << 2);
 }
 
-template <int D, bool QUAD>
+// QUAD: group shifts and the scalar gather (KV blocks of at least one wave
+// load); PART: with them, loads and 4-key groups crossing Nk may occur (Nk
+// not a whole number of wave loads), so their rows past Nk are handled.
+template <int D, bool QUAD, bool PART>
 __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 4;              // waves: one 32-query quarter each
   constexpr int KT = 32;             // keys per tile
@@ -131,6 +137,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float bias_s[QUAD ? 1 : CAP];
   __shared__ __attribute__((aligned(16))) float bring[QUAD ? 1 : NBUF * KT];
   __shared__ __attribute__((aligned(16))) float gb_s[QUAD ? CAPG : 1];
+  // Group shifts with Nk inside a 4-key group (only the block holding key
+  // Nk - 1): per tile, the rows past Nk of such groups.
+  __shared__ uint32_t pmask_s[QUAD && PART ? CAPG / 8 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,8 +219,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   // the ring barrier (its latency hides behind the wait) and the key row of
   // the load becomes a scalar base; each lane adds its 32-bit offset.
   // Masked loads (padded or invalid entries, rows past Nk) read row 0.
+  // nvr counts the load's rows below Nk: a load crossing Nk (rare) re-reads
+  // its last valid row in the lanes of the rows past it.
   typedef const __attribute__((address_space(4))) int32_t cint_t;
-  auto rows_of = [&](int t, int (&row)[LPW]) {
+  auto rows_of = [&](int t, int (&row)[LPW], int (&nvr)[LPW]) {
     int blk[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {  // all loads first (one wait); entry 0 stands in past the list
@@ -223,20 +234,29 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
       const int pos = t * KT + wave * RPW + j * RPI;
       const unsigned b = (unsigned)blk[j];
       const unsigned kk = (b << a.kv_shift) + (unsigned)(pos & (kvb - 1));
-      // (the load's rows are all below Nk or all past it)
       const bool ok = ((pos >> a.kv_shift) < pcnt) & (b < (unsigned)a.M) & (kk < (unsigned)a.Nk);
       row[j] = ok ? (int)kk : 0;
+      const int left = a.Nk - row[j];
+      nvr[j] = PART ? (left < RPI ? left : RPI) : RPI;
     }
   };
-  auto issue_rows = [&](auto slot_c, const int (&row)[LPW]) {
+  auto issue_rows = [&](auto slot_c, const int (&row)[LPW], const int (&nvr)[LPW]) {
     unsigned char *kt = kslot(slot_c);
     unsigned char *vt = vslot(slot_c);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const size_t src = (size_t)row[j] * ROWB;
       const int dst = (wave * RPW + j * RPI) * ROWB;
-      __builtin_amdgcn_global_load_lds((const void *)(kbase + src + (unsigned)g_koff[j]), (lds_void *)(kt + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vbase + src + (unsigned)g_voff[j]), (lds_void *)(vt + dst), 16, 0, 0);
+      unsigned ko = (unsigned)g_koff[j], vo = (unsigned)g_voff[j];
+      if (PART && nvr[j] < RPI) {  // uniform
+        const unsigned rel = (unsigned)((lane / NCH) * ROWB);
+        const unsigned cap = (unsigned)((nvr[j] - 1) * ROWB);
+        const unsigned fix = rel < cap ? rel : cap;
+        ko = ko - rel + fix;
+        vo = vo - rel + fix;
+      }
+      __builtin_amdgcn_global_load_lds((const void *)(kbase + src + ko), (lds_void *)(kt + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vbase + src + vo), (lds_void *)(vt + dst), 16, 0, 0);
     }
   };
 
@@ -262,9 +282,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   };
   auto issue_any = [&](auto slot_c, int t) {
     if constexpr (QUAD) {
-      int row[LPW];
-      rows_of(t, row);
-      issue_rows(slot_c, row);
+      int row[LPW], nvr[LPW];
+      rows_of(t, row, nvr);
+      issue_rows(slot_c, row, nvr);
     } else {
       issue(slot_c, t);
     }
@@ -354,6 +374,18 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+    if (QUAD && PART) {
+      // keys past Nk inside a group of this tile (rare): masked here, after
+      // the reference update, which their logits (copies of a valid key's
+      // logit in the same group) cannot have moved
+      const uint32_t pmt = pmask_s[t];
+      if (__builtin_amdgcn_readfirstlane(pmt) != 0u) {
+        const uint32_t pm = pmt >> (8 * hh);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[r] = ((pm >> (16 * (r >> 3) + (r & 7))) & 1u) ? -__builtin_inff() : sacc[r];
+      }
+    }
     bf16x8 pf[2];
     {
 #pragma unroll
@@ -400,12 +432,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     constexpr int S = decltype(slot_c)::value;
     constexpr int SN = (S + 2) % NBUF;
     const bool more = t + 2 < ntiles;
-    int row[LPW];
-    if (QUAD && more) rows_of(t + 2, row);
+    int row[LPW], nvr[LPW];
+    if (QUAD && more) rows_of(t + 2, row, nvr);
     if (t + 1 < ntiles) ring_barrier<LPT>();
     else ring_barrier<0>();
     if (more) {
-      if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row);
+      if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
       else issue(std::integral_constant<int, SN>(), t + 2);
     }
     qk(slot_c, sA);
@@ -424,15 +456,28 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
     if constexpr (QUAD) {
       // shift of every 4-key group of the phase's tiles, -inf for groups of
-      // padded or invalid entries and past Nk
+      // padded or invalid entries and wholly past Nk; a group crossing Nk
+      // marks its rows past Nk
+      if (PART) {
+        for (int i = tid; i < ntiles; i += NW * 64) pmask_s[i] = 0u;
+        __syncthreads();
+      }
       const int ng = ntiles * (KT / 4);
       for (int g = tid; g < ng; g += NW * 64) {
         const int e = (4 * g) >> a.kv_shift;
         float bv = -__builtin_inff();
         if (e < pc) {
           const int blk = idx_row[base + e];
-          if (blk >= 0 && blk < a.M && (blk << a.kv_shift) + ((4 * g) & (kvb - 1)) < a.Nk)
-            bv = bias_row ? bias_row[base + e] * kLog2e : 0.f;
+          if (blk >= 0 && blk < a.M) {
+            const int k0 = (blk << a.kv_shift) + ((4 * g) & (kvb - 1));
+            if (k0 < a.Nk) {
+              bv = bias_row ? bias_row[base + e] * kLog2e : 0.f;
+              if (PART && k0 + 4 > a.Nk) {
+                const uint32_t past = (0xfu << (a.Nk - k0)) & 0xfu;
+                atomicOr(&pmask_s[g >> 3], past << (4 * (g & 7)));
+              }
+            }
+          }
         }
         gb_s[(g & ~7) | quad_pos(g & 7)] = bv;
       }
@@ -503,16 +548,19 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   a.total_wg = (int)total;
   dim3 grid((unsigned)total), block(256);
   // Group shifts and the scalar gather need every wave load (4 rows at
-  // d = 128, 8 at d = 64) inside one KV block and wholly below Nk or wholly
-  // past it: blocks of at least that many keys and Nk a multiple of it.
+  // d = 128, 8 at d = 64) inside one KV block: blocks of at least that many
+  // keys.  Loads and groups crossing Nk are handled where they occur.
   const int rows_per_load = d == 128 ? 4 : 8;
-  const bool quad = kv_block >= rows_per_load && Nk % rows_per_load == 0;
+  const bool quad = kv_block >= rows_per_load;
+  const bool part = quad && Nk % rows_per_load != 0;
   if (d == 128) {
-    if (quad) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, stream, a);
+    if (part) hipLaunchKernelGGL((attn_fwd_kernel<128, true, true>), grid, block, 0, stream, a);
+    else if (quad) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<128, false, false>), grid, block, 0, stream, a);
   } else {
-    if (quad) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, stream, a);
+    if (part) hipLaunchKernelGGL((attn_fwd_kernel<64, true, true>), grid, block, 0, stream, a);
+    else if (quad) hipLaunchKernelGGL((attn_fwd_kernel<64, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false, false>), grid, block, 0, stream, a);
   }
   return status_of(hipGetLastError());
 }

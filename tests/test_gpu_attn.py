@@ -128,12 +128,15 @@ def _valid_entries(idx_row, bias_row, c, M):
     return bl[keep], b[keep]
 
 
-@pytest.mark.parametrize("d,Nk,kvb", [(128, 132, 8), (128, 260, 4), (64, 136, 16)])
+@pytest.mark.parametrize("d,Nk,kvb", [(128, 132, 8), (128, 260, 4), (64, 136, 16),
+                                      (128, 130, 4), (128, 263, 8), (128, 3, 4), (64, 131, 8),
+                                      (64, 5, 16)])
 def test_attn_group_shift_edges(env, d, Nk, kvb):
-    """The group-shift path (every wave load inside one KV block, Nk a whole
-    number of loads): a row with count 0, invalid indices (-1, M, 1000) among
-    valid ones, entries past the count, and the partial last block whose
-    tail groups lie past Nk."""
+    """The group-shift path (every wave load inside one KV block): a row with
+    count 0, invalid indices (-1, M, 1000) among valid ones, entries past the
+    count, and the partial last block -- whole groups past Nk, and (Nk not a
+    whole number of wave loads) a load and a 4-key group crossing Nk, down
+    to Nk smaller than one load."""
     bsa, g, torch = env
     g.say(f"case attn group-shift edges d={d} Nk={Nk} kv_block={kvb}")
     qb, kb, vb = make_qkv(1, 1, 384, 1, d, seed=Nk + kvb)
