@@ -24,6 +24,11 @@ What it follows (the pages are Korean summaries; facts restated, not quoted):
 * ``basa``    -- BASA page (onedev.kr/papers/688): shifted windows spanning
   all frames, pooled K/V memory, routed raw windows; key set = own window
   U routed windows U pooled memory.
+* ``diag``    -- accuracy diagnostics of a plan (AB-Attention page, sections
+  "무엇과 다른가", "어떻게 쓰나" and the ablation paragraph of "전제와 한계"):
+  the true attention mass of every KV block per query block, the mass a
+  plan retains, the oracle top-k by that mass, and the output error against
+  dense attention.
 
 Precision: fp64 everywhere, with one deliberate exception.  The k-means
 assignment (an argmin) and the BASA window routing (a top-2) are discrete
@@ -34,8 +39,10 @@ those decisions is fp64 again.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, special cases, brute force or figures printed on the
-pages.  The pages' quality claims (dB, retained mass, 41 % lower error) need
-real model activations and are parity unpinned; nothing here computes them.
+pages.  The pages' quality claims (dB, retained mass, 41 % lower error) were
+measured on real model activations; ``diag`` computes the same quantities on
+the seeded synthetic inputs, whose values are not expected to match the
+pages' figures.
 """
 
-from . import splitmix, select, plan, attn, basa  # noqa: F401
+from . import splitmix, select, plan, attn, basa, diag  # noqa: F401
