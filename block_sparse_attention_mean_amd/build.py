@@ -1,6 +1,7 @@
 """Build libbsa.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m block_sparse_attention_mean_amd.build  (or build() below).
+Usage: python block_sparse_attention_mean_amd/build.py  (or build() below).  It
+runs as a script, not through the package, whose import loads the library.
 Every source is compiled on each call; objects go to ``_build/`` next to
 this file and the shared library to ``libbsa.so``.
 """
@@ -16,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
-SOURCES = ["api.cpp", "attn_fwd.hip", "plan.hip", "select.hip", "basa.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "plan.hip", "select.hip", "basa.hip", "diag.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.
