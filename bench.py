@@ -17,8 +17,16 @@ path at the 1664x960 / 81-frame latent (21 x 60 x 104, 12 heads, 10 x 10
 windows, 4 x 4 pooled memory, top-2 routing): bsa_basa_plan ->
 bsa_attn_fwd -> bsa_window_unpermute, reported the same way.
 
+With ``--accuracy`` it prints instead one JSON report of the accuracy
+diagnostics (block_sparse_attention_mean_amd.accuracy) on the first
+``--accuracy-heads`` heads of the workload at its token budget: the oracle
+top-k's retained mass against KV block size, the output error of SIP, of an
+oracle top-k and of the ablation variants against dense attention, and the
+timing of the block-mass kernel.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload wan14b_720p|basa_1664x960]
+       python bench.py --accuracy [--workload wan14b_720p] [--accuracy-heads 40]
 """
 from __future__ import annotations
 
@@ -52,6 +60,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-heads", type=int, default=3,
                    help="whole heads of the workload in the oracle sample")
+    p.add_argument("--accuracy", action="store_true",
+                   help="print the accuracy diagnostics report instead of the benchmark line")
+    p.add_argument("--accuracy-heads", type=int, default=40)
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this size (counter calibration)")
     return p.parse_args()
@@ -296,6 +307,83 @@ def run_basa(args):
     print(json.dumps(rec), flush=True)
 
 
+def run_accuracy(args):
+    """Accuracy diagnostics of the workload's plans (see the module docstring)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    from block_sparse_attention_mean_amd import accuracy as acc
+    from synth import CONFIGS, make_qkv
+
+    c = CONFIGS[args.workload]
+    T, Hg, Wg, d = c["T"], c["Hg"], c["Wg"], c["d"]
+    H = min(args.accuracy_heads, c["H"])
+    N = T * Hg * Wg
+    tokens = c["budget"] * c["kv_block"]
+    dev = torch.device("cuda:0")
+    log(f"[accuracy] generating {args.workload}: heads 0..{H - 1}, N={N}")
+    qb, kb, vb = make_qkv(T, Hg, Wg, H, d, seed=args.seed, workers=min(16, os.cpu_count() or 1))
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    del qb, kb, vb
+    log("[accuracy] dense reference")
+    ref, lse = acc.dense_reference(q, k, v)
+    torch.cuda.synchronize()
+
+    # block-mass kernel timing (4-token blocks), HIP events on its stream
+    stream = torch.cuda.current_stream()
+    mass = bsa.bsa_block_mass(q, k, lse, 128, 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        bsa.bsa_block_mass(q, k, lse, 128, 4, mass=mass)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mass_ms = e0.elapsed_time(e1) / reps
+    mass_tf = 2.0 * d * N * N * H / mass_ms / 1e9
+    row_sums = mass.double().sum(dim=-1)
+    row_dev = float((row_sums - 1).abs().max())
+    del mass
+
+    log("[accuracy] oracle top-k curve")
+    curve = acc.oracle_topk_curve(q, k, lse, tokens)
+    log("[accuracy] variants")
+    var = acc.variants(q, k, v, ref, lse, tokens, seed=args.seed, n_clusters=c["n_clusters"],
+                       kmeans_iters=c["kmeans_iters"])
+    mean = lambda a: round(float(np.mean(a)), 5)  # noqa: E731
+    rep = {
+        "report": "accuracy",
+        "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, heads 0..{H - 1}, "
+                    f"d={d}, token budget {tokens} ({100 * tokens / N:.2f} % of the keys)",
+        "data": "synthetic",
+        "seed": args.seed,
+        "oracle_topk_retained_mass": {str(b): mean(r) for b, r in curve.items()},
+        "variants": {n: {"error": mean(r["error"]),
+                         "error_per_head": [round(float(x), 5) for x in np.ravel(r["error"])],
+                         **({"retained_mass": mean(r["retained_mass"])}
+                            if "retained_mass" in r else {})}
+                     for n, r in var.items()},
+        "sip_error_vs_oracle_topk": round(float(np.mean(var["ibcs_sip"]["error"])
+                                                / np.mean(var["oracle_topk"]["error"])), 4),
+        "block_mass": {"kernel": "bsa::block_mass_kernel<128>", "kv_block": 4,
+                       "ms_per_call": round(mass_ms, 4), "achieved": round(mass_tf, 2),
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(mass_tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+                       "max_row_sum_deviation": row_dev},
+    }
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rep["copy_calib_bytes"] = n
+    print(json.dumps(rep), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,6 +391,8 @@ def main():
               "measured on a single MI355X; heads shard across GPUs with no communication.",
               file=sys.stderr)
         sys.exit(2)
+    if args.accuracy:
+        return run_accuracy(args)
     if args.workload.startswith("basa"):
         return run_basa(args)
     import numpy as np

@@ -3,8 +3,8 @@
 Thin Python binding over the C ABI of ``libbsa.so`` (declared in
 ``include/bsa.h``).  It only marshals arguments: every step of the path runs
 in the library's HIP kernels.  PyTorch provides device memory and the
-current stream.  The library must be built (``python -m
-block_sparse_attention_mean_amd.build``); importing the binding without it
+current stream.  The library must be built (``python
+block_sparse_attention_mean_amd/build.py``); importing the binding without it
 raises ImportError -- there is no fallback path.
 """
 from __future__ import annotations
@@ -16,7 +16,8 @@ import os
 __all__ = [
     "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
-    "bsa_basa_plan", "bsa_window_unpermute", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH",
+    "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
+    "bsa_output_error", "dense_plan", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
@@ -24,7 +25,7 @@ PLAN_SIP, PLAN_TOPK = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
-                      "`python -m block_sparse_attention_mean_amd.build`")
+                      "`python block_sparse_attention_mean_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -51,11 +52,18 @@ lib.bsa_basa_plan.restype = _i
 lib.bsa_basa_plan.argtypes = [_p, _p, _p] + [_i] * 14 + [_p] * 6 + [_p, _sz, _p]
 lib.bsa_window_unpermute.restype = _i
 lib.bsa_window_unpermute.argtypes = [_p, _p] + [_i] * 10 + [_p]
+lib.bsa_block_mass.restype = _i
+lib.bsa_block_mass.argtypes = [_p, _p, _p] + [_i] * 7 + [_f, _p, _p]
+lib.bsa_plan_coverage.restype = _i
+lib.bsa_plan_coverage.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p]
+lib.bsa_output_error.restype = _i
+lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 
 # Exported symbols of include/bsa.h (checked by the CPU tests).
 SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bsa_select_scores",
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
-           "bsa_basa_plan", "bsa_window_unpermute"]
+           "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
+           "bsa_output_error"]
 
 
 class BsaError(RuntimeError):
@@ -225,6 +233,68 @@ def bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=None, stream=N
     _check(lib.bsa_window_unpermute(_ptr(out_perm), _ptr(out), B, H, T, Hg, Wg, d, wh, ww, dy,
                                     dx, _stream(stream)), "bsa_window_unpermute")
     return out
+
+
+def dense_plan(B, H, Nq, Nk, kv_block=128, device="cuda"):
+    """A list of every KV block for every query block (no bias): with it,
+    bsa_attn_fwd computes dense attention and its lse is the dense one."""
+    import torch
+    nqb, M = -(-Nq // 128), -(-Nk // kv_block)
+    idx = torch.arange(M, dtype=torch.int32, device=device).expand(B, H, nqb, M).contiguous()
+    count = torch.full((B, H, nqb), M, dtype=torch.int32, device=device)
+    return idx, count
+
+
+def bsa_block_mass(q, k, lse, q_block=128, kv_block=4, softmax_scale=0.0, mass=None,
+                   stream=None):
+    """q [B,H,Nq,d], k [B,H,Nk,d] bf16, lse [B,H,Nq] fp32 (dense) -> mass
+    [B,H,nQB,M] fp32: true attention mass of every KV block per query block."""
+    import torch
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    _need(lse, torch.float32, "lse", 3)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if mass is None:
+        mass = torch.empty((B, H, -(-Nq // q_block), -(-Nk // kv_block)), dtype=torch.float32,
+                           device=q.device)
+    _check(lib.bsa_block_mass(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, d, q_block, kv_block,
+                              float(softmax_scale), _ptr(mass), _stream(stream)), "bsa_block_mass")
+    return mass
+
+
+def bsa_plan_coverage(mass, idx, count, coverage=None, stream=None):
+    """mass [..., M] fp32, idx [..., L] int32, count [...] int32 -> retained
+    mass [...] fp64."""
+    import torch
+    _need(mass, torch.float32, "mass")
+    _need(idx, torch.int32, "idx")
+    _need(count, torch.int32, "count")
+    lead = tuple(mass.shape[:-1])
+    rows = count.numel()
+    if tuple(idx.shape[:-1]) != lead or tuple(count.shape) != lead:
+        raise ValueError("mass, idx and count must share their leading dims")
+    if coverage is None:
+        coverage = torch.empty(lead, dtype=torch.float64, device=mass.device)
+    _check(lib.bsa_plan_coverage(_ptr(mass), _ptr(idx), _ptr(count), rows, mass.shape[-1],
+                                 idx.shape[-1], _ptr(coverage), _stream(stream)),
+           "bsa_plan_coverage")
+    return coverage
+
+
+def bsa_output_error(out, ref, sums=None, stream=None):
+    """out, ref [B,H,N,d] bf16 -> sums [B,H,2] fp64: (sum (out-ref)^2, sum ref^2)."""
+    import torch
+    _need(out, torch.bfloat16, "out", 4)
+    _need(ref, torch.bfloat16, "ref", 4)
+    if out.shape != ref.shape:
+        raise ValueError("out and ref differ in shape")
+    B, H, N, d = out.shape
+    if sums is None:
+        sums = torch.empty((B, H, 2), dtype=torch.float64, device=out.device)
+    _check(lib.bsa_output_error(_ptr(out), _ptr(ref), B * H, N * d, _ptr(sums), _stream(stream)),
+           "bsa_output_error")
+    return sums
 
 
 def default_scale(d: int) -> float:

@@ -32,6 +32,13 @@ int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, 
 int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg,
                             int Wg, int d, int wh, int ww, int dy, int dx, hipStream_t stream);
 uint64_t sampling_offset(uint64_t seed, uint64_t row);
+int mass_chunk_keys(int kv_block);
+int launch_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
+                      int d, int kv_block, float scale, float *mass, hipStream_t stream);
+int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *count, int rows,
+                         int M, int max_blocks, double *cov, hipStream_t stream);
+int launch_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
+                        hipStream_t stream);
 }  // namespace bsa
 
 namespace {
@@ -179,6 +186,47 @@ int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, i
   if (!aligned(out_perm, 16) || !aligned(out, 16)) return BSA_ERR_ALIGN;
   return bsa::launch_window_unpermute(out_perm, out, B, H, T, Hg, Wg, d, wh, ww, dy, dx,
                                       (hipStream_t)stream);
+}
+
+int bsa_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
+                   int d, int q_block, int kv_block, float softmax_scale, float *mass,
+                   void *stream) {
+  if (!q || !k || !lse || !mass) return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || kv_block < 1) return BSA_ERR_ARG;
+  if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || q_block != 128 || kv_block > 1024) return BSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4) || !aligned(mass, 4))
+    return BSA_ERR_ALIGN;
+  const long long nqb = (Nq + 127) / 128, M = ((long long)Nk + kv_block - 1) / kv_block;
+  const long long ck = bsa::mass_chunk_keys(kv_block);
+  const long long wgs = (long long)B * H * nqb * ((Nk + ck - 1) / ck);
+  if ((long long)B * H * Nq * d > kMaxIndex * 8 || (long long)B * H * Nk * d > kMaxIndex * 8 ||
+      (long long)B * H * nqb * M > kMaxIndex || wgs > kMaxIndex)
+    return BSA_ERR_SIZE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  return bsa::launch_block_mass(q, k, lse, B, H, Nq, Nk, d, kv_block, scale, mass,
+                                (hipStream_t)stream);
+}
+
+int bsa_plan_coverage(const float *mass, const int32_t *idx, const int32_t *count, int rows,
+                      int M, int max_blocks, double *coverage, void *stream) {
+  if (!mass || !idx || !count || !coverage) return BSA_ERR_ARG;
+  if (rows < 1 || M < 1 || max_blocks < 1) return BSA_ERR_ARG;
+  if (!aligned(mass, 4) || !aligned(idx, 4) || !aligned(count, 4) || !aligned(coverage, 8))
+    return BSA_ERR_ALIGN;
+  if ((long long)rows * M > kMaxIndex * 8 || (long long)rows * max_blocks > kMaxIndex * 8)
+    return BSA_ERR_SIZE;
+  return bsa::launch_plan_coverage(mass, idx, count, rows, M, max_blocks, coverage,
+                                   (hipStream_t)stream);
+}
+
+int bsa_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
+                     void *stream) {
+  if (!out || !ref || !sums) return BSA_ERR_ARG;
+  if (slabs < 1 || n < 8 || n % 8 != 0) return BSA_ERR_ARG;
+  if (!aligned(out, 16) || !aligned(ref, 16) || !aligned(sums, 8)) return BSA_ERR_ALIGN;
+  if (slabs > 65535 * 16) return BSA_ERR_SIZE;
+  return bsa::launch_output_error(out, ref, slabs, n, sums, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -21,7 +21,12 @@
  *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
  *                      structure of the BASA page (onedev.kr/papers/688,
  *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
- *                      into block lists for bsa_attn_fwd.
+ *                      into block lists for bsa_attn_fwd;
+ *   bsa_block_mass,    accuracy diagnostics of a plan: the true attention
+ *   bsa_plan_coverage, mass of every KV block, the mass a plan retains, and
+ *   bsa_output_error   the output error against dense attention
+ *                      (AB-Attention page, sections "무엇과 다른가" and
+ *                      "어떻게 쓰나").
  *
  * Conventions for every entry point:
  *   - Tensors are dense, row-major and contiguous.  [B,H,N,d] means
@@ -226,6 +231,46 @@ int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int
 
 int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
                          int d, int wh, int ww, int dy, int dx, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Accuracy diagnostics (AB-Attention page, onedev.kr/papers/1521: section
+ * "무엇과 다른가" compares the attention mass an oracle top-k keeps at
+ * 128-token and 4-token KV blocks; section "어떻게 쓰나" compares SIP's
+ * attention error with that of an oracle top-k).
+ *
+ * bsa_block_mass: true attention mass of every KV block for every query
+ * block of (b, h):
+ *   mass[b,h,i,j] = (1/n_i) sum_{n in query block i} sum_{t in block j, t < Nk}
+ *                   exp(scale q_n . k_t - lse[b,h,n])
+ * with n_i the block's query count.  lse [B,H,Nq] fp32 must be the dense
+ * natural-log normaliser of each query (the lse output of bsa_attn_fwd with
+ * every block listed and no bias); then every row of mass sums to 1.
+ * q [B,H,Nq,d], k [B,H,Nk,d] bf16, 16-byte aligned; mass
+ * [B,H,ceil(Nq/128),ceil(Nk/kv_block)] fp32.  q_block = 128; kv_block any
+ * integer in [1, 1024] (not only powers of two); d in {64, 128};
+ * softmax_scale <= 0 selects 1/sqrt(d).  Logits are bf16 products summed
+ * in fp32 (matrix cores); exponentials and sums in fp32; the result is
+ * deterministic.
+ * --------------------------------------------------------------------- */
+int bsa_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
+                   int d, int q_block, int kv_block, float softmax_scale, float *mass,
+                   void *stream);
+
+/* bsa_plan_coverage: retained mass of a plan,
+ *   coverage[r] = sum_{e < count[r]} mass[r, idx[r, e]]   (fp64, in list
+ * order), for rows r of [rows, M] fp32 mass and [rows, max_blocks] int32
+ * idx; count is clamped to [0, max_blocks] and entries outside [0, M) are
+ * skipped.  coverage [rows] fp64. */
+int bsa_plan_coverage(const float *mass, const int32_t *idx, const int32_t *count, int rows,
+                      int M, int max_blocks, double *coverage, void *stream);
+
+/* bsa_output_error: for each of `slabs` consecutive slabs of n bf16 values
+ * (one head's [N, d] output: n = N * d), sums[2 s] = sum (out - ref)^2 and
+ * sums[2 s + 1] = sum ref^2, fp64 (relative Frobenius error =
+ * sqrt(sums[2 s] / sums[2 s + 1])).  n must be a multiple of 8; out and ref
+ * 16-byte aligned; sums [slabs, 2] fp64.  Deterministic. */
+int bsa_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
+                     void *stream);
 
 #ifdef __cplusplus
 }

@@ -124,3 +124,32 @@ def test_basa_rejects_invalid_arguments(bsa):
         bsa.bsa_basa_layout(21, 60, 104, 128, 70, 10, 4, 4, 2)
     with pytest.raises(bsa.BsaError):   # 3-token kv blocks are not powers of two
         bsa.bsa_basa_layout(21, 60, 104, 128, 10, 10, 4, 4, 2, kv_block=3)
+
+
+def _mass(bsa, **kw):
+    a = dict(q=FAKE, k=FAKE, lse=FAKE, B=1, H=1, Nq=300, Nk=500, d=128, qb=128, kvb=4, scale=0.0,
+             mass=FAKE)
+    a.update(kw)
+    return bsa.lib.bsa_block_mass(a["q"], a["k"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                  a["d"], a["qb"], a["kvb"], a["scale"], a["mass"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(mass=None), -1), (dict(Nk=0), -1),
+    (dict(kvb=0), -1), (dict(scale=float("inf")), -1),
+    (dict(d=96), -2), (dict(qb=64), -2), (dict(kvb=1025), -2),
+    (dict(k=FAKE + 8), -4), (dict(lse=FAKE + 2), -4),
+    (dict(H=2**16, Nq=2**16, Nk=2**16), -7),
+])
+def test_block_mass_rejects_invalid_arguments(bsa, kw, status):
+    assert _mass(bsa, **kw) == status
+
+
+def test_coverage_and_error_reject_invalid_arguments(bsa):
+    L = bsa.lib
+    assert L.bsa_plan_coverage(None, FAKE, FAKE, 4, 10, 3, FAKE, None) == -1
+    assert L.bsa_plan_coverage(FAKE, FAKE, FAKE, 0, 10, 3, FAKE, None) == -1
+    assert L.bsa_plan_coverage(FAKE, FAKE, FAKE, 4, 10, 3, FAKE + 4, None) == -4
+    assert L.bsa_output_error(FAKE, FAKE, 2, 12, FAKE, None) == -1
+    assert L.bsa_output_error(FAKE, None, 2, 16, FAKE, None) == -1
+    assert L.bsa_output_error(FAKE + 8, FAKE, 2, 16, FAKE, None) == -4
