@@ -1,14 +1,20 @@
 """Full-size parity at the Wan2.1-14B 720p workload in the launch
 configuration the benchmark times: all 40 heads of 75,600 tokens go through
 bsa_select_scores -> bsa_sip_plan (SIP, budget 2048, seed 0) ->
-bsa_attn_fwd in single calls, then sampled outputs are checked against the
-oracle one by one:
+bsa_attn_fwd in single calls, and sampled outputs are checked against the
+oracle one by one.  The oracle only ever sees its own values:
 
-* scores: sampled rows of heads 0 and 39 against the oracle's selector;
-* plan: sampled rows of three heads, the oracle planning on the GPU's own
-  scores (widened exactly) -- indices, counts and lambda bit-exact;
-* attention: sampled query blocks of three heads (including the 80-row last
-  block) against the oracle on the GPU's plan."""
+* scores: sampled rows of heads 0, 17 and 39 against the oracle's selector;
+* plan: the oracle's scores of those heads replace the device's in the
+  score tensor and the 40-head plan call runs again; the rows of those heads
+  must equal the oracle's plan of its own scores (indices, counts, lambda
+  bit-exact);
+* attention: the 40-head attention call on that plan; sampled query blocks
+  of the three heads (including the 80-row last block) against the oracle
+  on its own plan;
+* the plan of the device's own scores (the benchmark's chain) is checked
+  for validity: s distinct ascending blocks per row, finite shifts >= 0,
+  and agreement with the oracle's plan on almost every entry."""
 import os
 
 import numpy as np
@@ -20,6 +26,9 @@ from oracle import select as osel
 from synth import CONFIGS, bf16_bits_to_f64, make_qkv
 
 pytestmark = pytest.mark.gpu
+
+
+HEADS = (0, 17, 39)
 
 
 @pytest.fixture(scope="module")
@@ -39,18 +48,33 @@ def run():
     idx, bias, cnt, lam = bsa.bsa_sip_plan(S, s, bsa.PLAN_SIP, seed=0, want_lambda=True)
     out, _ = bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb)
     torch.cuda.synchronize()
-    return dict(c=c, qb=qb, kb=kb, vb=vb, S=S, idx=idx, bias=bias, cnt=cnt, lam=lam, out=out, g=g)
+    g.say("case full size wan14b_720p: oracle scores of the sampled heads")
+    So = {h: osel.select_scores_head(qb[0, h], kb[0, h], 128, kvb, c["n_clusters"],
+                                     c["kmeans_iters"])[0] for h in HEADS}
+    g.say("case full size wan14b_720p: plan and attention on the oracle's scores")
+    S2 = S.clone()
+    for h in HEADS:
+        S2[0, h] = g.dev_f32(So[h])
+    idx2, bias2, cnt2, lam2 = bsa.bsa_sip_plan(S2, s, bsa.PLAN_SIP, seed=0, want_lambda=True)
+    out2, _ = bsa.bsa_attn_fwd(q, k, v, idx2, bias2, cnt2, 128, kvb)
+    torch.cuda.synchronize()
+    return dict(c=c, qb=qb, kb=kb, vb=vb, S=S, So=So, idx=idx, bias=bias, cnt=cnt, out=out,
+                idx2=idx2, bias2=bias2, cnt2=cnt2, lam2=lam2, out2=out2, g=g)
+
+
+def _oracle_plan(run, h, rows):
+    c, nqb = run["c"], run["S"].shape[2]
+    offs = np.array([opl.sampling_offset(0, h * nqb + int(i)) for i in rows], dtype=np.uint64)
+    return opl.plan(run["So"][h][rows], c["budget"], opl.SIP, offsets=offs)
 
 
 def test_fullsize_scores_sampled_rows(run):
-    g, c = run["g"], run["c"]
-    for h in (0, 39):
+    g = run["g"]
+    for h in HEADS:
         g.say(f"case full size scores head {h}")
-        want, _, _ = osel.select_scores_head(run["qb"][0, h], run["kb"][0, h], 128, c["kv_block"],
-                                             c["n_clusters"], c["kmeans_iters"])
         rows = np.r_[0:4, 290:294, 587:591]
         got = run["S"][0, h, rows].cpu().numpy().astype(np.float64)
-        ref = want[rows]
+        ref = run["So"][h][rows]
         keep = np.abs(ref) >= 1e-30
         rel = np.abs(got - ref)[keep] / np.abs(ref)[keep]
         g.say(f"  max rel {rel.max():.3e}")
@@ -58,19 +82,16 @@ def test_fullsize_scores_sampled_rows(run):
 
 
 def test_fullsize_plan_sampled_rows(run):
-    g, c = run["g"], run["c"]
+    g = run["g"]
     nqb = run["S"].shape[2]
-    for h in (0, 17, 39):
+    for h in HEADS:
         g.say(f"case full size plan head {h}")
         rows = np.r_[0:3, 300:303, nqb - 3:nqb]
-        S = run["S"][0, h, rows].cpu().numpy().astype(np.float64)
-        # oracle offsets of these rows: the same seeded function, row = h * nQB + i
-        offs = np.array([opl.sampling_offset(0, h * nqb + int(i)) for i in rows], dtype=np.uint64)
-        want_idx, want_bias, want_cnt, want_lam = opl.plan(S, c["budget"], opl.SIP, offsets=offs)
-        got_idx = run["idx"][0, h, rows].cpu().numpy()
-        got_cnt = run["cnt"][0, h, rows].cpu().numpy()
-        got_bias = run["bias"][0, h, rows].cpu().numpy()
-        got_lam = run["lam"][0, h, rows].cpu().numpy()
+        want_idx, want_bias, want_cnt, want_lam = _oracle_plan(run, h, rows)
+        got_idx = run["idx2"][0, h, rows].cpu().numpy()
+        got_cnt = run["cnt2"][0, h, rows].cpu().numpy()
+        got_bias = run["bias2"][0, h, rows].cpu().numpy()
+        got_lam = run["lam2"][0, h, rows].cpu().numpy()
         np.testing.assert_array_equal(got_cnt, want_cnt)
         np.testing.assert_array_equal(got_idx, want_idx)
         np.testing.assert_array_equal(got_lam, want_lam)
@@ -82,14 +103,42 @@ def test_fullsize_attention_sampled_blocks(run):
     g, c = run["g"], run["c"]
     nqb = run["S"].shape[2]
     rng = np.random.default_rng(7)
-    for h in (0, 17, 39):
+    for h in HEADS:
         blocks = sorted(set(rng.choice(nqb - 1, 7, replace=False).tolist()) | {nqb - 1})
         g.say(f"case full size attention head {h} blocks {blocks}")
-        idx = run["idx"][0, h].cpu().numpy()
-        bias = run["bias"][0, h].cpu().numpy()
-        cnt = run["cnt"][0, h].cpu().numpy()
+        idx = np.full((nqb, c["budget"]), -1, np.int32)
+        bias = np.zeros((nqb, c["budget"]), np.float32)
+        cnt = np.zeros(nqb, np.int32)
+        pi, pb, pc, _ = _oracle_plan(run, h, np.array(blocks))
+        idx[blocks], bias[blocks], cnt[blocks] = pi, pb, pc
         q, k, v = (bf16_bits_to_f64(x[0, h]) for x in (run["qb"], run["kb"], run["vb"]))
         ref, _ = oat.attn_fwd(q, k, v, 128, c["kv_block"], idx, bias, cnt, blocks=blocks)
         rows = np.concatenate([np.arange(i * 128, min(q.shape[0], i * 128 + 128)) for i in blocks])
-        got = g.from_dev_bf16(run["out"][0, h])
+        got = g.from_dev_bf16(run["out2"][0, h])
         g.assert_attn_close(got[rows], ref[rows], f"head {h} sampled blocks")
+
+
+def test_fullsize_chain_plan_is_valid(run):
+    """The benchmark's own chain (plan of the device's scores): every row
+    holds exactly s distinct ascending blocks in range with finite shifts
+    >= 0, the outputs are finite, and the sampled heads' plans agree with
+    the oracle's plan of its own scores on almost every entry (the two
+    score sets differ in the last bits, which can move a sampling point
+    across a block boundary)."""
+    g, c = run["g"], run["c"]
+    s, nqb = c["budget"], run["S"].shape[2]
+    M = run["S"].shape[3]
+    cnt = run["cnt"].cpu().numpy()
+    assert (cnt == s).all()
+    idx = run["idx"].cpu().numpy()
+    assert (np.diff(idx, axis=-1) > 0).all() and idx.min() >= 0 and idx.max() < M
+    bias = run["bias"].cpu().numpy()
+    assert np.isfinite(bias).all() and (bias >= 0).all()
+    import torch
+    assert bool(torch.isfinite(run["out"].float()).all())
+    for h in HEADS:
+        rows = np.arange(nqb)
+        want_idx = _oracle_plan(run, h, rows)[0]
+        same = np.mean([len(np.intersect1d(idx[0, h, i], want_idx[i])) / s for i in rows])
+        g.say(f"  head {h}: {100 * same:.4f} % of plan entries shared with the oracle's")
+        assert same >= 0.999
