@@ -24,9 +24,17 @@ top-k's retained mass against KV block size, the output error of SIP, of an
 oracle top-k and of the ablation variants against dense attention, and the
 timing of the block-mass kernel.
 
+With ``--curve`` it prints one JSON report of the latency-density curve at
+the workload's shape: the selector once, then for SIP budgets from 1 % to
+100 % of the KV blocks the plan and the attention times, against two dense
+bf16 attentions of the same shape (bsa_attn_fwd over every 128-token block,
+and torch's flash SDPA timed in a child process), with the sparse/dense
+crossover.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload wan14b_720p|basa_1664x960]
        python bench.py --accuracy [--workload wan14b_720p] [--accuracy-heads 40]
+       python bench.py --curve [--workload wan14b_720p]
 """
 from __future__ import annotations
 
@@ -63,6 +71,11 @@ def parse():
     p.add_argument("--accuracy", action="store_true",
                    help="print the accuracy diagnostics report instead of the benchmark line")
     p.add_argument("--accuracy-heads", type=int, default=40)
+    p.add_argument("--curve", action="store_true",
+                   help="print the latency-density curve report instead of the benchmark line")
+    p.add_argument("--dense-sdpa", action="store_true",
+                   help="(child of --curve) time torch's flash SDPA at the workload's shape")
+    p.add_argument("--reps", type=int, default=3)
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this size (counter calibration)")
     return p.parse_args()
@@ -384,6 +397,137 @@ def run_accuracy(args):
     print(json.dumps(rep), flush=True)
 
 
+CURVE_DENSITIES = (0.01, 0.02, 0.05, None, 0.2, 0.3, 0.5, 0.75, 1.0)   # None: the workload's
+
+
+def _inputs(args, c, H=None):
+    import numpy as np
+    import torch
+    from synth import make_qkv
+    H = c["H"] if H is None else H
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], H, c["d"], seed=args.seed,
+                          workers=min(16, os.cpu_count() or 1))
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    return to_dev(qb), to_dev(kb), to_dev(vb)
+
+
+def _time(fn, reps, warmup=1):
+    """Mean ms per call over reps calls (HIP events on the current stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_dense_sdpa(args):
+    """torch flash SDPA (no math fallback) at the workload's shape."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    from synth import CONFIGS
+    c = CONFIGS[args.workload]
+    q, k, v = _inputs(args, c)
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+        f = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)  # noqa: E731
+        ms = _time(f, args.reps)
+    print(json.dumps({"sdpa_ms": ms}), flush=True)
+
+
+def run_curve(args):
+    """Latency-density curve of the sparse path against dense attention."""
+    import subprocess
+    import numpy as np
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    from synth import CONFIGS
+
+    c = CONFIGS[args.workload]
+    T, Hg, Wg, H, d, kvb, C = c["T"], c["Hg"], c["Wg"], c["H"], c["d"], c["kv_block"], c["n_clusters"]
+    N = T * Hg * Wg
+    M, nqb = -(-N // kvb), -(-N // 128)
+    rows = np.minimum(128, N - 128 * np.arange(nqb))
+    log(f"[curve] generating {args.workload}: H={H} N={N}")
+    q, k, v = _inputs(args, c)
+    S = torch.empty((1, H, nqb, M), dtype=torch.float32, device=q.device)
+    sel_ms = _time(lambda: bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"], scores=S),
+                   args.reps)
+    points = []
+    for f in CURVE_DENSITIES:
+        s = c["budget"] if f is None else max(1, min(M, int(round(f * M))))
+        log(f"[curve] budget {s} of {M}")
+        idx = torch.empty((1, H, nqb, s), dtype=torch.int32, device=q.device)
+        bias = torch.empty((1, H, nqb, s), dtype=torch.float32, device=q.device)
+        cnt = torch.empty((1, H, nqb), dtype=torch.int32, device=q.device)
+        plan = lambda: bsa.bsa_sip_plan(S, s, bsa.PLAN_SIP, seed=args.seed, idx=idx, bias=bias,  # noqa: E731
+                                        count=cnt)
+        plan_ms = _time(plan, args.reps)
+        out = torch.empty_like(q)
+        attn_ms = _time(lambda: bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out),
+                        args.reps)
+        ch = cnt.cpu().numpy().astype(np.int64)
+        flops = 4.0 * d * float((ch[0] * kvb * rows[None, :]).sum())
+        points.append({"budget": s, "density": round(float(ch.sum()) / (H * nqb * M), 5),
+                       "plan_ms": round(plan_ms, 4), "attn_ms": round(attn_ms, 4),
+                       "step_ms": round(sel_ms + plan_ms + attn_ms, 4),
+                       "attn_tflops": round(flops / attn_ms / 1e9, 2)})
+        del idx, bias, cnt, out
+    dflops = 4.0 * d * N * N * H
+    didx, dcnt = bsa.dense_plan(1, H, N, N, 128, device=q.device)
+    dout = torch.empty_like(q)
+    dense_ms = _time(lambda: bsa.bsa_attn_fwd(q, k, v, didx, None, dcnt, 128, 128, out=dout),
+                     args.reps)
+    del q, k, v, S, didx, dout
+    torch.cuda.empty_cache()
+    log("[curve] torch flash SDPA in a child process")
+    sdpa_ms = None
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--dense-sdpa", "--workload",
+                            args.workload, "--seed", str(args.seed), "--reps", str(args.reps)],
+                           capture_output=True, text=True, timeout=600)
+        if r.returncode == 0:
+            sdpa_ms = json.loads(r.stdout.strip().splitlines()[-1])["sdpa_ms"]
+        else:
+            log(f"[curve] SDPA child failed (rc {r.returncode}): {r.stderr[-400:]}")
+    except Exception as e:  # noqa: BLE001
+        log(f"[curve] SDPA child failed: {e}")
+    for p in points:
+        p["r_vs_dense_bsa"] = round(p["attn_ms"] / dense_ms, 4)
+        if sdpa_ms:
+            p["r_vs_sdpa"] = round(p["attn_ms"] / sdpa_ms, 4)
+
+    def crossover(key, ref):
+        xs = [p["density"] for p in points]
+        ys = [p[key] - ref for p in points]
+        for i in range(1, len(xs)):
+            if ys[i - 1] < 0 <= ys[i]:
+                return round(xs[i - 1] + (xs[i] - xs[i - 1]) * -ys[i - 1] / (ys[i] - ys[i - 1]), 4)
+        return None if ys[0] >= 0 else 1.0
+    best = min(x for x in (dense_ms, sdpa_ms) if x)
+    rep = {
+        "report": "latency-density curve",
+        "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
+                    f"KV block {kvb}, SIP plans of the selector's scores",
+        "data": "synthetic", "seed": args.seed, "reps": args.reps,
+        "select_ms": round(sel_ms, 4),
+        "dense_bsa_ms": round(dense_ms, 4),
+        "dense_bsa_tflops": round(dflops / dense_ms / 1e9, 2),
+        "dense_sdpa_ms": round(sdpa_ms, 4) if sdpa_ms else None,
+        "dense_sdpa_tflops": round(dflops / sdpa_ms / 1e9, 2) if sdpa_ms else None,
+        "points": points,
+        "crossover_density_attn_vs_best_dense": crossover("attn_ms", best),
+        "crossover_density_step_vs_best_dense": crossover("step_ms", best),
+    }
+    print(json.dumps(rep), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +537,10 @@ def main():
         sys.exit(2)
     if args.accuracy:
         return run_accuracy(args)
+    if args.dense_sdpa:
+        return run_dense_sdpa(args)
+    if args.curve:
+        return run_curve(args)
     if args.workload.startswith("basa"):
         return run_basa(args)
     import numpy as np

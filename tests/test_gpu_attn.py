@@ -250,3 +250,44 @@ def test_attn_wan13b_head_full_size(env):
     ref, _ = oat.attn_fwd(q, k, v, 128, 4, idx, bias, cnt, blocks=blocks)
     rows = np.concatenate([np.arange(i * 128, min(q.shape[0], i * 128 + 128)) for i in blocks])
     g.assert_attn_close(O[0, 0][rows], ref[rows], "wan13b sampled blocks")
+
+
+@pytest.mark.parametrize("kind", ["dense_kv128", "sip_50pct_kv4"])
+def test_attn_high_density_full_size(env, kind):
+    """The ends of the latency-density curve at the Wan2.1-14B 720p shape
+    (one head, 75,600 tokens): the dense plan (every 128-token block, no
+    shift) against the oracle's dense attention, and SIP at half of the
+    18,900 4-token blocks (the oracle's scores through the device planner,
+    checked equal to the oracle's plan) against the oracle on its own plan;
+    sampled query blocks including the 80-row last one."""
+    bsa, g, torch = env
+    c = CONFIGS["wan14b_720p"]
+    g.say(f"case attn high density full size {kind}")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    N = q.shape[0]
+    blocks = [0, 1, 300, 590]
+    rows = np.concatenate([np.arange(i * 128, min(N, i * 128 + 128)) for i in blocks])
+    qd, kd, vd = g.to_dev_bf16(qb), g.to_dev_bf16(kb), g.to_dev_bf16(vb)
+    if kind == "dense_kv128":
+        idx, cnt = bsa.dense_plan(1, 1, N, N, 128)
+        out, _ = bsa.bsa_attn_fwd(qd, kd, vd, idx, None, cnt, 128, 128)
+        ref = np.full((N, q.shape[1]), np.nan)
+        ref[rows] = oat.dense_attn(q[rows], k, v)[0]
+    else:
+        s = 9450
+        S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, 4, 8, 1)
+        idx, bias, cnt, _ = bsa.bsa_sip_plan(g.dev_f32(S[None, None]), s, bsa.PLAN_SIP, seed=0)
+        wi, wb, wc, _ = opl.plan(S[blocks], s, opl.SIP,
+                                 offsets=[opl.sampling_offset(0, i) for i in blocks])
+        np.testing.assert_array_equal(idx[0, 0, blocks].cpu().numpy(), wi)
+        np.testing.assert_array_equal(cnt[0, 0, blocks].cpu().numpy(), wc)
+        out, _ = bsa.bsa_attn_fwd(qd, kd, vd, idx, bias, cnt, 128, 4)
+        fi = np.full((591, s), -1, np.int32)
+        fb = np.zeros((591, s), np.float32)
+        fc = np.zeros(591, np.int32)
+        fi[blocks], fb[blocks], fc[blocks] = wi, wb, wc
+        ref, _ = oat.attn_fwd(q, k, v, 128, 4, fi, fb, fc, blocks=blocks)
+    torch.cuda.synchronize()
+    got = g.from_dev_bf16(out)[0, 0]
+    g.assert_attn_close(got[rows], ref[rows], f"{kind} sampled blocks")
