@@ -17,7 +17,8 @@ __all__ = [
     "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
     "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-    "bsa_output_error", "dense_plan", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH",
+    "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "PLAN_SIP",
+    "PLAN_TOPK", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
@@ -56,6 +57,10 @@ lib.bsa_block_mass.restype = _i
 lib.bsa_block_mass.argtypes = [_p, _p, _p] + [_i] * 7 + [_f, _p, _p]
 lib.bsa_plan_coverage.restype = _i
 lib.bsa_plan_coverage.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p]
+lib.bsa_basa_offsets.restype = _i
+lib.bsa_basa_offsets.argtypes = [_i, _i, _pi]
+lib.bsa_basa_shifts.restype = _i
+lib.bsa_basa_shifts.argtypes = [_i, _i, _i, _i, _pi, _pi, _pi, _pi]
 lib.bsa_output_error.restype = _i
 lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 
@@ -63,7 +68,7 @@ lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bsa_select_scores",
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
            "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-           "bsa_output_error"]
+           "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts"]
 
 
 class BsaError(RuntimeError):
@@ -295,6 +300,27 @@ def bsa_output_error(out, ref, sums=None, stream=None):
     _check(lib.bsa_output_error(_ptr(out), _ptr(ref), B * H, N * d, _ptr(sums), _stream(stream)),
            "bsa_output_error")
     return sums
+
+
+def bsa_basa_offsets(w: int, L: int) -> list:
+    """The L per-layer window offsets along an axis of window size w."""
+    out = (ctypes.c_int * L)()
+    _check(lib.bsa_basa_offsets(w, L, out), "bsa_basa_offsets")
+    return list(out)
+
+
+def bsa_basa_shifts(wh: int, ww: int, L: int, S: int = 1, c_h=None, c_w=None):
+    """(dy, dx), each a list of L lists of S ints: Delta_{l,s} of layer l at
+    step s, with optional per-step offsets c_h, c_w (length S)."""
+    ch = None if c_h is None else (ctypes.c_int * S)(*[int(x) for x in c_h])
+    cw = None if c_w is None else (ctypes.c_int * S)(*[int(x) for x in c_w])
+    for c, n in ((c_h, "c_h"), (c_w, "c_w")):
+        if c is not None and len(c) != S:
+            raise ValueError(f"{n} must have S = {S} entries")
+    dy, dx = (ctypes.c_int * (L * S))(), (ctypes.c_int * (L * S))()
+    _check(lib.bsa_basa_shifts(wh, ww, L, S, ch, cw, dy, dx), "bsa_basa_shifts")
+    return ([list(dy[l * S:(l + 1) * S]) for l in range(L)],
+            [list(dx[l * S:(l + 1) * S]) for l in range(L)])
 
 
 def default_scale(d: int) -> float:

@@ -33,6 +33,8 @@ int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T
                             int Wg, int d, int wh, int ww, int dy, int dx, hipStream_t stream);
 uint64_t sampling_offset(uint64_t seed, uint64_t row);
 int mass_chunk_keys(int kv_block);
+void basa_offsets(int w, int L, int *b);
+void basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w, int *dy, int *dx);
 int launch_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
                       int d, int kv_block, float scale, float *mass, hipStream_t stream);
 int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *count, int rows,
@@ -227,6 +229,20 @@ int bsa_output_error(const void *out, const void *ref, int slabs, long long n, d
   if (!aligned(out, 16) || !aligned(ref, 16) || !aligned(sums, 8)) return BSA_ERR_ALIGN;
   if (slabs > 65535 * 16) return BSA_ERR_SIZE;
   return bsa::launch_output_error(out, ref, slabs, n, sums, (hipStream_t)stream);
+}
+
+int bsa_basa_offsets(int w, int L, int *offsets) {
+  if (!offsets || w < 1 || L < 1) return BSA_ERR_ARG;
+  bsa::basa_offsets(w, L, offsets);
+  return BSA_OK;
+}
+
+int bsa_basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w, int *dy,
+                    int *dx) {
+  if (!dy || !dx || wh < 1 || ww < 1 || L < 1 || S < 1) return BSA_ERR_ARG;
+  if ((long long)L * S > kMaxIndex) return BSA_ERR_SIZE;
+  bsa::basa_shifts(wh, ww, L, S, c_h, c_w, dy, dx);
+  return BSA_OK;
 }
 
 }  // extern "C"

@@ -457,4 +457,32 @@ int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T
   return status_of(hipGetLastError());
 }
 
+// Per-layer window offsets (BASA page, section "어떻게 동작하나"): candidates
+// a_i = (i delta) mod w with delta = max(1, floor(w / L)), laid out with the
+// first half and the second half alternating, so position l holds a_{l/2}
+// for even l and a_{K + (l-1)/2} for odd l, K = ceil(L / 2).
+static int offset_at(int w, int L, int l) {
+  const long long delta = w / L > 1 ? w / L : 1;
+  const long long i = (l & 1) ? (L + 1) / 2 + (l >> 1) : (l >> 1);
+  return (int)((i * delta) % w);
+}
+
+void basa_offsets(int w, int L, int *b) {
+  for (int l = 0; l < L; ++l) b[l] = offset_at(w, L, l);
+}
+
+// Delta_{l,s} = ((b^h_l + c^h_s) mod w_h, (b^w_l + c^w_s) mod w_w), for every
+// layer l < L and step s < S (row-major [L][S]); step offsets may be
+// negative or absent (zero).
+void basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w, int *dy, int *dx) {
+  auto mod = [](long long x, int m) { return (int)(((x % m) + m) % m); };
+  for (int l = 0; l < L; ++l) {
+    const int bh = offset_at(wh, L, l), bw = offset_at(ww, L, l);
+    for (int s = 0; s < S; ++s) {
+      dy[(size_t)l * S + s] = mod((long long)bh + (c_h ? c_h[s] : 0), wh);
+      dx[(size_t)l * S + s] = mod((long long)bw + (c_w ? c_w[s] : 0), ww);
+    }
+  }
+}
+
 }  // namespace bsa

@@ -21,7 +21,8 @@
  *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
  *                      structure of the BASA page (onedev.kr/papers/688,
  *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
- *                      into block lists for bsa_attn_fwd;
+ *                      into block lists for bsa_attn_fwd, and its per-layer
+ *                      shift schedule;
  *   bsa_block_mass,    accuracy diagnostics of a plan: the true attention
  *   bsa_plan_coverage, mass of every KV block, the mass a plan retains, and
  *   bsa_output_error   the output error against dense attention
@@ -231,6 +232,30 @@ int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int
 
 int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
                          int d, int wh, int ww, int dy, int dx, void *stream);
+
+/* ------------------------------------------------------------------------
+ * BASA shift schedule (BASA page, section "어떻게 동작하나": the window
+ * boundaries move from layer to layer and from denoising step to step).
+ * Host helpers, no GPU; every pointer here is a HOST pointer.
+ *
+ * bsa_basa_offsets: the L per-layer offsets along an axis of window size w.
+ *   Candidates a_i = (i * delta) mod w, delta = max(1, floor(w / L)),
+ *   i = 0..L-1; the first half (a_0 .. a_{K-1}, K = ceil(L / 2)) and the
+ *   second half alternate: offsets = (a_0, a_K, a_1, a_{K+1}, ...).  For
+ *   w = 8, L = 4: (0, 2, 4, 6) -> (0, 4, 2, 6).  offsets [L] int.
+ *
+ * bsa_basa_shifts: the roll of layer l at step s,
+ *   Delta_{l,s} = ((b^h_l + c^h_s) mod wh, (b^w_l + c^w_s) mod ww)
+ *   with b^h = bsa_basa_offsets(wh, L), b^w = bsa_basa_offsets(ww, L) and
+ *   caller-given per-step offsets c_h, c_w [S] (may be negative; NULL =
+ *   zero).  dy, dx [L, S] int, row-major; pass (dy[l*S + s], dx[l*S + s])
+ *   to bsa_basa_plan / bsa_window_unpermute of layer l at step s.
+ * Errors: BSA_ERR_ARG for null outputs or w, wh, ww, L, S < 1.
+ * --------------------------------------------------------------------- */
+int bsa_basa_offsets(int w, int L, int *offsets /* host out */);
+
+int bsa_basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w,
+                    int *dy, int *dx /* host out */);
 
 /* ------------------------------------------------------------------------
  * Accuracy diagnostics (AB-Attention page, onedev.kr/papers/1521: section

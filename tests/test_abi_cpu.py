@@ -153,3 +153,33 @@ def test_coverage_and_error_reject_invalid_arguments(bsa):
     assert L.bsa_output_error(FAKE, FAKE, 2, 12, FAKE, None) == -1
     assert L.bsa_output_error(FAKE, None, 2, 16, FAKE, None) == -1
     assert L.bsa_output_error(FAKE + 8, FAKE, 2, 16, FAKE, None) == -4
+
+
+def test_basa_shift_schedule_matches_oracle(bsa):
+    from oracle import basa as ob
+    assert bsa.bsa_basa_offsets(8, 4) == [0, 4, 2, 6]
+    rng = __import__("numpy").random.default_rng(3)
+    for w in (1, 2, 7, 8, 10, 15, 26, 32):
+        for L in (1, 2, 3, 4, 5, 12, 30, 40):
+            assert bsa.bsa_basa_offsets(w, L) == ob.shift_offsets(w, L), (w, L)
+    for wh, ww, L, S in ((10, 10, 4, 3), (15, 26, 30, 2), (5, 7, 6, 1)):
+        ch = rng.integers(-40, 40, S).tolist()
+        cw = rng.integers(-40, 40, S).tolist()
+        dy, dx = bsa.bsa_basa_shifts(wh, ww, L, S, ch, cw)
+        bh, bw = ob.shift_offsets(wh, L), ob.shift_offsets(ww, L)
+        for l in range(L):
+            for s in range(S):
+                assert (dy[l][s], dx[l][s]) == ob.layer_step_shift(bh, bw, ch, cw, l, s, wh, ww)
+        dy0, dx0 = bsa.bsa_basa_shifts(wh, ww, L, S)
+        assert all(dy0[l] == [bh[l]] * S and dx0[l] == [bw[l]] * S for l in range(L))
+
+
+def test_basa_shift_schedule_rejects_invalid_arguments(bsa):
+    L = bsa.lib
+    buf = (ctypes.c_int * 8)()
+    assert L.bsa_basa_offsets(0, 4, buf) == -1
+    assert L.bsa_basa_offsets(8, 0, buf) == -1
+    assert L.bsa_basa_offsets(8, 4, None) == -1
+    assert L.bsa_basa_shifts(10, 10, 2, 0, None, None, buf, buf) == -1
+    assert L.bsa_basa_shifts(10, 0, 2, 2, None, None, buf, buf) == -1
+    assert L.bsa_basa_shifts(10, 10, 2, 2, None, None, None, buf) == -1

@@ -19,6 +19,34 @@ def test_shift_schedule_worked_example(golden_dir):
     assert ob.shift_offsets(g["w"], g["L"]) == g["interleaved"]
 
 
+@pytest.mark.parametrize("w,L", [(8, 4), (10, 5), (10, 10), (26, 30), (15, 4), (1, 3), (7, 1)])
+def test_shift_schedule_properties(w, L):
+    """The interleave only reorders the candidates; even positions carry the
+    first half in order and odd positions the second half; with L <= w the
+    offsets are distinct multiples of delta; with L > w they cycle."""
+    delta = max(1, w // L)
+    cand = [(i * delta) % w for i in range(L)]
+    b = ob.shift_offsets(w, L)
+    K = -(-L // 2)
+    assert sorted(b) == sorted(cand) and len(b) == L
+    assert b[0::2] == cand[:K] and b[1::2] == cand[K:]
+    if L <= w:
+        assert len(set(b)) == L and all(x % delta == 0 for x in b)
+    else:
+        assert set(b) == set(range(w))
+
+
+def test_layer_step_shift():
+    bh, bw = ob.shift_offsets(10, 4), ob.shift_offsets(26, 4)
+    ch, cw = [0, 3, -4], [5, 0, 30]
+    for l in range(4):
+        assert ob.layer_step_shift(bh, bw, [0], [0], l, 0, 10, 26) == (bh[l], bw[l])
+        for s in range(3):
+            dy, dx = ob.layer_step_shift(bh, bw, ch, cw, l, s, 10, 26)
+            assert 0 <= dy < 10 and 0 <= dx < 26
+            assert (dy - bh[l] - ch[s]) % 10 == 0 and (dx - bw[l] - cw[s]) % 26 == 0
+
+
 def test_windows_partition_tokens():
     T, Hg, Wg = 3, 12, 14
     mem = ob.window_members(T, Hg, Wg, 5, 4, 3, 7)
