@@ -15,7 +15,9 @@ stream it runs on) and the CPU oracle on a bounded sample.
 With ``--workload basa_1664x960`` the step is instead the BASA-structured
 path at the 1664x960 / 81-frame latent (21 x 60 x 104, 12 heads, 10 x 10
 windows, 4 x 4 pooled memory, top-2 routing): bsa_basa_plan ->
-bsa_attn_fwd -> bsa_window_unpermute, reported the same way.
+bsa_attn_fwd -> bsa_window_unpermute, reported the same way
+(``basa_1664x960_p2``: 2 x 2 pooling; ``basa_1664x960_w15x26``: 15 x 26
+windows).
 
 With ``--accuracy`` it prints instead one JSON report of the accuracy
 diagnostics (block_sparse_attention_mean_amd.accuracy) on the first
@@ -305,7 +307,8 @@ def run_basa(args):
         "unpermute_ms": round(unp, 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": "bsa::attn_fwd_kernel<128, true, true>",
+            "kernel": f"bsa::attn_fwd_kernel<{d}, {str(kvb >= (4 if d == 128 else 8)).lower()}, "
+                      f"{str(kvb >= (4 if d == 128 else 8) and nk % (4 if d == 128 else 8) != 0).lower()}>",
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -314,6 +317,13 @@ def run_basa(args):
             "traffic": None,
         },
     }
+    # context, outside the timed step: dense attention of the same raster-order
+    # Q/K/V (this library over every 128-token block, no bias)
+    del qp, kp, vp, outp, idx, ws
+    didx, dcnt = bsa.dense_plan(1, H, N, N, 128, device=dev)
+    dense_ms = _time(lambda: bsa.bsa_attn_fwd(q, k, v, didx, None, dcnt, 128, 128, out=out), 2)
+    rec["dense_attn_ms"] = round(dense_ms, 4)
+    rec["speedup_vs_dense_attn"] = round(dense_ms / ms_step, 3)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         rec["cpu_baseline"] = basa_cpu_baseline(c, args.seed, 2)

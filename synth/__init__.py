@@ -43,6 +43,12 @@ CONFIGS = {
     # BASA-structured 1664x960 x 81 frames (latent 21x60x104)
     "basa_1664x960": dict(T=21, Hg=60, Wg=104, H=12, d=128, q_block=128, kv_block=4,
                           wh=10, ww=10, dy=3, dx=7, ph=4, pw=4, topk=2),
+    # the same with 2 x 2 pooling (more global tokens)
+    "basa_1664x960_p2": dict(T=21, Hg=60, Wg=104, H=12, d=128, q_block=128, kv_block=4,
+                             wh=10, ww=10, dy=3, dx=7, ph=2, pw=2, topk=2),
+    # the same with 15 x 26 windows (16 windows of 8,190 tokens: KV block 2)
+    "basa_1664x960_w15x26": dict(T=21, Hg=60, Wg=104, H=12, d=128, q_block=128, kv_block=2,
+                                 wh=15, ww=26, dy=3, dx=7, ph=4, pw=4, topk=2),
 }
 
 

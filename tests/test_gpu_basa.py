@@ -155,19 +155,30 @@ def _check_small(env, geo):
     assert got.shape == (1, H, N, d)
 
 
-def test_basa_full_size_sampled_windows(env):
-    """The 1664x960 / 81-frame latent (21 x 60 x 104), one head, w = (10, 10),
-    Delta = (3, 7), pooled 4 x 4, top-2: routes of every window exact, output
-    rows of sampled windows (full, ragged last column, last) against the
-    oracle."""
+FULL = {
+    # name: (windows sampled, windows, padded query rows)
+    "basa_1664x960": ([0, 10, 37, 65], 66, 135936),
+    "basa_1664x960_p2": ([0, 37, 65], 66, 135936),
+    "basa_1664x960_w15x26": ([0, 15], 16, 131072),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_basa_full_size_sampled_windows(env, name):
+    """The 1664x960 / 81-frame latent (21 x 60 x 104), one head, Delta =
+    (3, 7), top-2 routing: w = (10, 10) with 4 x 4 or 2 x 2 pooling, and
+    w = (15, 26) with 4 x 4 pooling (KV block 2).  Routes of every window
+    exact, output rows of sampled windows (full, ragged last column, last)
+    against the oracle."""
     bsa, g, torch = env
-    c = CONFIGS["basa_1664x960"]
+    c = CONFIGS[name]
+    wins, nwin, nq_pad = FULL[name]
     geo = dict(T=c["T"], Hg=c["Hg"], Wg=c["Wg"], wh=c["wh"], ww=c["ww"], dy=c["dy"], dx=c["dx"],
                ph=c["ph"], pw=c["pw"], topk=c["topk"], kvb=c["kv_block"])
-    g.say(f"case basa full size {geo}")
+    g.say(f"case basa full size {name} {geo}")
     qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=11)
     plan, out = _run_basa(env, qb, kb, vb, geo)
-    assert plan["nwin"] == 66 and plan["Nq_pad"] == 135936
+    assert plan["nwin"] == nwin and plan["Nq_pad"] == nq_pad
     cnt = plan["count"].cpu().numpy()
     assert cnt.max() <= plan["max_blocks"]
     members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
@@ -175,9 +186,37 @@ def test_basa_full_size_sampled_windows(env):
                               c["topk"])
     np.testing.assert_array_equal(plan["routes"].cpu().numpy()[0, 0], want_routes)
     got = g.from_dev_bf16(out)[0, 0]
-    wins = [0, 10, 37, 65]
     want, _ = obasa.basa_attn(qb[0, 0], kb[0, 0], vb[0, 0], c["T"], c["Hg"], c["Wg"], c["wh"],
                               c["ww"], c["dy"], c["dx"], c["ph"], c["pw"], c["topk"],
                               windows=wins, routes=want_routes)
     rows = np.concatenate([members[w] for w in wins])
-    g.assert_attn_close(got[rows], want[rows], "basa full size sampled windows")
+    g.assert_attn_close(got[rows], want[rows], f"basa {name} sampled windows")
+
+
+def test_basa_layer_schedule(env):
+    """Per-layer structured plans: four layers (each with its own
+    activations) at two denoising steps with step offsets, the roll of each
+    (layer, step) from bsa_basa_shifts (checked equal to the oracle's
+    schedule); each layer's plan, attention and un-permute against the
+    oracle at the oracle's own roll."""
+    bsa, g, torch = env
+    T, Hg, Wg, wh, ww, ph, pw, topk, kvb, d, L, S = 2, 12, 20, 4, 6, 5, 4, 2, 4, 64, 4, 2
+    ch, cw = [0, 1], [0, -2]
+    dy, dx = bsa.bsa_basa_shifts(wh, ww, L, S, ch, cw)
+    bh, bw = obasa.shift_offsets(wh, L), obasa.shift_offsets(ww, L)
+    for l in range(L):
+        for s in range(S):
+            oy, ox = obasa.layer_step_shift(bh, bw, ch, cw, l, s, wh, ww)
+            assert (dy[l][s], dx[l][s]) == (oy, ox)
+            g.say(f"case basa layer {l} step {s}: Delta = ({oy}, {ox})")
+            qb, kb, vb = make_qkv(T, Hg, Wg, 1, d, seed=100 + l)
+            geo = dict(T=T, Hg=Hg, Wg=Wg, wh=wh, ww=ww, dy=dy[l][s], dx=dx[l][s], ph=ph, pw=pw,
+                       topk=topk, kvb=kvb)
+            plan, out = _run_basa(env, qb, kb, vb, geo)
+            members = obasa.window_members(T, Hg, Wg, wh, ww, oy, ox)
+            routes = obasa.route(bf16_bits_to_f32(qb[0, 0]), bf16_bits_to_f32(kb[0, 0]), members,
+                                 topk)
+            np.testing.assert_array_equal(plan["routes"].cpu().numpy()[0, 0], routes)
+            want, _ = obasa.basa_attn(qb[0, 0], kb[0, 0], vb[0, 0], T, Hg, Wg, wh, ww, oy, ox,
+                                      ph, pw, topk, routes=routes)
+            g.assert_attn_close(g.from_dev_bf16(out)[0, 0], want, f"layer {l} step {s}")
