@@ -13,6 +13,11 @@ no online rescaling.
 Readings: scale 1/sqrt(d) unless given; no causal mask (full 3D attention of
 a video DiT); natural log; the shift applies to every token of the block;
 keys with index >= Nk (partial last block, padding) are left out.
+
+``attn_bwd`` is the gradient of the same definition (the page names a
+trainable version, with a backward pass, as future work in its closing
+paragraph): with the plan and its shifts held fixed, dQ, dK and dV of
+sum(dO * O), each listed occurrence of a block being its own set of keys.
 """
 from __future__ import annotations
 
@@ -68,3 +73,47 @@ def dense_attn(q, k, v, scale: float | None = None):
     e = np.exp(logits - m)
     den = e.sum(axis=1, keepdims=True)
     return (e @ v) / den, (m + np.log(den))[:, 0]
+
+
+def attn_bwd(q, k, v, dout, q_block: int, kv_block: int, idx, bias, count,
+             scale: float | None = None):
+    """Gradients of sum(dout * O) for O = attn_fwd(q, k, v, ...), fp64.
+
+    Per query block: gather the listed keys (an entry listed twice is two
+    sets of keys), P = softmax(scale q k^T + shift), O = P v, dP = dout v^T,
+    D = rowsum(dout * O), dS = P (dP - D); dQ = scale dS k, and dS^T q
+    (times scale) and P^T dout are added into dK and dV at the gathered
+    token rows.  Returns (dq (Nq, d), dk (Nk, d), dv (Nk, d)).
+    """
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nqb = -(-Nq // q_block)
+    dq = np.zeros((Nq, d))
+    dk = np.zeros((Nk, d))
+    dv = np.zeros((Nk, d))
+    M = -(-Nk // kv_block)
+    for i in range(nqb):
+        L = np.asarray(idx[i]).shape[0]
+        c = max(0, min(int(count[i]), L))
+        bl = np.asarray(idx[i][:c]).astype(np.int64)
+        b = np.zeros(c, np.float32) if bias is None else np.asarray(bias[i][:c])
+        ok = (bl >= 0) & (bl < M)
+        keys, kb = gather_keys(bl[ok], b[ok], kv_block, Nk)
+        if keys.size == 0:
+            continue
+        r0, r1 = i * q_block, min(Nq, (i + 1) * q_block)
+        qi, gi = q[r0:r1], dout[r0:r1]
+        logits = (qi @ k[keys].T) * scale + kb[None, :]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        P = e / e.sum(axis=1, keepdims=True)
+        O = P @ v[keys]
+        dP = gi @ v[keys].T
+        D = (gi * O).sum(axis=1, keepdims=True)
+        dS = P * (dP - D)
+        dq[r0:r1] = scale * (dS @ k[keys])
+        np.add.at(dk, keys, scale * (dS.T @ qi))
+        np.add.at(dv, keys, P.T @ gi)
+    return dq, dk, dv
