@@ -17,7 +17,8 @@ __all__ = [
     "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
     "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-    "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "PLAN_SIP",
+    "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
+    "PLAN_SIP",
     "PLAN_TOPK", "LIB_PATH",
 ]
 
@@ -57,6 +58,8 @@ lib.bsa_block_mass.restype = _i
 lib.bsa_block_mass.argtypes = [_p, _p, _p] + [_i] * 7 + [_f, _p, _p]
 lib.bsa_plan_coverage.restype = _i
 lib.bsa_plan_coverage.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p]
+lib.bsa_attn_bwd.restype = _i
+lib.bsa_attn_bwd.argtypes = [_p] * 6 + [_i] * 7 + [_p, _p, _p, _i, _f, _p, _p, _p, _p]
 lib.bsa_basa_offsets.restype = _i
 lib.bsa_basa_offsets.argtypes = [_i, _i, _pi]
 lib.bsa_basa_shifts.restype = _i
@@ -68,7 +71,7 @@ lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bsa_select_scores",
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
            "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-           "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts"]
+           "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd"]
 
 
 class BsaError(RuntimeError):
@@ -190,6 +193,33 @@ def bsa_attn_fwd(q, k, v, idx, bias, count, q_block=128, kv_block=4, softmax_sca
                             float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
            "bsa_attn_fwd")
     return out, lse
+
+
+def bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_block=4,
+                 softmax_scale=0.0, dq=None, dk=None, dv=None, stream=None):
+    """Gradients of sum(dout * out) for out = bsa_attn_fwd(q, k, v, idx, bias,
+    count, ...) with the plan fixed: (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]) fp32."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, torch.bfloat16, n, 4)
+    _need(lse, torch.float32, "lse", 3)
+    _need(idx, torch.int32, "idx", 4)
+    _need(count, torch.int32, "count", 3)
+    if bias is not None:
+        _need(bias, torch.float32, "bias", 4)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if dq is None:
+        dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    _check(lib.bsa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), B, H, Nq,
+                            Nk, d, q_block, kv_block, _ptr(idx), _ptr(bias), _ptr(count),
+                            idx.shape[-1], float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _stream(stream)), "bsa_attn_bwd")
+    return dq, dk, dv
 
 
 def bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block=4, B=1, H=1):

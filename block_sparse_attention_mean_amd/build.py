@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
-SOURCES = ["api.cpp", "attn_fwd.hip", "plan.hip", "select.hip", "basa.hip", "diag.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "plan.hip", "select.hip", "basa.hip",
+           "diag.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.

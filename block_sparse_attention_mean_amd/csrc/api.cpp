@@ -33,6 +33,10 @@ int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T
                             int Wg, int d, int wh, int ww, int dy, int dx, hipStream_t stream);
 uint64_t sampling_offset(uint64_t seed, uint64_t row);
 int mass_chunk_keys(int kv_block);
+int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                    const float *lse, int B, int H, int Nq, int Nk, int kv_block,
+                    const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
+                    float scale, float *dq, float *dk, float *dv, hipStream_t stream);
 void basa_offsets(int w, int L, int *b);
 void basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w, int *dy, int *dx);
 int launch_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
@@ -243,6 +247,28 @@ int bsa_basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w
   if ((long long)L * S > kMaxIndex) return BSA_ERR_SIZE;
   bsa::basa_shifts(wh, ww, L, S, c_h, c_w, dy, dx);
   return BSA_OK;
+}
+
+int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                 const float *lse, int B, int H, int Nq, int Nk, int d, int q_block, int kv_block,
+                 const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
+                 float softmax_scale, float *dq, float *dk, float *dv, void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !idx || !count || !dq || !dk || !dv)
+    return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
+  if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
+  if (d != 128 || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)))
+    return BSA_ERR_ALIGN;
+  const long long nqb = (Nq + 127) / 128;
+  if ((long long)B * H * nqb > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+  return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, kv_block, idx, bias, count,
+                              max_blocks, scale, dq, dk, dv, (hipStream_t)stream);
 }
 
 }  // extern "C"

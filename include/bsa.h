@@ -18,6 +18,7 @@
  *                      blocks into full tiles, shifts logits by -log pi,
  *                      and runs online softmax with P.V accumulation (same
  *                      page, section "전제와 한계", first paragraph);
+ *   bsa_attn_bwd       its gradients dQ, dK, dV with the plan held fixed;
  *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
  *                      structure of the BASA page (onedev.kr/papers/688,
  *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
@@ -182,6 +183,31 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
                  int d, int q_block, int kv_block, const int32_t *idx, const float *bias,
                  const int32_t *count, int max_blocks, float softmax_scale, void *out,
                  float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of bsa_attn_fwd (AB-Attention page: the fused pass of section
+ * "전제와 한계" with the shift of section "어떻게 쓰나"; the page's closing
+ * paragraph names a trainable version, with a backward pass, as future
+ * work).  With the plan and its shifts held fixed, the gradients of
+ * sum(dout * out) for every query n of query block i and every gathered key
+ * t (each listed occurrence of a block is its own set of keys):
+ *   P_nt = exp(scale q_n . k_t + bias - lse_n),   D_n = dout_n . out_n,
+ *   dS_nt = P_nt (dout_n . v_t - D_n),
+ *   dq_n  = scale sum_t dS_nt k_t,
+ *   dk_t += scale sum_n dS_nt q_n,   dv_t += sum_n P_nt dout_n.
+ * q, k, v, idx, bias, count, Nq, Nk, kv_block, max_blocks and
+ * softmax_scale are those of the forward call; out [B,H,Nq,d] bf16 and
+ * lse [B,H,Nq] fp32 are its outputs (P is recomputed from lse; a row with
+ * lse = -inf gets zero gradients); dout [B,H,Nq,d] bf16.
+ * dq [B,H,Nq,d], dk, dv [B,H,Nk,d] fp32 (16-byte aligned); dk and dv are
+ * zeroed by the call and accumulated with atomic adds, so their last bits
+ * may differ from run to run.  Only d = 128 is supported
+ * (BSA_ERR_UNSUPPORTED otherwise).
+ * --------------------------------------------------------------------- */
+int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                 const float *lse, int B, int H, int Nq, int Nk, int d, int q_block, int kv_block,
+                 const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
+                 float softmax_scale, float *dq, float *dk, float *dv, void *stream);
 
 /* ------------------------------------------------------------------------
  * BASA-structured lists (BASA page, onedev.kr/papers/688).

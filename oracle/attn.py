@@ -76,14 +76,16 @@ def dense_attn(q, k, v, scale: float | None = None):
 
 
 def attn_bwd(q, k, v, dout, q_block: int, kv_block: int, idx, bias, count,
-             scale: float | None = None):
+             scale: float | None = None, blocks=None):
     """Gradients of sum(dout * O) for O = attn_fwd(q, k, v, ...), fp64.
 
     Per query block: gather the listed keys (an entry listed twice is two
     sets of keys), P = softmax(scale q k^T + shift), O = P v, dP = dout v^T,
     D = rowsum(dout * O), dS = P (dP - D); dQ = scale dS k, and dS^T q
     (times scale) and P^T dout are added into dK and dV at the gathered
-    token rows.  Returns (dq (Nq, d), dk (Nk, d), dv (Nk, d)).
+    token rows.  Returns (dq (Nq, d), dk (Nk, d), dv (Nk, d)).  ``blocks``
+    limits the work to the listed query blocks: their dq rows, and dk / dv
+    rows complete for keys that no other query block lists.
     """
     Nq, d = q.shape
     Nk = k.shape[0]
@@ -94,7 +96,7 @@ def attn_bwd(q, k, v, dout, q_block: int, kv_block: int, idx, bias, count,
     dk = np.zeros((Nk, d))
     dv = np.zeros((Nk, d))
     M = -(-Nk // kv_block)
-    for i in range(nqb):
+    for i in (range(nqb) if blocks is None else blocks):
         L = np.asarray(idx[i]).shape[0]
         c = max(0, min(int(count[i]), L))
         bl = np.asarray(idx[i][:c]).astype(np.int64)

@@ -183,3 +183,22 @@ def test_basa_shift_schedule_rejects_invalid_arguments(bsa):
     assert L.bsa_basa_shifts(10, 10, 2, 0, None, None, buf, buf) == -1
     assert L.bsa_basa_shifts(10, 0, 2, 2, None, None, buf, buf) == -1
     assert L.bsa_basa_shifts(10, 10, 2, 2, None, None, None, buf) == -1
+
+
+def _bwd(bsa, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, Nq=300, Nk=300, d=128,
+             qb=128, kvb=4, idx=FAKE, bias=None, cnt=FAKE, L=8, scale=0.0, dq=FAKE, dk=FAKE,
+             dv=FAKE)
+    a.update(kw)
+    return bsa.lib.bsa_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["B"], a["H"],
+                                a["Nq"], a["Nk"], a["d"], a["qb"], a["kvb"], a["idx"], a["bias"],
+                                a["cnt"], a["L"], a["scale"], a["dq"], a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), -1), (dict(lse=None), -1), (dict(dk=None), -1), (dict(Nk=0), -1),
+    (dict(scale=float("nan")), -1), (dict(d=64), -2), (dict(kvb=3), -2), (dict(qb=64), -2),
+    (dict(dq=FAKE + 4), -4), (dict(do=FAKE + 8), -4), (dict(L=2**28, kvb=128), -7),
+])
+def test_attn_bwd_rejects_invalid_arguments(bsa, kw, status):
+    assert _bwd(bsa, **kw) == status
