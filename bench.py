@@ -37,6 +37,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload wan14b_720p|basa_1664x960]
        python bench.py --accuracy [--workload wan14b_720p] [--accuracy-heads 40]
        python bench.py --curve [--workload wan14b_720p]
+       python bench.py --backward [--workload wan14b_720p]
+
+With ``--backward`` it prints one JSON report of bsa_attn_bwd at the
+workload: the selector's SIP plan, one forward call for the output and its
+LSE, then the backward timed with HIP events (warmup + steps), against the
+algorithmic 10 d flops per (valid query, listed valid key) pair.
 """
 from __future__ import annotations
 
@@ -78,6 +84,8 @@ def parse():
     p.add_argument("--dense-sdpa", action="store_true",
                    help="(child of --curve) time torch's flash SDPA at the workload's shape")
     p.add_argument("--reps", type=int, default=3)
+    p.add_argument("--backward", action="store_true",
+                   help="print the backward-pass report instead of the benchmark line")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this size (counter calibration)")
     return p.parse_args()
@@ -422,7 +430,7 @@ def _inputs(args, c, H=None):
     return to_dev(qb), to_dev(kb), to_dev(vb)
 
 
-def _time(fn, reps, warmup=1):
+def _time(fn, reps, warmup=1):  # noqa: D401
     """Mean ms per call over reps calls (HIP events on the current stream)."""
     import torch
     for _ in range(warmup):
@@ -449,6 +457,55 @@ def run_dense_sdpa(args):
         f = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)  # noqa: E731
         ms = _time(f, args.reps)
     print(json.dumps({"sdpa_ms": ms}), flush=True)
+
+
+def run_backward(args):
+    """Backward of the sparse attention at the workload (see the module docstring)."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    from synth import CONFIGS
+
+    c = CONFIGS[args.workload]
+    T, Hg, Wg, H, d, kvb, C = c["T"], c["Hg"], c["Wg"], c["H"], c["d"], c["kv_block"], c["n_clusters"]
+    N, s = T * Hg * Wg, c["budget"]
+    nqb = -(-N // 128)
+    log(f"[backward] generating {args.workload}: H={H} N={N}")
+    q, k, v = _inputs(args, c)
+    g = torch.Generator(device="cpu").manual_seed(args.seed + 1)
+    dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(q.device)
+    S, _, _ = bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"])
+    idx, bias, cnt, _ = bsa.bsa_sip_plan(S, s, bsa.PLAN_SIP, seed=args.seed)
+    del S
+    out, lse = bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, want_lse=True)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    f = lambda: bsa.bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, cnt, 128, kvb,  # noqa: E731
+                                 dq=dq, dk=dk, dv=dv)
+    fwd_ms = _time(lambda: bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out),
+                   args.steps, args.warmup)
+    bwd_ms = _time(f, args.steps, args.warmup)
+    ch = cnt.cpu().numpy().astype(np.int64)
+    rows = np.minimum(128, N - 128 * np.arange(nqb))
+    pairs = float((ch[0] * kvb * rows[None, :]).sum())
+    for t in (dq, dk, dv):
+        if not torch.isfinite(t).all():
+            raise SystemExit("non-finite gradient")
+    tf = 10.0 * d * pairs / bwd_ms / 1e9
+    rep = {
+        "report": "backward",
+        "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
+                    f"KV block {kvb}, SIP budget {s}",
+        "data": "synthetic", "seed": args.seed, "steps": args.steps, "warmup": args.warmup,
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "bwd_over_fwd": round(bwd_ms / fwd_ms, 3),
+        "bwd_flop_per_call": 10.0 * d * pairs,
+        "roofline": {"kernel": "bsa_attn_bwd (zero + dq + dkdv kernels)", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+    }
+    print(json.dumps(rep), flush=True)
 
 
 def run_curve(args):
@@ -551,6 +608,8 @@ def main():
         return run_dense_sdpa(args)
     if args.curve:
         return run_curve(args)
+    if args.backward:
+        return run_backward(args)
     if args.workload.startswith("basa"):
         return run_basa(args)
     import numpy as np
