@@ -34,7 +34,7 @@ int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T
 uint64_t sampling_offset(uint64_t seed, uint64_t row);
 int mass_chunk_keys(int kv_block);
 int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                    const float *lse, int B, int H, int Nq, int Nk, int kv_block,
+                    const float *lse, int B, int H, int Nq, int Nk, int d, int kv_block,
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream);
 void basa_offsets(int w, int L, int *b);
@@ -257,7 +257,7 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
     return BSA_ERR_ARG;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
   if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
-  if (d != 128 || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)))
@@ -267,7 +267,7 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
   if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
   if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
-  return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, kv_block, idx, bias, count,
+  return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, d, kv_block, idx, bias, count,
                               max_blocks, scale, dq, dk, dv, (hipStream_t)stream);
 }
 

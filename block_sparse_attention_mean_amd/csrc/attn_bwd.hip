@@ -25,7 +25,7 @@
 //     transposing read.  Each key's rows are then added into fp32 dK and dV
 //     in global memory (atomic adds: a key is listed by many query blocks).
 // Outputs are fp32: dQ is written, dK and dV are zeroed by the entry point
-// first.  Only d = 128 is built.
+// first.  Head dims 64 and 128.
 #include <type_traits>
 
 #include "common.h"
@@ -37,18 +37,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int D = 128;
-constexpr int ROWB = D * 2;    // row bytes
-constexpr int NCH = D / 8;     // 16-byte chunks per row
-constexpr int DS = D / 16;     // k-steps over the head dim
-constexpr int DT = D / 32;     // 32-wide dim tiles
 constexpr int CAP = 512;       // list entries staged per phase
 
-// Chunk swizzle of a 256-byte row: 16 consecutive rows read at one chunk
-// hit 16 different chunks, and 4 consecutive rows (first one a multiple of
-// 4) read at 4 consecutive chunks (first one a multiple of 4) hit 16
-// different chunks -- the row-read and the transposing-read patterns.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Chunk swizzle of row r: 16 consecutive rows read at one chunk, and 4
+// consecutive rows (the first a multiple of 4) read at 4 consecutive chunks
+// (the first a multiple of 4), both hit 16 different 16-byte bank slots --
+// the row-read and the transposing-read patterns.  256-byte rows (d = 128)
+// fill the 64 banks; 128-byte rows (d = 64) pair up, so there bit 2 of the
+// chunk separates rows 2m and 2m + 2.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // MFMA A-row -> key within a 32-key tile, chosen so that accumulator
 // register r of lane half h holds key 16 (r >> 3) + 8 h + (r & 7): S^T's
@@ -62,11 +62,12 @@ __device__ __forceinline__ int key_of_row(int i) {
 // the four rows base + 0..3 (base depends only on the lane's half): lanes of
 // a 16-lane group read row base + (i >> 2) at columns 4 (i & 3) .. +3 of
 // their group's 16 columns.
+template <int D>
 __device__ __forceinline__ int tr_off(int base, int dt, int lane) {
   const int gi = lane & 15, gg = lane >> 4;
   const int r = base + (gi >> 2);
   const int n0 = dt * 32 + 16 * (gg & 1) + 4 * (gi & 3);
-  return r * ROWB + (((n0 >> 3) ^ swz(r)) << 4) + ((n0 >> 2) & 1) * 8;
+  return r * (D * 2) + (((n0 >> 3) ^ swz<D>(r)) << 4) + ((n0 >> 2) & 1) * 8;
 }
 
 template <int N>
@@ -86,14 +87,16 @@ __device__ __forceinline__ bf16x8 tr_pair(const unsigned char *base, int off0, i
   return as_bf16x8(w);
 }
 
-// fp32 sum of dO . O over this lane's 64 dims of its query row (the dims
-// of the B/A operand fragments: 16 ds + 8 hh + 0..7), plus the other half.
+// fp32 sum of dO . O over this lane's half of the dims of its query row
+// (the dims of the B/A operand fragments: 16 ds + 8 hh + 0..7), plus the
+// other half.
+template <int D>
 __device__ __forceinline__ float row_dot(const uint16_t *o_row, const uint16_t *do_row, int hh,
                                          bool valid) {
   float part = 0.f;
   if (valid) {
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
+    for (int ds = 0; ds < D / 16; ++ds) {
       const u32x4 x = ld16(o_row + ds * 16 + hh * 8), y = ld16(do_row + ds * 16 + hh * 8);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -150,7 +153,12 @@ __device__ __forceinline__ void stage_list(const BwdArgs &a, const int32_t *idx_
   }
 }
 
+template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;        // row bytes
+  constexpr int NCH = D / 8;         // 16-byte chunks per row
+  constexpr int DS = D / 16;         // k-steps over the head dim
+  constexpr int DT = D / 32;         // 32-wide dim tiles
   constexpr int NW = 4, KT = 32, NBUF = 3;
   constexpr int TILEB = KT * ROWB;
   constexpr int RPI = 64 / NCH;      // rows per 1 KB wave load
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     qf[ds] = as_bf16x8(x);
     df[ds] = as_bf16x8(y);
   }
-  const float Dq = row_dot(a.o + qoff, a.dout + qoff, hh, qok);
+  const float Dq = row_dot<D>(a.o + qoff, a.dout + qoff, hh, qok);
   float Lq = __builtin_inff();
   if (qok) {
     const float l = a.lse[(size_t)bh * a.Nq + qrow];
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int j = 0; j < LPW; ++j) {
     const int r = wave * RPW + j * RPI + lane / NCH;
     g_row[j] = r;
-    g_off[j] = ((lane % NCH) ^ swz(r)) << 4;
+    g_off[j] = ((lane % NCH) ^ swz<D>(r)) << 4;
   }
   auto kslot = [&](auto c) -> unsigned char * {
     constexpr int S = decltype(c)::value;
@@ -248,11 +256,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int krow = key_of_row(l32);
   int koff[DS], toff[DT][2];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) koff[ds] = krow * ROWB + (((2 * ds + hh) ^ swz(krow)) << 4);
+  for (int ds = 0; ds < DS; ++ds) koff[ds] = krow * ROWB + (((2 * ds + hh) ^ swz<D>(krow)) << 4);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) toff[dt][p] = tr_off(8 * hh + 4 * p, dt, lane);
+    for (int p = 0; p < 2; ++p) toff[dt][p] = tr_off<D>(8 * hh + 4 * p, dt, lane);
 
   auto compute = [&](auto slot_c) {
     constexpr int S = decltype(slot_c)::value;
@@ -342,7 +350,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+template <int D>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;        // row bytes
+  constexpr int NCH = D / 8;         // 16-byte chunks per row
+  constexpr int DS = D / 16;         // k-steps over the head dim
+  constexpr int DT = D / 32;         // 32-wide dim tiles
   constexpr int NW = 4;
   constexpr int KT = 128;            // gathered keys per pass (32 per wave)
   constexpr int QTB = 128 * ROWB;    // bytes of the Q (or dO) block
@@ -381,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
         x = ld16(qg + (size_t)r * D + ch * 8);
         y = ld16(dg + (size_t)r * D + ch * 8);
       }
-      const int off = r * ROWB + ((ch ^ swz(r)) << 4);
+      const int off = r * ROWB + ((ch ^ swz<D>(r)) << 4);
       st16(q_s + off, x);
       st16(do_s + off, y);
     }
@@ -389,9 +402,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int qr = tid >> 1, half = tid & 1;
     float part = 0.f;
     if (qr < nrow) {
-      const size_t off = ((size_t)bh * a.Nq + (size_t)qb * 128 + qr) * D + half * 64;
+      const size_t off = ((size_t)bh * a.Nq + (size_t)qb * 128 + qr) * D + half * (D / 2);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < D / 16; ++c) {
         const u32x4 x = ld16(a.o + off + c * 8), y = ld16(a.dout + off + c * 8);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -418,13 +431,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   // dim 32 dt + l32, queries 32 qs + 16 ks + 8 p + 4 hh + 0..3)
   int roff[DS], toff[DT][2][2];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hh) ^ swz(l32)) << 4);
+  for (int ds = 0; ds < DS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hh) ^ swz<D>(l32)) << 4);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) toff[dt][ks][p] = tr_off(16 * ks + 8 * p + 4 * hh, dt, lane);
+      for (int p = 0; p < 2; ++p) toff[dt][ks][p] = tr_off<D>(16 * ks + 8 * p + 4 * hh, dt, lane);
 
   const uint16_t *kbase = a.k + (size_t)bh * a.Nk * D;
   const uint16_t *vbase = a.v + (size_t)bh * a.Nk * D;
@@ -547,7 +560,7 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4 *p, size_t n4) {
 }  // namespace
 
 int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                    const float *lse, int B, int H, int Nq, int Nk, int kv_block,
+                    const float *lse, int B, int H, int Nq, int Nk, int d, int kv_block,
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream) {
   BwdArgs a;
@@ -573,12 +586,17 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
   a.scale_log2 = scale * kLog2e;
   const long long total = (long long)B * H * a.nqb;
   a.total_wg = (int)total;
-  const size_t n4 = (size_t)B * H * Nk * D / 4;
+  const size_t n4 = (size_t)B * H * Nk * d / 4;
   const unsigned zg = (unsigned)min((size_t)8192, (n4 + 255) / 256);
   hipLaunchKernelGGL(zero_kernel, dim3(zg), dim3(256), 0, stream, (f32x4 *)dk, n4);
   hipLaunchKernelGGL(zero_kernel, dim3(zg), dim3(256), 0, stream, (f32x4 *)dv, n4);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)total), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)total), dim3(256), 0, stream, a);
+  if (d == 128) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), dim3((unsigned)total), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), dim3((unsigned)total), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), dim3((unsigned)total), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), dim3((unsigned)total), dim3(256), 0, stream, a);
+  }
   return status_of(hipGetLastError());
 }
 

@@ -201,8 +201,7 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
  * lse = -inf gets zero gradients); dout [B,H,Nq,d] bf16.
  * dq [B,H,Nq,d], dk, dv [B,H,Nk,d] fp32 (16-byte aligned); dk and dv are
  * zeroed by the call and accumulated with atomic adds, so their last bits
- * may differ from run to run.  Only d = 128 is supported
- * (BSA_ERR_UNSUPPORTED otherwise).
+ * may differ from run to run.  d in {64, 128}.
  * --------------------------------------------------------------------- */
 int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
                  const float *lse, int B, int H, int Nq, int Nk, int d, int q_block, int kv_block,

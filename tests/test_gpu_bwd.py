@@ -75,24 +75,27 @@ def _run(env, q, k, v, dout, kvb, idx, bias, cnt):
     return dq.cpu().numpy()[0, 0], dk.cpu().numpy()[0, 0], dv.cpu().numpy()[0, 0]
 
 
-def _inputs(Nq, Nk, seed):
-    qb, _, _ = make_qkv(1, 1, Nq, 1, 128, seed=seed)
-    _, kb, vb = make_qkv(1, 1, Nk, 1, 128, seed=seed + 1)
-    db, _, _ = make_qkv(1, 1, Nq, 1, 128, seed=seed + 2)
+def _inputs(Nq, Nk, seed, d=128):
+    qb, _, _ = make_qkv(1, 1, Nq, 1, d, seed=seed)
+    _, kb, vb = make_qkv(1, 1, Nk, 1, d, seed=seed + 1)
+    db, _, _ = make_qkv(1, 1, Nq, 1, d, seed=seed + 2)
     return tuple(bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb, db))
 
 
-@pytest.mark.parametrize("Nq,Nk,kvb,s,mode", [
-    (300, 300, 4, 20, opl.SIP), (256, 256, 1, 60, opl.SIP), (512, 512, 16, 9, opl.TOPK),
-    (1000, 1000, 128, 3, opl.SIP), (384, 390, 8, 30, opl.SIP), (200, 700, 4, 50, opl.TOPK),
-    (130, 2048, 2, 600, opl.SIP),
+@pytest.mark.parametrize("Nq,Nk,kvb,s,mode,d", [
+    (300, 300, 4, 20, opl.SIP, 128), (256, 256, 1, 60, opl.SIP, 128),
+    (512, 512, 16, 9, opl.TOPK, 128), (1000, 1000, 128, 3, opl.SIP, 128),
+    (384, 390, 8, 30, opl.SIP, 128), (200, 700, 4, 50, opl.TOPK, 128),
+    (130, 2048, 2, 600, opl.SIP, 128),
+    (300, 300, 4, 20, opl.SIP, 64), (256, 260, 1, 70, opl.SIP, 64), (640, 2048, 64, 8, opl.TOPK, 64),
+    (130, 2048, 2, 600, opl.SIP, 64),
 ])
-def test_bwd_matches_oracle(env, Nq, Nk, kvb, s, mode):
+def test_bwd_matches_oracle(env, Nq, Nk, kvb, s, mode, d):
     """Ragged query and key counts (a partial last KV block), block sizes 1-128,
-    SIP shifts and top-k, lists longer than one staging phase."""
+    SIP shifts and top-k, lists longer than one staging phase, d = 64 and 128."""
     bsa, g, torch = env
-    g.say(f"case bwd Nq={Nq} Nk={Nk} kv={kvb} s={s} mode={mode}")
-    q, k, v, dout = _inputs(Nq, Nk, seed=Nq + kvb)
+    g.say(f"case bwd Nq={Nq} Nk={Nk} kv={kvb} s={s} mode={mode} d={d}")
+    q, k, v, dout = _inputs(Nq, Nk, seed=Nq + kvb, d=d)
     nqb, M = -(-Nq // 128), -(-Nk // kvb)
     idx, bias, cnt, _ = _plan(nqb, M, s, mode, seed=Nk)
     gq, gk, gv = _run(env, q, k, v, dout, kvb, idx, bias if mode == opl.SIP else None, cnt)
