@@ -111,6 +111,16 @@ def traffic_for_current_kernel():
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(c, seed, heads):
     """The oracle (as it stands) on whole heads 0..heads-1 of the workload:
     pooling, k-means, scores, SIP plan and attention of every query block.
@@ -154,7 +164,7 @@ def cpu_baseline(c, seed, heads):
                    f"scores, SIP plan and attention, fp64 numpy (k-means in its stated fp32 order)"),
         "seconds": round(total, 3),
         "stage_seconds": {k2: round(v2, 3) for k2, v2 in st.items()},
-        "host_cpus": os.cpu_count(),
+        "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
     }
 
 
@@ -199,7 +209,7 @@ def basa_cpu_baseline(c, seed, heads):
         "value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"heads 0..{heads - 1} of {c['name']}, all {len(members)} windows: routing and "
                    f"attention, fp64 numpy (routing in its stated fp32 order)"),
-        "seconds": round(sec, 3), "host_cpus": os.cpu_count(),
+        "seconds": round(sec, 3), "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
     }
 
 
@@ -710,6 +720,9 @@ def main():
             "step": "bsa_select_scores + bsa_sip_plan + bsa_attn_fwd",
         },
         "attn_ms_per_call": round(attn_ms, 4),
+        "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(att, [10, 50, 90])],
+        "step_ms_p10_p50_p90": [round(float(x), 4) for x in
+                                np.percentile([m[0].elapsed_time(m[3]) for m in marks], [10, 50, 90])],
         "attn_tflops": round(attn_tf, 2),
         "select_ms": round(float(np.mean(sel)), 4),
         "plan_ms": round(float(np.mean(pln)), 4),
@@ -725,6 +738,25 @@ def main():
             "gathered_bytes_per_launch": gathered,
         },
     }
+    # the page rebuilds the plan every 4 denoising steps and reuses it:
+    # one selector + plan and four attention calls, per attention call
+    def reuse4():
+        bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"], scores=scores, workspace=ws)
+        bsa.bsa_sip_plan(scores, s, bsa.PLAN_SIP, seed=args.seed, idx=idx, bias=bias, count=cnt)
+        for _ in range(4):
+            bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
+    rec["ms_per_step_plan_every_4"] = round(_time(reuse4, 3) / 4, 4)
+    # one cold call (outside the timed region): a 512 MB write evicts the
+    # Infinity Cache first
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush.fill_(3)
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    rec["attn_ms_cold"] = round(c0.elapsed_time(c1), 4)
+    del flush
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
