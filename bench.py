@@ -440,7 +440,7 @@ def _inputs(args, c, H=None):
     return to_dev(qb), to_dev(kb), to_dev(vb)
 
 
-def _time(fn, reps, warmup=1):  # noqa: D401
+def _time(fn, reps, warmup=1):
     """Mean ms per call over reps calls (HIP events on the current stream)."""
     import torch
     for _ in range(warmup):

@@ -231,7 +231,7 @@ int bsa_output_error(const void *out, const void *ref, int slabs, long long n, d
   if (!out || !ref || !sums) return BSA_ERR_ARG;
   if (slabs < 1 || n < 8 || n % 8 != 0) return BSA_ERR_ARG;
   if (!aligned(out, 16) || !aligned(ref, 16) || !aligned(sums, 8)) return BSA_ERR_ALIGN;
-  if (slabs > 65535 * 16) return BSA_ERR_SIZE;
+  if ((long long)slabs * n > kMaxIndex * 16) return BSA_ERR_SIZE;
   return bsa::launch_output_error(out, ref, slabs, n, sums, (hipStream_t)stream);
 }
 
@@ -258,6 +258,7 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
   if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
   if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  if (dk == dv || dq == dk || dq == dv) return BSA_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4) || !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)))

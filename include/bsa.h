@@ -199,9 +199,10 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
  * softmax_scale are those of the forward call; out [B,H,Nq,d] bf16 and
  * lse [B,H,Nq] fp32 are its outputs (P is recomputed from lse; a row with
  * lse = -inf gets zero gradients); dout [B,H,Nq,d] bf16.
- * dq [B,H,Nq,d], dk, dv [B,H,Nk,d] fp32 (16-byte aligned); dk and dv are
- * zeroed by the call and accumulated with atomic adds, so their last bits
- * may differ from run to run.  d in {64, 128}.
+ * dq [B,H,Nq,d], dk, dv [B,H,Nk,d] fp32 (16-byte aligned, three distinct
+ * buffers: BSA_ERR_ARG if two are the same); dk and dv are zeroed by the
+ * call and accumulated with atomic adds, so their last bits may differ from
+ * run to run.  d in {64, 128}.
  * --------------------------------------------------------------------- */
 int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
                  const float *lse, int B, int H, int Nq, int Nk, int d, int q_block, int kv_block,

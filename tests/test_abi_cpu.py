@@ -197,6 +197,7 @@ def _bwd(bsa, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), -1), (dict(lse=None), -1), (dict(dk=None), -1), (dict(Nk=0), -1),
+    (dict(dv=FAKE + 4096, dk=FAKE + 4096), -1),
     (dict(scale=float("nan")), -1), (dict(d=96), -2), (dict(kvb=3), -2), (dict(qb=64), -2),
     (dict(dq=FAKE + 4), -4), (dict(do=FAKE + 8), -4), (dict(L=2**28, kvb=128), -7),
 ])
