@@ -187,8 +187,8 @@ def test_basa_shift_schedule_rejects_invalid_arguments(bsa):
 
 def _bwd(bsa, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, Nq=300, Nk=300, d=128,
-             qb=128, kvb=4, idx=FAKE, bias=None, cnt=FAKE, L=8, scale=0.0, dq=FAKE, dk=FAKE,
-             dv=FAKE)
+             qb=128, kvb=4, idx=FAKE, bias=None, cnt=FAKE, L=8, scale=0.0, dq=FAKE,
+             dk=FAKE + 4096, dv=FAKE + 8192)
     a.update(kw)
     return bsa.lib.bsa_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["B"], a["H"],
                                 a["Nq"], a["Nk"], a["d"], a["qb"], a["kvb"], a["idx"], a["bias"],
@@ -197,7 +197,7 @@ def _bwd(bsa, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), -1), (dict(lse=None), -1), (dict(dk=None), -1), (dict(Nk=0), -1),
-    (dict(dv=FAKE + 4096, dk=FAKE + 4096), -1),
+    (dict(dv=FAKE + 4096), -1), (dict(dq=FAKE + 8192), -1),
     (dict(scale=float("nan")), -1), (dict(d=96), -2), (dict(kvb=3), -2), (dict(qb=64), -2),
     (dict(dq=FAKE + 4), -4), (dict(do=FAKE + 8), -4), (dict(L=2**28, kvb=128), -7),
 ])
