@@ -443,6 +443,21 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     qk(slot_c, sA);
     softmax_pv(slot_c, sA, t);
   };
+  // Steady state (tile t + 2 exists): the same step without conditions, and
+  // with the backend's hint to interleave LDS reads and matrix operations
+  // (1-2 % faster than the conditional step at the Wan2.1-14B 720p shape).
+  auto step_full = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    __builtin_amdgcn_iglp_opt(0);
+    constexpr int SN = (S + 2) % NBUF;
+    int row[LPW], nvr[LPW];
+    if (QUAD) rows_of(t + 2, row, nvr);
+    ring_barrier<LPT>();
+    if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
+    else issue(std::integral_constant<int, SN>(), t + 2);
+    qk(slot_c, sA);
+    softmax_pv(slot_c, sA, t);
+  };
 
   // A phase covers CAP list entries (per-key shifts) or CAPG 4-key groups
   // (group shifts).
@@ -498,7 +513,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     __syncthreads();
     if (ntiles > 0) issue_any(std::integral_constant<int, 0>(), 0);
     if (ntiles > 1) issue_any(std::integral_constant<int, 1>(), 1);
-    for (int t = 0; t < ntiles; t += 3) {
+    int t = 0;
+    for (; t + 4 < ntiles; t += 3) {
+      step_full(std::integral_constant<int, 0>(), t);
+      step_full(std::integral_constant<int, 1>(), t + 1);
+      step_full(std::integral_constant<int, 2>(), t + 2);
+    }
+    for (; t < ntiles; t += 3) {
       step(std::integral_constant<int, 0>(), t);
       if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
       if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
