@@ -9,16 +9,17 @@
 //     block, A_ij = mean over the block's queries n of
 //     sum_{t in block j} exp(scale q_n . k_t - lse_n), with lse the dense
 //     log-normaliser (the LSE output of a dense attention call).  One
-//     workgroup covers one 128-query block and a chunk of at most 1024 keys
+//     workgroup covers one 128-query block and a chunk of at most 3584 keys
 //     that starts on a KV-block boundary; wave w holds queries 32 w .. +32
 //     as the A operand of S = Q K^T (bf16 MFMA 32x32x16) and every wave
 //     reads the same 32-key K tiles from a three-slot LDS ring filled by
 //     direct global->LDS loads (16-byte-chunk XOR swizzle, bank-conflict
 //     free operand reads).  Each lane's accumulators hold one key of 16
 //     queries, so a key's column sum over the wave's 32 queries is 15
-//     in-lane adds and one swap with the other lane half.  Per-wave column
-//     sums of the chunk are kept in LDS and summed into blocks in a fixed
-//     order at the end, so the result is deterministic for any block size.
+//     in-lane adds and one swap with the other lane half.  The four waves'
+//     sums of a tile are added per key (in wave order) one step later, into
+//     the chunk's key sums in LDS, which are summed into blocks in key order
+//     at the end: deterministic for any block size.
 //   * plan_coverage: sum of A over the blocks a plan lists (fp64, list
 //     order).
 //   * output_error: sum (O - R)^2 and sum R^2 per head (fp64).
@@ -31,7 +32,7 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kMassChunk = 1024;  // keys per workgroup, at most
+constexpr int kMassChunk = 3584;  // keys per workgroup, at most (LDS under 40 KB: 4 workgroups per CU)
 
 // This wave's global->LDS loads older than the newest N vector-memory ops
 // and its LDS accesses are complete, then a workgroup barrier.
@@ -74,7 +75,8 @@ __global__ __launch_bounds__(256, 2) void block_mass_kernel(MassArgs a) {
   static_assert(LPW >= 1 && RPW % RPI == 0, "tile split");
 
   __shared__ __attribute__((aligned(16))) unsigned char k0[TILEB], k1[TILEB], k2[TILEB];
-  __shared__ float colsum[NW][kMassChunk];
+  __shared__ float colw[2][NW][KT];       // per-wave key sums of the last two tiles
+  __shared__ float keysum[kMassChunk];    // key sums of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,8 +166,14 @@ __global__ __launch_bounds__(256, 2) void block_mass_kernel(MassArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) col += __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -nl[r]));
     col += xor32(col);  // both halves add the same two values
+    if (hh == 0) colw[t & 1][wave][l32] = col;
+  };
+  // key sums of tile t (its four wave sums complete: called after a
+  // barrier that every wave passed after computing tile t)
+  auto fold = [&](int t) {
     const int key = t * KT + l32;
-    if (hh == 0 && key < nk) colsum[wave][key] = col;
+    if (wave == (t & 3) && hh == 0 && key < nk)
+      keysum[key] = ((colw[t & 1][0][l32] + colw[t & 1][1][l32]) + colw[t & 1][2][l32]) + colw[t & 1][3][l32];
   };
 
   auto step = [&](auto slot_c, int t) {
@@ -173,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void block_mass_kernel(MassArgs a) {
     if (t + 1 < ntiles) ring_wait_barrier<LPW>();
     else ring_wait_barrier<0>();
     if (t + 2 < ntiles) issue(std::integral_constant<int, (S + 2) % 3>(), t + 2);
+    if (t > 0) fold(t - 1);
     compute(slot_c, t);
   };
 
@@ -184,6 +193,8 @@ __global__ __launch_bounds__(256, 2) void block_mass_kernel(MassArgs a) {
     if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
   }
   __syncthreads();
+  if (ntiles > 0) fold(ntiles - 1);
+  __syncthreads();
 
   // Block sums in key order, each key's four wave sums in wave order; one
   // IEEE division by the query count.
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void block_mass_kernel(MassArgs a) {
   for (int b = tid; b < nb; b += NW * 64) {
     const int t0 = b * a.kv_block, t1 = min(nk, t0 + a.kv_block);
     float acc = 0.f;
-    for (int t = t0; t < t1; ++t) acc += ((colsum[0][t] + colsum[1][t]) + colsum[2][t]) + colsum[3][t];
+    for (int t = t0; t < t1; ++t) acc += keysum[t];
     orow[b] = acc / (float)nrow;
   }
 }

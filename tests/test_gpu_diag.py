@@ -38,7 +38,9 @@ def _check_mass(g, got, want, what):
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,d,kvb", [
-    (1, 2, 300, 2500, 128, 4),      # ragged query block; three key chunks, ragged last tile
+    (1, 2, 300, 2500, 128, 4),      # ragged query block, ragged last tile
+    (1, 1, 200, 9000, 128, 4),      # three key chunks
+    (1, 1, 130, 9000, 64, 3),       # three chunks (3582 keys each)
     (1, 2, 128, 1000, 64, 3),       # block size not a power of two
     (2, 1, 200, 777, 128, 128),
     (1, 2, 64, 20, 128, 1),         # fewer keys than one tile
