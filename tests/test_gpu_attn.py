@@ -291,3 +291,23 @@ def test_attn_high_density_full_size(env, kind):
     torch.cuda.synchronize()
     got = g.from_dev_bf16(out)[0, 0]
     g.assert_attn_close(got[rows], ref[rows], f"{kind} sampled blocks")
+
+
+def test_attn_hunyuan_head_full_size_topk(env):
+    """One head of the HunyuanVideo 720p shape (33 x 45 x 80 = 118,800 tokens,
+    KV block 4, budget 2272 of 29,700 blocks) with the oracle's top-k plan on
+    the oracle's scores; sampled query blocks including the 16-row last one."""
+    bsa, g, torch = env
+    c = CONFIGS["hunyuan_720p"]
+    g.say("case attn hunyuan one head full size top-k")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
+    S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, 4, 8, 1)
+    idx, bias, cnt, _ = opl.plan(S, c["budget"], opl.TOPK)
+    O, _ = _run(env, qb, kb, vb, 4, idx[None, None], None, cnt[None, None], want_lse=False)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    nqb = idx.shape[0]
+    assert nqb == 929 and q.shape[0] - 128 * (nqb - 1) == 16
+    blocks = [0, 464, nqb - 2, nqb - 1]
+    ref, _ = oat.attn_fwd(q, k, v, 128, 4, idx, None, cnt, blocks=blocks)
+    rows = np.concatenate([np.arange(i * 128, min(q.shape[0], i * 128 + 128)) for i in blocks])
+    g.assert_attn_close(O[0, 0][rows], ref[rows], "hunyuan top-k sampled blocks")
