@@ -133,7 +133,8 @@ def _valid_entries(idx_row, bias_row, c, M):
                                       (64, 5, 16)])
 def test_attn_group_shift_edges(env, d, Nk, kvb):
     """The group-shift path (every wave load inside one KV block): a row with
-    count 0, invalid indices (-1, M, 1000) among valid ones, entries past the
+    count 0, invalid indices (-1, M, 1000, and 2^30 + 1 and -2^31, whose key
+    row wraps around in 32-bit arithmetic) among valid ones, entries past the
     count, and the partial last block -- whole groups past Nk, and (Nk not a
     whole number of wave loads) a load and a 4-key group crossing Nk, down
     to Nk smaller than one load."""
@@ -142,11 +143,11 @@ def test_attn_group_shift_edges(env, d, Nk, kvb):
     qb, kb, vb = make_qkv(1, 1, 384, 1, d, seed=Nk + kvb)
     kb2, vb2 = kb[:, :, :Nk], vb[:, :, :Nk]
     M = -(-Nk // kvb)
-    idx = np.full((1, 1, 3, 12), M + 5, np.int32)
-    cnt = np.array([[[0, 12, 9]]], np.int32)
-    idx[0, 0, 1] = [0, 5 % M, -1, M - 1, M, 2, 3, 1000, 4 % M, 1, M - 2, 6 % M]
+    idx = np.full((1, 1, 3, 14), M + 5, np.int32)
+    cnt = np.array([[[0, 14, 9]]], np.int32)
+    idx[0, 0, 1] = [0, 5 % M, -1, M - 1, M, 2, 3, 1000, 4 % M, 1, M - 2, 6 % M, 2**30 + 1, -2**31]
     idx[0, 0, 2, :9] = [M - 1, M - 2, 0, 1, 2, 3, 4 % M, 5 % M, 6 % M]
-    bias = np.random.default_rng(1).random((1, 1, 3, 12)).astype(np.float32)
+    bias = np.random.default_rng(1).random((1, 1, 3, 14)).astype(np.float32)
     O, lse = _run(env, qb, kb2, vb2, kvb, idx, bias, cnt)
     q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb2, vb2))
     assert np.all(O[0, 0, :128] == 0) and np.all(np.isneginf(lse[0, 0, :128]))
