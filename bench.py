@@ -17,7 +17,11 @@ path at the 1664x960 / 81-frame latent (21 x 60 x 104, 12 heads, 10 x 10
 windows, 4 x 4 pooled memory, top-2 routing): bsa_basa_plan ->
 bsa_attn_fwd -> bsa_window_unpermute, reported the same way
 (``basa_1664x960_p2``: 2 x 2 pooling; ``basa_1664x960_w15x26``: 15 x 26
-windows).
+windows).  ``--workload wan13b_480p`` (Wan2.1-1.3B 480p, SIP budget 887),
+``hunyuan_720p`` (HunyuanVideo 720p, 118,800 tokens, SIP budget 2272) and
+``tiny_2x32x32`` (top-8 of 64-token blocks) time the same step as the
+headline at those shapes, under their own metric name and without a
+traffic figure (the counter runs cover the headline workload).
 
 With ``--accuracy`` it prints instead one JSON report of the accuracy
 diagnostics (block_sparse_attention_mean_amd.accuracy) on the first
@@ -34,7 +38,8 @@ and torch's flash SDPA timed in a child process), with the sparse/dense
 crossover.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload wan14b_720p|basa_1664x960]
+                       [--workload wan14b_720p|wan13b_480p|hunyuan_720p|tiny_2x32x32|
+                                   basa_1664x960|basa_1664x960_p2|basa_1664x960_w15x26]
        python bench.py --accuracy [--workload wan14b_720p] [--accuracy-heads 40]
        python bench.py --curve [--workload wan14b_720p]
        python bench.py --backward [--workload wan14b_720p]
@@ -111,6 +116,16 @@ def traffic_for_current_kernel():
     return rec.get("hbm_bytes_per_launch")
 
 
+def attn_kernel_name(d, kv_block, Nk):
+    """The attention instance a call launches: group shifts when every wave
+    load (4 rows at d = 128, 8 at d = 64) lies inside one KV block, with the
+    Nk-crossing checks when Nk is not a whole number of wave loads."""
+    rows = 4 if d == 128 else 8
+    quad = kv_block >= rows
+    part = quad and Nk % rows != 0
+    return f"bsa::attn_fwd_kernel<{d}, {str(quad).lower()}, {str(part).lower()}>"
+
+
 def host_cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -123,7 +138,8 @@ def host_cpu_model():
 
 def cpu_baseline(c, seed, heads):
     """The oracle (as it stands) on whole heads 0..heads-1 of the workload:
-    pooling, k-means, scores, SIP plan and attention of every query block.
+    pooling, k-means, scores, plan (SIP, or top-k where the workload says
+    so) and attention of every query block.
     Returns effective TFLOP/s (same definition as the GPU value)."""
     import numpy as np
     from oracle import attn as oat
@@ -148,7 +164,8 @@ def cpu_baseline(c, seed, heads):
         mu, w = osel.kmeans_head(q32, 128, c["n_clusters"], c["kmeans_iters"])
         S = osel.scores_from_centroids(mu, w, kbar)
         t1 = time.perf_counter()
-        idx, bias, cnt, _ = opl.plan(S, s, opl.SIP, seed=seed, row_base=h * nqb)
+        mode = opl.TOPK if c.get("mode") == "topk" else opl.SIP
+        idx, bias, cnt, _ = opl.plan(S, s, mode, seed=seed, row_base=h * nqb)
         t2 = time.perf_counter()
         oat.attn_fwd(q, k, v, 128, kvb, idx, bias, cnt)
         t3 = time.perf_counter()
@@ -161,7 +178,8 @@ def cpu_baseline(c, seed, heads):
         "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
         "sample": (f"heads 0..{heads - 1} of {c['name']} (all query blocks): pooling, k-means, "
-                   f"scores, SIP plan and attention, fp64 numpy (k-means in its stated fp32 order)"),
+                   f"scores, {'top-k' if c.get('mode') == 'topk' else 'SIP'} plan and attention, "
+                   f"fp64 numpy (k-means in its stated fp32 order)"),
         "seconds": round(total, 3),
         "stage_seconds": {k2: round(v2, 3) for k2, v2 in st.items()},
         "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
@@ -325,8 +343,7 @@ def run_basa(args):
         "unpermute_ms": round(unp, 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": f"bsa::attn_fwd_kernel<{d}, {str(kvb >= (4 if d == 128 else 8)).lower()}, "
-                      f"{str(kvb >= (4 if d == 128 else 8) and nk % (4 if d == 128 else 8) != 0).lower()}>",
+            "kernel": attn_kernel_name(d, kvb, nk),
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -650,6 +667,8 @@ def main():
     cnt = torch.empty((1, H, nqb), dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    mode = bsa.PLAN_TOPK if c.get("mode") == "topk" else bsa.PLAN_SIP
+    headline = args.workload == "wan14b_720p"
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -659,7 +678,7 @@ def main():
         bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"], scores=scores, workspace=ws)
         if marks is not None:
             marks[1].record(stream)
-        bsa.bsa_sip_plan(scores, s, bsa.PLAN_SIP, seed=args.seed, idx=idx, bias=bias, count=cnt)
+        bsa.bsa_sip_plan(scores, s, mode, seed=args.seed, idx=idx, bias=bias, count=cnt)
         if marks is not None:
             marks[2].record(stream)
         bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
@@ -696,10 +715,11 @@ def main():
     attn_ms = float(np.mean(att))
     attn_tf = flops / attn_ms / 1e9
     value = flops / ms_step / 1e9
-    traffic = traffic_for_current_kernel()
+    traffic = traffic_for_current_kernel() if headline else None
     gathered = float(cnt_h.sum() * kvb * d * 2 * 2)
     rec = {
-        "metric": "block-sparse attn ms/call + effective TFLOP/s at Wan-14B 720p shape, 89% sparse",
+        "metric": ("block-sparse attn ms/call + effective TFLOP/s at Wan-14B 720p shape, 89% sparse"
+                   if headline else f"block-sparse attn effective TFLOP/s, {args.workload}"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -714,7 +734,8 @@ def main():
         "config": {
             "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
                         f"query block 128, KV block {kvb}, {C} clusters / {c['kmeans_iters']} "
-                        f"k-means iteration, SIP budget {s} of {M} blocks",
+                        f"k-means iteration, {'top-k' if mode == bsa.PLAN_TOPK else 'SIP'} "
+                        f"budget {s} of {M} blocks",
             "B": 1, "H": H, "N": N, "d": d, "kv_block": kvb, "budget": s,
             "sparsity": round(1 - s / M, 5), "seed": args.seed,
             "step": "bsa_select_scores + bsa_sip_plan + bsa_attn_fwd",
@@ -728,7 +749,7 @@ def main():
         "plan_ms": round(float(np.mean(pln)), 4),
         "attn_flop_per_call": flops,
         "roofline": {
-            "kernel": "bsa::attn_fwd_kernel<128, true, false>",
+            "kernel": attn_kernel_name(d, kvb, N),
             "bound": "mfma",
             "achieved": round(attn_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -742,7 +763,7 @@ def main():
     # one selector + plan and four attention calls, per attention call
     def reuse4():
         bsa.bsa_select_scores(q, k, 128, kvb, C, c["kmeans_iters"], scores=scores, workspace=ws)
-        bsa.bsa_sip_plan(scores, s, bsa.PLAN_SIP, seed=args.seed, idx=idx, bias=bias, count=cnt)
+        bsa.bsa_sip_plan(scores, s, mode, seed=args.seed, idx=idx, bias=bias, count=cnt)
         for _ in range(4):
             bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
     rec["ms_per_step_plan_every_4"] = round(_time(reuse4, 3) / 4, 4)
@@ -767,7 +788,7 @@ def main():
         rec["copy_calib_bytes"] = n
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        rec["cpu_baseline"] = cpu_baseline(c, args.seed, args.cpu_sample_heads)
+        rec["cpu_baseline"] = cpu_baseline(c, args.seed, min(args.cpu_sample_heads, H))
     print(json.dumps(rec), flush=True)
 
 
