@@ -450,9 +450,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     qk(slot_c, sA);
     softmax_pv(slot_c, sA, t);
   };
-  // Steady state (tile t + 2 exists): the same step without conditions, and
-  // with the backend's hint to interleave LDS reads and matrix operations
-  // (1-2 % faster than the conditional step at the Wan2.1-14B 720p shape).
+  // Steady state of the group-shift path (tile t + 2 exists): the same step
+  // without conditions, and with the backend's hint to interleave LDS reads
+  // and matrix operations (1-2 % faster than the conditional step at the
+  // Wan2.1-14B 720p shape).
   auto step_full = [&](auto slot_c, int t) {
     constexpr int S = decltype(slot_c)::value;
     __builtin_amdgcn_iglp_opt(0);
@@ -521,7 +522,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     if (ntiles > 0) issue_any(std::integral_constant<int, 0>(), 0);
     if (ntiles > 1) issue_any(std::integral_constant<int, 1>(), 1);
     int t = 0;
-    for (; t + 4 < ntiles; t += 3) {
+    // the per-key path keeps the conditional step: unconditional steps (with or
+    // without the hint) made it 13 % slower at KV block 2
+    if constexpr (QUAD) for (; t + 4 < ntiles; t += 3) {
       step_full(std::integral_constant<int, 0>(), t);
       step_full(std::integral_constant<int, 1>(), t + 1);
       step_full(std::integral_constant<int, 2>(), t + 2);
