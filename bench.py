@@ -119,11 +119,15 @@ def traffic_for_current_kernel():
 def attn_kernel_name(d, kv_block, Nk):
     """The attention instance a call launches: group shifts when every wave
     load (4 rows at d = 128, 8 at d = 64) lies inside one KV block, with the
-    Nk-crossing checks when Nk is not a whole number of wave loads."""
+    Nk-crossing checks when Nk is not a whole number of wave loads; the
+    half-load variant when KV blocks are half a load and Nk a whole number
+    of blocks (below 4 GiB of rows)."""
     rows = 4 if d == 128 else 8
+    if 2 * kv_block == rows and Nk % kv_block == 0 and Nk * d * 2 <= 1 << 32:
+        return f"bsa::attn_fwd_kernel<{d}, true, false, true>"
     quad = kv_block >= rows
     part = quad and Nk % rows != 0
-    return f"bsa::attn_fwd_kernel<{d}, {str(quad).lower()}, {str(part).lower()}>"
+    return f"bsa::attn_fwd_kernel<{d}, {str(quad).lower()}, {str(part).lower()}, false>"
 
 
 def host_cpu_model():

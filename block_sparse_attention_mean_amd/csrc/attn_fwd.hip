@@ -38,7 +38,14 @@
 //     add per gather.  When Nk is not a whole number of loads, a separate
 //     instance also handles the load and the 4-key group crossing Nk: the
 //     load's lanes past Nk re-read its last valid row, and the tile's keys
-//     past Nk are masked before the exponentials.
+//     past Nk are masked before the exponentials;
+//   * half-load variant of that path, for KV blocks of half a wave load
+//     (2 tokens at d = 128, 4 at d = 64) and Nk a whole number of blocks:
+//     each 32-lane half of a load gathers one block (two scalar list loads
+//     per load, one lane select), and at d = 128 the shifts are staged per
+//     2-key group (8 per lane and tile, two 16-byte reads);
+//   * otherwise (smaller blocks, or a block crossing Nk) the per-key path:
+//     the phase's list staged in LDS and one shift per key.
 #include <type_traits>
 
 #include "common.h"
@@ -102,11 +109,20 @@ __device__ __forceinline__ int swz_v(int r) {
 __device__ __forceinline__ int quad_pos(int q) {
   return (q & 1) | (((q >> 2) & 1) << 1) | (((q >> 1) & 1) << 2);
 }
+// The same for 2-key groups p (0..15): [0-3 8-11 | 4-7 12-15], so that lane
+// half h finds its eight pairs in two 16-byte reads at 8 h.
+__device__ __forceinline__ int pair_pos(int p) {
+  return (((p >> 2) & 1) << 3) | ((p >> 3) << 2) | (p & 3);
+}
 
 // QUAD: group shifts and the scalar gather (KV blocks of at least one wave
 // load); PART: with them, loads and 4-key groups crossing Nk may occur (Nk
 // not a whole number of wave loads), so their rows past Nk are handled.
-template <int D, bool QUAD, bool PART>
+// HALF (with QUAD, without PART): KV blocks of exactly half a wave load
+// (2 tokens at d = 128, 4 at d = 64) and Nk a whole number of blocks; each
+// 32-lane half of a load gathers one block, and at d = 128 the shifts are
+// staged per 2-key group.
+template <int D, bool QUAD, bool PART, bool HALF = false>
 __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NW = 4;              // waves: one 32-query quarter each
   constexpr int KT = 32;             // keys per tile
@@ -121,7 +137,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   constexpr int DS = D / 16;         // k-steps of QK^T
   constexpr int DT = D / 32;         // dim tiles of O^T
   constexpr int CAP = 512;           // list entries staged per phase (per-key shifts)
-  constexpr int CAPG = 1024;         // 4-key groups staged per phase (group shifts)
+  constexpr int CAPG = 1024;         // key groups staged per phase (group shifts)
+  constexpr int SG = HALF && D == 128 ? 2 : 4;  // keys per group shift
+  static_assert(!HALF || (QUAD && !PART), "HALF is a mode of the group-shift path");
   static_assert(LPW >= 1 && RPW % RPI == 0, "tile too small for the gather split");
 
   // Ring of K/V tiles.  Separate arrays let the compiler see that a gather
@@ -198,7 +216,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
   for (int j = 0; j < LPW; ++j) {
     const int r = wave * RPW + j * RPI + lane / NCH;
     const int cl = lane % NCH;
-    const int rel = QUAD ? (lane / NCH) * ROWB : 0;
+    const int rel = QUAD ? ((lane / NCH) % (HALF ? RPI / 2 : RPI)) * ROWB : 0;
     g_row[j] = r;
     g_koff[j] = rel + ((cl ^ swz_k<D>(r)) << 4);
     g_voff[j] = rel + ((cl ^ swz_v<D>(r)) << 4);
@@ -267,6 +285,41 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     }
   };
 
+  // HALF: the two halves of wave load j gather one block each (entries
+  // e(pos) and e(pos + RPI / 2)); a block past the list or outside
+  // [0, Nk) reads row 0, its keys masked by the staged shifts.
+  auto rows_of_h = [&](int t, int (&row)[2 * LPW]) {
+    unsigned blk[2 * LPW];
+#pragma unroll
+    for (int i = 0; i < 2 * LPW; ++i) {  // all loads first (one wait)
+      const unsigned pos = (unsigned)(t * KT + wave * RPW + (i >> 1) * RPI + (i & 1) * (RPI / 2));
+      const unsigned ec = min(pos >> a.kv_shift, (unsigned)pcnt - 1u);
+      const unsigned byte = 4u * ((unsigned)pbase + ec);
+      blk[i] = (unsigned)*(cint_t *)((const __attribute__((address_space(4))) char *)idx_row + byte);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * LPW; ++i) {
+      const unsigned kk = blk[i] << a.kv_shift;
+      row[i] = kk < (unsigned)a.Nk ? (int)kk : 0;
+    }
+  };
+  auto issue_rows_h = [&](auto slot_c, const int (&row)[2 * LPW]) {
+    unsigned char *kt = kslot(slot_c);
+    unsigned char *vt = vslot(slot_c);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      // scalar base at the lower of the two rows, 32-bit lane offsets (the
+      // launch keeps Nk rows below 4 GiB)
+      const unsigned r0 = (unsigned)row[2 * j], r1 = (unsigned)row[2 * j + 1];
+      const unsigned rmin = min(r0, r1);
+      const unsigned dl = ((hh ? r1 : r0) - rmin) * (unsigned)ROWB;
+      const size_t src = (size_t)rmin * ROWB;
+      const int dst = (wave * RPW + j * RPI) * ROWB;
+      __builtin_amdgcn_global_load_lds((const void *)(kbase + src + (dl + (unsigned)g_koff[j])), (lds_void *)(kt + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vbase + src + (dl + (unsigned)g_voff[j])), (lds_void *)(vt + dst), 16, 0, 0);
+    }
+  };
+
   // Per-key shifts: gather tile t into slot S; this wave loads rows
   // [RPW w, RPW w + RPW).  Masked keys (invalid or padded list entries, rows
   // past Nk) load row 0 and get a -inf shift.
@@ -288,7 +341,11 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     }
   };
   auto issue_any = [&](auto slot_c, int t) {
-    if constexpr (QUAD) {
+    if constexpr (HALF) {
+      int row[2 * LPW];
+      rows_of_h(t, row);
+      issue_rows_h(slot_c, row);
+    } else if constexpr (QUAD) {
       int row[LPW], nvr[LPW];
       rows_of(t, row, nvr);
       issue_rows(slot_c, row, nvr);
@@ -343,7 +400,16 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     // lane halves (different keys of the same query) then agree on the new
     // reference through one exchange.
     const float *bt = bring + S * KT;
-    if (QUAD) {
+    if constexpr (QUAD && SG == 2) {
+      // pairs (m, half, i) at 8 half + 4 m + i: register r holds pair r / 2
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f32x4 bq = *(const f32x4 *)&gb_s[t * (KT / 2) + 8 * hh + 4 * m];
+#pragma unroll
+        for (int r = 8 * m; r < 8 * m + 8; ++r)
+          sacc[r] = __builtin_fmaf(sacc[r], a.scale_log2, bq[(r >> 1) & 3] - m_run);
+      }
+    } else if (QUAD) {
       // groups (m, half): (0,0) (0,1) (1,0) (1,1)
       const f32x4 bq = *(const f32x4 *)&gb_s[t * (KT / 4) + 4 * hh];
       f32x4 bm;
@@ -439,12 +505,14 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     constexpr int S = decltype(slot_c)::value;
     constexpr int SN = (S + 2) % NBUF;
     const bool more = t + 2 < ntiles;
-    int row[LPW], nvr[LPW];
-    if (QUAD && more) rows_of(t + 2, row, nvr);
+    int row[LPW], nvr[LPW], hrow[2 * LPW];
+    if (HALF && more) rows_of_h(t + 2, hrow);
+    else if (QUAD && more) rows_of(t + 2, row, nvr);
     if (t + 1 < ntiles) ring_barrier<LPT>();
     else ring_barrier<0>();
     if (more) {
-      if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
+      if constexpr (HALF) issue_rows_h(std::integral_constant<int, SN>(), hrow);
+      else if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
       else issue(std::integral_constant<int, SN>(), t + 2);
     }
     qk(slot_c, sA);
@@ -458,10 +526,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     constexpr int S = decltype(slot_c)::value;
     __builtin_amdgcn_iglp_opt(0);
     constexpr int SN = (S + 2) % NBUF;
-    int row[LPW], nvr[LPW];
-    if (QUAD) rows_of(t + 2, row, nvr);
+    int row[LPW], nvr[LPW], hrow[2 * LPW];
+    if (HALF) rows_of_h(t + 2, hrow);
+    else if (QUAD) rows_of(t + 2, row, nvr);
     ring_barrier<LPT>();
-    if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
+    if constexpr (HALF) issue_rows_h(std::integral_constant<int, SN>(), hrow);
+    else if constexpr (QUAD) issue_rows(std::integral_constant<int, SN>(), row, nvr);
     else issue(std::integral_constant<int, SN>(), t + 2);
     qk(slot_c, sA);
     softmax_pv(slot_c, sA, t);
@@ -469,7 +539,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
 
   // A phase covers CAP list entries (per-key shifts) or CAPG 4-key groups
   // (group shifts).
-  const int per_phase = QUAD ? (CAPG * 4) >> a.kv_shift : CAP;
+  const int per_phase = QUAD ? (CAPG * SG) >> a.kv_shift : CAP;
   for (int base = 0; base < cnt; base += per_phase) {
     const int pc = min(per_phase, cnt - base);
     pbase = base;
@@ -478,21 +548,21 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     ntiles = (nkeys + KT - 1) / KT;
     __syncthreads();
     if constexpr (QUAD) {
-      // shift of every 4-key group of the phase's tiles, -inf for groups of
+      // shift of every SG-key group of the phase's tiles, -inf for groups of
       // padded or invalid entries and wholly past Nk; a group crossing Nk
       // marks its rows past Nk
       if (PART) {
         for (int i = tid; i < ntiles; i += NW * 64) pmask_s[i] = 0u;
         __syncthreads();
       }
-      const int ng = ntiles * (KT / 4);
+      const int ng = ntiles * (KT / SG);
       for (int g = tid; g < ng; g += NW * 64) {
-        const int e = (4 * g) >> a.kv_shift;
+        const int e = (SG * g) >> a.kv_shift;
         float bv = -__builtin_inff();
         if (e < pc) {
           const int blk = idx_row[base + e];
           if (blk >= 0 && blk < a.M) {
-            const int k0 = (blk << a.kv_shift) + ((4 * g) & (kvb - 1));
+            const int k0 = (blk << a.kv_shift) + ((SG * g) & (kvb - 1));
             if (k0 < a.Nk) {
               bv = bias_row ? bias_row[base + e] * kLog2e : 0.f;
               if (PART && k0 + 4 > a.Nk) {
@@ -502,7 +572,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
             }
           }
         }
-        gb_s[(g & ~7) | quad_pos(g & 7)] = bv;
+        gb_s[SG == 4 ? (g & ~7) | quad_pos(g & 7) : (g & ~15) | pair_pos(g & 15)] = bv;
       }
     } else {
       // entries covering whole tiles (list tail padded with masked entries)
@@ -584,12 +654,18 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
   const int rows_per_load = d == 128 ? 4 : 8;
   const bool quad = kv_block >= rows_per_load;
   const bool part = quad && Nk % rows_per_load != 0;
+  // blocks of half a load: each half gathers one block; Nk must be a whole
+  // number of blocks (a block crossing Nk takes the per-key path)
+  const bool half = 2 * kv_block == rows_per_load && Nk % kv_block == 0 &&
+                    (long long)Nk * d * 2 <= (1ll << 32);
   if (d == 128) {
-    if (part) hipLaunchKernelGGL((attn_fwd_kernel<128, true, true>), grid, block, 0, stream, a);
+    if (half) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false, true>), grid, block, 0, stream, a);
+    else if (part) hipLaunchKernelGGL((attn_fwd_kernel<128, true, true>), grid, block, 0, stream, a);
     else if (quad) hipLaunchKernelGGL((attn_fwd_kernel<128, true, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<128, false, false>), grid, block, 0, stream, a);
   } else {
-    if (part) hipLaunchKernelGGL((attn_fwd_kernel<64, true, true>), grid, block, 0, stream, a);
+    if (half) hipLaunchKernelGGL((attn_fwd_kernel<64, true, false, true>), grid, block, 0, stream, a);
+    else if (part) hipLaunchKernelGGL((attn_fwd_kernel<64, true, true>), grid, block, 0, stream, a);
     else if (quad) hipLaunchKernelGGL((attn_fwd_kernel<64, true, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<64, false, false>), grid, block, 0, stream, a);
   }

@@ -26,11 +26,15 @@ def test_more_than_one_gpu_is_refused():
 def test_kernel_instance_names():
     sys.path.insert(0, ROOT)
     import bench
-    assert bench.attn_kernel_name(128, 4, 75600) == "bsa::attn_fwd_kernel<128, true, false>"
-    assert bench.attn_kernel_name(128, 4, 144126) == "bsa::attn_fwd_kernel<128, true, true>"
-    assert bench.attn_kernel_name(128, 2, 144126) == "bsa::attn_fwd_kernel<128, false, false>"
-    assert bench.attn_kernel_name(64, 8, 2048) == "bsa::attn_fwd_kernel<64, true, false>"
-    assert bench.attn_kernel_name(64, 4, 2048) == "bsa::attn_fwd_kernel<64, false, false>"
+    assert bench.attn_kernel_name(128, 4, 75600) == "bsa::attn_fwd_kernel<128, true, false, false>"
+    assert bench.attn_kernel_name(128, 4, 144126) == "bsa::attn_fwd_kernel<128, true, true, false>"
+    assert bench.attn_kernel_name(128, 2, 139262) == "bsa::attn_fwd_kernel<128, true, false, true>"
+    assert bench.attn_kernel_name(128, 2, 139263) == "bsa::attn_fwd_kernel<128, false, false, false>"
+    assert bench.attn_kernel_name(128, 1, 139262) == "bsa::attn_fwd_kernel<128, false, false, false>"
+    assert bench.attn_kernel_name(64, 8, 2048) == "bsa::attn_fwd_kernel<64, true, false, false>"
+    assert bench.attn_kernel_name(64, 4, 2048) == "bsa::attn_fwd_kernel<64, true, false, true>"
+    assert bench.attn_kernel_name(64, 4, 2046) == "bsa::attn_fwd_kernel<64, false, false, false>"
+    assert bench.attn_kernel_name(64, 2, 2048) == "bsa::attn_fwd_kernel<64, false, false, false>"
 
 
 @pytest.mark.gpu

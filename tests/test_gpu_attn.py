@@ -128,7 +128,9 @@ def _valid_entries(idx_row, bias_row, c, M):
     return bl[keep], b[keep]
 
 
-@pytest.mark.parametrize("d,Nk,kvb", [(128, 132, 8), (128, 260, 4), (64, 136, 16),
+@pytest.mark.parametrize("d,Nk,kvb", [(128, 260, 2), (128, 130, 2), (128, 6, 2), (128, 131, 2),
+                                      (64, 136, 4), (64, 132, 4), (64, 4, 4),
+                                      (128, 132, 8), (128, 260, 4), (64, 136, 16),
                                       (128, 130, 4), (128, 263, 8), (128, 3, 4), (64, 131, 8),
                                       (64, 5, 16)])
 def test_attn_group_shift_edges(env, d, Nk, kvb):
@@ -137,7 +139,10 @@ def test_attn_group_shift_edges(env, d, Nk, kvb):
     row wraps around in 32-bit arithmetic) among valid ones, entries past the
     count, and the partial last block -- whole groups past Nk, and (Nk not a
     whole number of wave loads) a load and a 4-key group crossing Nk, down
-    to Nk smaller than one load."""
+    to Nk smaller than one load.  KV blocks of half a wave load (2 tokens at
+    d = 128, 4 at d = 64) take the half-load variant of the path when Nk is
+    a whole number of blocks (Nk = 131 at 2-token blocks takes the per-key
+    path)."""
     bsa, g, torch = env
     g.say(f"case attn group-shift edges d={d} Nk={Nk} kv_block={kvb}")
     qb, kb, vb = make_qkv(1, 1, 384, 1, d, seed=Nk + kvb)
@@ -182,6 +187,30 @@ def test_attn_multi_phase_lists(env):
         ref, _ = oat.attn_fwd(q, k, v, 128, 4, i_, b_, c_, blocks=blocks)
         rows = np.concatenate([np.arange(i * 128, min(N, i * 128 + 128)) for i in blocks])
         g.assert_attn_close(O[0, 0][rows], ref[rows], f"N={N} sampled blocks")
+
+
+@pytest.mark.parametrize("d,kvb,N", [(128, 2, 12000), (128, 2, 11999), (64, 4, 12000)])
+def test_attn_multi_phase_half_loads(env, d, kvb, N):
+    """KV blocks of half a wave load with lists longer than one staging phase
+    (1,024 entries): exactly one phase, one entry more, a ragged third phase
+    and a short list; N = 11,999 (a partial last block) takes the per-key
+    path instead."""
+    bsa, g, torch = env
+    g.say(f"case attn multi-phase half loads N={N} d={d} kv_block={kvb}")
+    qb, kb, vb = make_qkv(1, 1, N, 1, d, seed=N + d)
+    M = -(-N // kvb)
+    nqb = -(-N // 128)
+    s = 3000
+    i_, b_, c_, _ = _random_plan(nqb, M, s, opl.SIP, seed=N + kvb)
+    c_ = c_.copy()
+    c_[0], c_[1], c_[2], c_[3] = 1024, 1025, 2500, 511
+    O, _ = _run(env, qb, kb, vb, kvb, i_[None, None], b_[None, None], c_[None, None],
+                want_lse=False)
+    q, k, v = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb))
+    blocks = [0, 1, 2, 3, 40, nqb - 1]
+    ref, _ = oat.attn_fwd(q, k, v, 128, kvb, i_, b_, c_, blocks=blocks)
+    rows = np.concatenate([np.arange(i * 128, min(N, i * 128 + 128)) for i in blocks])
+    g.assert_attn_close(O[0, 0][rows], ref[rows], f"N={N} d={d} kv={kvb} sampled blocks")
 
 
 def test_attn_fuzz_geometries(env):
