@@ -55,6 +55,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -97,10 +98,13 @@ def parse():
 
 
 def attn_build_sha():
-    """Hash of the attention kernel's source and its per-file build flags:
-    what the committed counter runs must have been taken on."""
+    """Hash of the attention kernel's code (its source without comments and
+    blank lines) and its per-file build flags: what the committed counter
+    runs must have been taken on."""
     from block_sparse_attention_mean_amd.build import FILE_FLAGS
-    h = hashlib.sha256(open(ATTN_SRC, "rb").read())
+    code = re.sub(r"//[^\n]*", "", open(ATTN_SRC).read())
+    code = "\n".join(ln.rstrip() for ln in code.splitlines() if ln.strip())
+    h = hashlib.sha256(code.encode())
     h.update(" ".join(FILE_FLAGS.get("attn_fwd.hip", [])).encode())
     return h.hexdigest()
 

@@ -537,8 +537,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnArgs a) {
     softmax_pv(slot_c, sA, t);
   };
 
-  // A phase covers CAP list entries (per-key shifts) or CAPG 4-key groups
-  // (group shifts).
+  // A phase covers CAP list entries (per-key shifts) or CAPG groups of SG
+  // keys (group shifts).
   const int per_phase = QUAD ? (CAPG * SG) >> a.kv_shift : CAP;
   for (int base = 0; base < cnt; base += per_phase) {
     const int pc = min(per_phase, cnt - base);
