@@ -64,3 +64,18 @@ def test_bench_line_on_the_tiny_workload():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cpu, key
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["unit"] == rec["unit"]
+
+
+def test_traffic_record_keyed_on_code(tmp_path, monkeypatch):
+    """The committed counter runs stay valid across comment edits of the
+    attention source and are dropped by any code change."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(bench.ATTN_SRC).read()
+    base = bench.attn_build_sha()
+    p = tmp_path / "attn_fwd.hip"
+    monkeypatch.setattr(bench, "ATTN_SRC", str(p))
+    p.write_text(src.replace("// ", "// (reworded) ", 3) + "\n// a trailing note\n\n")
+    assert bench.attn_build_sha() == base
+    p.write_text(src.replace("constexpr int NBUF = 3;", "constexpr int NBUF = 4;"))
+    assert bench.attn_build_sha() != base
