@@ -144,11 +144,13 @@ __global__ __launch_bounds__(256) void pool_split_kernel(SelArgs a) {
 // One workgroup per query block.  Member sums follow the stated order
 // exactly: a stable counting sort lists each cluster's rows in ascending
 // order, and one thread per (dim, cluster) adds them in that order.
-template <int D>
+// CMAX bounds the cluster count: with CMAX = 8 the workgroup's LDS stays
+// under 40 KB, so four workgroups share a CU instead of three.
+template <int D, int CMAX>
 __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
   constexpr int QS = D + 8;  // padded bf16 row stride (16-byte aligned rows)
   __shared__ __attribute__((aligned(16))) uint16_t qb16[128 * QS];
-  __shared__ __attribute__((aligned(16))) float mu[16 * D];
+  __shared__ __attribute__((aligned(16))) float mu[CMAX * D];
   __shared__ int asg[128];
   __shared__ int order[128];  // rows sorted by cluster, ascending within
   __shared__ int cnt[16], off[16];
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
       if (r < n) st16(&qb16[r * QS + c8 * 8], v[i]);
     }
   }
-  for (int e = t; e < 16 * D; e += 256) mu[e] = 0.f;
+  for (int e = t; e < CMAX * D; e += 256) mu[e] = 0.f;
   if (t < 16) active[t] = (t < C) && (((t + 1) * n) / C > (t * n) / C);
   if (t < n) {
     int c = 0;
@@ -668,12 +670,14 @@ int launch_select_scores(const void *q, const void *k, int B, int H, int N, int 
   const dim3 gpool(L.ktiles, BH), gkm(L.nqb, BH), gsc((unsigned)nsc);
   if (d == 128) {
     hipLaunchKernelGGL(pool_split_kernel<128>, gpool, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(kmeans_kernel<128>, gkm, dim3(256), 0, stream, a);
+    if (n_clusters <= 8) hipLaunchKernelGGL((kmeans_kernel<128, 8>), gkm, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((kmeans_kernel<128, 16>), gkm, dim3(256), 0, stream, a);
     hipLaunchKernelGGL((score_kernel<128, 0>), gsc, dim3(256), 0, stream, a);
     hipLaunchKernelGGL((score_kernel<128, 1>), gsc, dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL(pool_split_kernel<64>, gpool, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(kmeans_kernel<64>, gkm, dim3(256), 0, stream, a);
+    if (n_clusters <= 8) hipLaunchKernelGGL((kmeans_kernel<64, 8>), gkm, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((kmeans_kernel<64, 16>), gkm, dim3(256), 0, stream, a);
     hipLaunchKernelGGL((score_kernel<64, 0>), gsc, dim3(256), 0, stream, a);
     hipLaunchKernelGGL((score_kernel<64, 1>), gsc, dim3(256), 0, stream, a);
   }
