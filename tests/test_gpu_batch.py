@@ -23,13 +23,15 @@ def env():
     return bsa, _gpu, torch
 
 
-def test_batch_select_plan_attention(env):
+@pytest.mark.parametrize("d,kvb,Wg", [(128, 4, 37), (128, 2, 37), (64, 4, 38)])
+def test_batch_select_plan_attention(env, d, kvb, Wg):
     """Scores of every (b, h) against the oracle's; then the oracle's scores
     go through the device plan and attention (the oracle sees only its own
-    values), which must match the oracle's plan and attention."""
+    values), which must match the oracle's plan and attention.  KV blocks of
+    2 tokens at d = 128 and 4 at d = 64 run the half-load gather."""
     bsa, g, torch = env
-    B, H, T, Hg, Wg, d, kvb, C, budget = 2, 3, 2, 9, 37, 128, 4, 8, 40
-    g.say(f"case batch path B={B} H={H} N={T * Hg * Wg}")
+    B, H, T, Hg, C, budget = 2, 3, 2, 9, 8, 40
+    g.say(f"case batch path B={B} H={H} N={T * Hg * Wg} d={d} kv_block={kvb}")
     qb, kb, vb = make_qkv(T, Hg, Wg, H, d, seed=21, B=B)
     q, k, v = g.to_dev_bf16(qb), g.to_dev_bf16(kb), g.to_dev_bf16(vb)
     S, _, _ = bsa.bsa_select_scores(q, k, 128, kvb, C, 1)
