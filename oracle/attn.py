@@ -12,7 +12,12 @@ no online rescaling.
 
 Readings: scale 1/sqrt(d) unless given; no causal mask (full 3D attention of
 a video DiT); natural log; the shift applies to every token of the block;
-keys with index >= Nk (partial last block, padding) are left out.
+keys with index >= Nk (partial last block, padding) are left out.  The list
+format (fixed stride, a per-row count) has two more rules: the count is
+clamped to [0, list length], and an entry outside [0, ceil(Nk / kv_block))
+names no block and is skipped (the planner marks unused entries with -1 and
+a row it could not plan with count -1).  A query block left with no key gets
+a zero output and LSE = -inf (the empty sum).
 
 ``attn_bwd`` is the gradient of the same definition (the page names a
 trainable version, with a backward pass, as future work in its closing
@@ -24,8 +29,21 @@ from __future__ import annotations
 import numpy as np
 
 
+def listed_blocks(idx_row, bias_row, count: int, M: int):
+    """The entries of one list row that name a block: the first
+    min(max(count, 0), L) entries, minus those outside [0, M).  Returns
+    (blocks int64, bias fp32); ``bias_row`` None means every shift is 0."""
+    row = np.asarray(idx_row).astype(np.int64)
+    c = max(0, min(int(count), row.shape[0]))
+    bl = row[:c]
+    b = np.zeros(c, np.float32) if bias_row is None else np.asarray(bias_row)[:c]
+    ok = (bl >= 0) & (bl < M)
+    return bl[ok], b[ok]
+
+
 def gather_keys(blocks: np.ndarray, bias: np.ndarray, kv_block: int, Nk: int):
-    """Token indices and per-token logit shift of the listed blocks."""
+    """Token indices and per-token logit shift of the listed blocks (each in
+    [0, ceil(Nk / kv_block)))."""
     keys = (blocks[:, None].astype(np.int64) * kv_block + np.arange(kv_block)).ravel()
     kb = np.repeat(bias.astype(np.float64), kv_block)
     valid = keys < Nk
@@ -38,22 +56,27 @@ def attn_fwd(q, k, v, q_block: int, kv_block: int, idx, bias, count,
     fp32 or None (all pi = 1), count (nqb,) int.
 
     Returns (O (Nq, d) fp64, LSE (Nq,) fp64 natural log).  ``blocks`` limits the
-    work to the listed query blocks (other rows stay NaN).
+    work to the listed query blocks (other rows stay NaN).  List entries
+    follow ``listed_blocks``; a query block with no key gets O = 0 and
+    LSE = -inf.
     """
     Nq, d = q.shape
     Nk = k.shape[0]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     nqb = -(-Nq // q_block)
+    M = -(-Nk // kv_block)
     O = np.full((Nq, d), np.nan)
     lse = np.full(Nq, np.nan)
     todo = range(nqb) if blocks is None else blocks
     for i in todo:
-        c = int(count[i])
-        bl = np.asarray(idx[i][:c])
-        b = np.zeros(c, np.float32) if bias is None else np.asarray(bias[i][:c])
+        bl, b = listed_blocks(idx[i], None if bias is None else bias[i], count[i], M)
         keys, kb = gather_keys(bl, b, kv_block, Nk)
         r0, r1 = i * q_block, min(Nq, (i + 1) * q_block)
+        if keys.size == 0:
+            O[r0:r1] = 0.0
+            lse[r0:r1] = -np.inf
+            continue
         logits = (q[r0:r1] @ k[keys].T) * scale + kb[None, :]
         m = logits.max(axis=1, keepdims=True)
         e = np.exp(logits - m)
@@ -97,12 +120,8 @@ def attn_bwd(q, k, v, dout, q_block: int, kv_block: int, idx, bias, count,
     dv = np.zeros((Nk, d))
     M = -(-Nk // kv_block)
     for i in (range(nqb) if blocks is None else blocks):
-        L = np.asarray(idx[i]).shape[0]
-        c = max(0, min(int(count[i]), L))
-        bl = np.asarray(idx[i][:c]).astype(np.int64)
-        b = np.zeros(c, np.float32) if bias is None else np.asarray(bias[i][:c])
-        ok = (bl >= 0) & (bl < M)
-        keys, kb = gather_keys(bl[ok], b[ok], kv_block, Nk)
+        bl, b = listed_blocks(idx[i], None if bias is None else bias[i], count[i], M)
+        keys, kb = gather_keys(bl, b, kv_block, Nk)
         if keys.size == 0:
             continue
         r0, r1 = i * q_block, min(Nq, (i + 1) * q_block)

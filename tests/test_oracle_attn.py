@@ -96,3 +96,62 @@ def test_topk_plan_attention_equals_dense_over_selected_keys():
     keys = np.concatenate([np.arange(j * 4, j * 4 + 4) for j in idx[0]])
     ref, _ = oat.dense_attn(q, k[keys], v[keys])
     np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-13)
+
+
+def _sdpa_over(q, k, v, keys, shift):
+    """torch fp64 SDPA over the given key rows with an additive per-key shift."""
+    tq = torch.from_numpy(q)[None, None]
+    tk = torch.from_numpy(k[keys])[None, None]
+    tv = torch.from_numpy(v[keys])[None, None]
+    mask = torch.from_numpy(np.broadcast_to(shift, (q.shape[0], len(keys))).copy())[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)[0, 0].numpy()
+
+
+def test_list_entries_outside_range_and_count_clamping():
+    """The list rules of the boundary: entries outside [0, M) (-1, M, 2^30 + 1,
+    -2^31) name no block and are skipped, a block listed twice counts twice,
+    the count is clamped to [0, L] (negative -> empty, beyond L -> L), and an
+    empty row gives zeros with LSE -inf.  Checked against torch SDPA over the
+    explicitly listed key rows (Nk = 130: block 32 holds 2 keys)."""
+    q, k, v = _head(1, 10, 39, 32, seed=8)       # Nq = 390: 4 query blocks (last 6 rows)
+    k, v = k[:130], v[:130]
+    M = 33
+    L = 8
+    idx = np.full((4, L), 5, np.int64)
+    bias = np.random.default_rng(2).random((4, L)).astype(np.float32)
+    idx[0] = [3, -1, M, 2**30 + 1, -2**31, 32, 3, 0]
+    idx[1] = [1, 2, 3, 4, 5, 6, 7, 8]
+    idx[2] = [-1, M, 40, -7, 9, 9, 9, 9]
+    idx[3] = [10, 11, 12, 13, 14, 15, 16, 17]
+    cnt = np.array([8, -1, 5, 99])
+    O, lse = oat.attn_fwd(q, k, v, 128, 4, idx, bias, cnt)
+    # row 0: entries 0, 5, 6, 7 are blocks 3, 32, 3, 0
+    keep = [(3, 0), (32, 5), (3, 6), (0, 7)]
+    keys = np.concatenate([np.arange(j * 4, min(130, j * 4 + 4)) for j, _ in keep])
+    shift = np.concatenate([np.full(min(130, j * 4 + 4) - j * 4, np.float64(bias[0, e]))
+                            for j, e in keep])
+    np.testing.assert_allclose(O[:128], _sdpa_over(q[:128], k, v, keys, shift),
+                               rtol=1e-10, atol=1e-12)
+    # row 1: count -1 -> no key; row 2: the first five entries, only block 9 valid
+    assert np.all(O[128:256] == 0) and np.all(np.isneginf(lse[128:256]))
+    keys = np.arange(36, 40)
+    np.testing.assert_allclose(O[256:384], _sdpa_over(q[256:384], k, v, keys,
+                                                      np.full(4, np.float64(bias[2, 4]))),
+                               rtol=1e-10, atol=1e-12)
+    # row 3: count beyond L -> all L entries
+    keys = np.arange(40, 72)
+    shift = np.repeat(bias[3].astype(np.float64), 4)
+    np.testing.assert_allclose(O[384:], _sdpa_over(q[384:], k, v, keys, shift),
+                               rtol=1e-10, atol=1e-12)
+    # the backward skips by the same rule: its dq of the empty row is zero
+    dq, _, _ = oat.attn_bwd(q, k, v, np.ones_like(q), 128, 4, idx, bias, cnt)
+    assert np.all(dq[128:256] == 0)
+
+
+def test_list_row_of_only_invalid_entries_is_empty():
+    q, k, v = _head(1, 8, 16, 32, seed=9)
+    idx = np.array([[-1, -1, 32, 99]])
+    O, lse = oat.attn_fwd(q, k, v, 128, 4, idx, None, [4])
+    assert np.all(O == 0) and np.all(np.isneginf(lse))
+    O, lse = oat.attn_fwd(q, k, v, 128, 4, idx, None, [0])
+    assert np.all(O == 0) and np.all(np.isneginf(lse))

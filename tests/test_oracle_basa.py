@@ -136,3 +136,34 @@ def test_basa_key_set_definition_small():
         lg = kk @ q[n] / 4.0
         p = np.exp(lg - lg.max()); p /= p.sum()
         np.testing.assert_allclose(O[n], p @ vv, rtol=1e-12, atol=1e-13)
+
+
+def _tie_inputs(d=8):
+    """A 1 x 12 x 12 grid cut into nine 4 x 4 windows (no roll) whose key
+    descriptors are a_w e_0 + 0.5 (e_1 + ... + e_{d-1}) with a = (2, 3, 3, 1,
+    3, 2, 1, 3, 2), and every query all ones: the score of candidate w is
+    a_w + 0.5 (d - 1) for every query window, exactly, in fp32 -- four
+    windows tie at the top, three below them, two at the bottom."""
+    T, Hg, Wg = 1, 12, 12
+    a = np.array([2, 3, 3, 1, 3, 2, 1, 3, 2], np.float32)
+    mem = ob.window_members(T, Hg, Wg, 4, 4, 0, 0)
+    q = np.ones((T * Hg * Wg, d), np.float32)
+    k = np.full((T * Hg * Wg, d), 0.5, np.float32)
+    for w, m in enumerate(mem):
+        k[m, 0] = a[w]
+    return q, k, mem
+
+
+@pytest.mark.parametrize("topk,expect", [
+    (3, {0: [1, 2, 4], 1: [2, 4, 7], 2: [1, 4, 7], 3: [1, 2, 4], 4: [1, 2, 7],
+         5: [1, 2, 4], 6: [1, 2, 4], 7: [1, 2, 4], 8: [1, 2, 4]}),
+    (6, {0: [1, 2, 4, 7, 5, 8], 1: [2, 4, 7, 0, 5, 8], 5: [1, 2, 4, 7, 0, 8],
+         3: [1, 2, 4, 7, 0, 5], 8: [1, 2, 4, 7, 0, 5]}),
+])
+def test_routing_ties_go_to_the_lowest_window(topk, expect):
+    """Equal relevance: rank order best first, and among equal scores the
+    lowest window id first (the reading the boundary documents)."""
+    q, k, mem = _tie_inputs()
+    routes = ob.route(q, k, mem, topk)
+    for i, want in expect.items():
+        assert routes[i].tolist() == want, (i, routes[i].tolist())
