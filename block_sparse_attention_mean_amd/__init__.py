@@ -13,6 +13,12 @@ import ctypes
 import math
 import os
 
+# torch first: it carries its own HIP runtime, and libbsa.so's dependency on
+# libamdhip64.so.7 must resolve to that copy.  Loaded before torch, the
+# library would pull in a second HIP runtime (/opt/rocm's), in which torch's
+# streams and allocations do not exist, and every launch would fail.
+import torch  # noqa: F401
+
 __all__ = [
     "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",

@@ -563,6 +563,7 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
                     const float *lse, int B, int H, int Nq, int Nk, int d, int kv_block,
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream) {
+  clear_pending_error();
   BwdArgs a;
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;

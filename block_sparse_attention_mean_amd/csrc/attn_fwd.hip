@@ -629,6 +629,7 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
                     int d, int kv_block, const int32_t *idx, const float *bias,
                     const int32_t *count, int max_blocks, float scale, void *out, float *lse,
                     hipStream_t stream) {
+  clear_pending_error();
   AttnArgs a;
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;

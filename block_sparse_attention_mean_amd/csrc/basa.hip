@@ -407,6 +407,7 @@ int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, 
                      int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
                      int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
                      int32_t *routes, void *workspace, hipStream_t stream) {
+  clear_pending_error();
   int nwin, nqp, nk, mb;
   size_t ws;
   int st = basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, &nwin, &nqp, &nk, &mb,
@@ -448,6 +449,7 @@ int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, 
 
 int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
                             int d, int wh, int ww, int dy, int dx, hipStream_t stream) {
+  clear_pending_error();
   Geo g;
   if (!make_geo(T, Hg, Wg, wh, ww, dy, dx, 1, 1, 1, g)) return BSA_ERR_UNSUPPORTED;
   const int N = T * Hg * Wg;

@@ -46,4 +46,10 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 
 inline int status_of(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
+// hipGetLastError also returns an error that an earlier, unrelated HIP call
+// of the same thread left pending (a runtime probe of the caller's framework,
+// say).  Every launcher clears that first, so that the status it returns
+// after its launches speaks of its own launches only.
+inline void clear_pending_error() { (void)hipGetLastError(); }
+
 }  // namespace bsa

@@ -270,6 +270,7 @@ int mass_chunk_keys(int kv_block) { return kv_block * (kMassChunk / kv_block); }
 
 int launch_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
                       int d, int kv_block, float scale, float *mass, hipStream_t stream) {
+  clear_pending_error();
   MassArgs a;
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -293,6 +294,7 @@ int launch_block_mass(const void *q, const void *k, const float *lse, int B, int
 
 int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *count, int rows,
                          int M, int max_blocks, double *cov, hipStream_t stream) {
+  clear_pending_error();
   dim3 grid((unsigned)((rows + 255) / 256)), block(256);
   hipLaunchKernelGGL(plan_coverage_kernel, grid, block, 0, stream, mass, idx, count, rows, M,
                      max_blocks, cov);
@@ -301,6 +303,7 @@ int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *c
 
 int launch_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
                         hipStream_t stream) {
+  clear_pending_error();
   dim3 grid((unsigned)slabs), block(1024);
   hipLaunchKernelGGL(output_error_kernel, grid, block, 0, stream, (const uint16_t *)out,
                      (const uint16_t *)ref, n, sums);

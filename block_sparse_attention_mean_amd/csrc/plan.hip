@@ -883,6 +883,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
 int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, int mode,
                     uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
                     int32_t *count, double *lambda, hipStream_t stream) {
+  clear_pending_error();
   (void)nqb;
   PlanArgs a{scores, rows, M, budget, mode, seed, offsets, idx, bias, count, lambda};
   int dev = 0, max_lds = 65536;

@@ -637,6 +637,7 @@ size_t select_workspace_bytes(int B, int H, int N, int d, int kv_block, int n_cl
 int launch_select_scores(const void *q, const void *k, int B, int H, int N, int d, int kv_block,
                          int n_clusters, int kmeans_iters, float *scores, float *centroids,
                          float *weights, void *workspace, hipStream_t stream) {
+  clear_pending_error();
   if (n_clusters & (n_clusters - 1)) return BSA_ERR_UNSUPPORTED;  // 1, 2, 4, 8, 16
   const Layout L = make_layout(B, H, N, d, kv_block, n_clusters);
   char *ws = (char *)workspace;

@@ -42,7 +42,9 @@
  *     enqueued asynchronously on it; no entry point synchronises.
  *   - All argument checks run on the host before any HIP call, so an
  *     invalid call returns an error code without touching the GPU.  A HIP
- *     launch failure returns BSA_ERR_HIP.  Errors that only the device can
+ *     launch failure returns BSA_ERR_HIP (an error that an earlier HIP call
+ *     outside the library left pending on the thread is cleared first, so
+ *     the status speaks of the call's own launches).  Errors that only the device can
  *     see (non-finite scores, out-of-range block indices) are reported in
  *     the outputs as documented per call; they never fault.
  *   - Supported sizes: head dim d in {64, 128}; q_block = 128; kv_block a

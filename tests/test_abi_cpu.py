@@ -203,3 +203,20 @@ def _bwd(bsa, **kw):
 ])
 def test_attn_bwd_rejects_invalid_arguments(bsa, kw, status):
     assert _bwd(bsa, **kw) == status
+
+
+def test_binding_loads_the_library_into_torchs_hip_runtime():
+    """Importing the binding in a fresh process maps a single HIP runtime:
+    the one torch carries.  (Loaded before torch, libbsa.so would bring in
+    /opt/rocm's runtime as a second copy, in which torch's streams and
+    memory do not exist.)"""
+    import subprocess
+    import sys
+    code = ("import os, block_sparse_attention_mean_amd\n"
+            "m = open(f'/proc/{os.getpid()}/maps').read().splitlines()\n"
+            "print(sorted(set(l.split()[-1] for l in m if 'libamdhip64' in l)))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1 and "torch" in libs[0], libs
