@@ -22,8 +22,8 @@ import torch  # noqa: F401
 __all__ = [
     "lib", "BsaError", "bsa_select_scores", "bsa_sip_plan", "bsa_attn_fwd",
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
-    "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-    "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
+    "bsa_basa_plan", "bsa_basa_plan_noalloc", "bsa_window_unpermute", "bsa_block_mass",
+    "bsa_plan_coverage", "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
     "PLAN_SIP",
     "PLAN_TOPK", "LIB_PATH",
 ]
@@ -58,6 +58,8 @@ lib.bsa_basa_layout.restype = _i
 lib.bsa_basa_layout.argtypes = [_i] * 12 + [_pi] * 4 + [_psz]
 lib.bsa_basa_plan.restype = _i
 lib.bsa_basa_plan.argtypes = [_p, _p, _p] + [_i] * 14 + [_p] * 6 + [_p, _sz, _p]
+lib.bsa_basa_plan_noalloc.restype = _i
+lib.bsa_basa_plan_noalloc.argtypes = [_p, _p, _p] + [_i] * 14 + [_p] * 6 + [_p]
 lib.bsa_window_unpermute.restype = _i
 lib.bsa_window_unpermute.argtypes = [_p, _p] + [_i] * 10 + [_p]
 lib.bsa_block_mass.restype = _i
@@ -77,7 +79,8 @@ lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bsa_select_scores",
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
            "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
-           "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd"]
+           "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
+           "bsa_basa_plan_noalloc"]
 
 
 class BsaError(RuntimeError):
@@ -240,6 +243,35 @@ def bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block=4, B=1, H=1):
     return out
 
 
+def _basa_outputs(q, lay, topk, want_routes, out):
+    """Output tensors of the BASA list builder: the caller's (``out``, a dict
+    with the keys bsa_basa_plan returns, checked against the layout) or new
+    ones."""
+    import torch
+    B, H, _, d = q.shape
+    nqb = lay["Nq_pad"] // 128
+    shapes = dict(qp=((B, H, lay["Nq_pad"], d), torch.bfloat16),
+                  kp=((B, H, lay["Nk"], d), torch.bfloat16),
+                  vp=((B, H, lay["Nk"], d), torch.bfloat16),
+                  idx=((B, H, nqb, lay["max_blocks"]), torch.int32),
+                  count=((B, H, nqb), torch.int32),
+                  routes=((B, H, lay["nwin"], max(topk, 1)), torch.int32))
+    res = {}
+    for key, (shape, dtype) in shapes.items():
+        t = None if out is None else out.get(key)
+        if t is None:
+            if key == "routes" and not want_routes:
+                res[key] = None
+                continue
+            t = torch.empty(shape, dtype=dtype, device=q.device)
+        else:
+            _need(t, dtype, key)
+            if tuple(t.shape) != shape or t.device != q.device:
+                raise ValueError(f"{key} must have shape {shape} on {q.device}")
+        res[key] = t
+    return res
+
+
 def bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
                   want_routes=False, stream=None):
     """Window-major Q/K/V (+ pooled memory) and the block lists of BASA."""
@@ -248,21 +280,34 @@ def bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
         _need(t, torch.bfloat16, n, 4)
     B, H, N, d = q.shape
     lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
-    dev = q.device
-    qp = torch.empty((B, H, lay["Nq_pad"], d), dtype=torch.bfloat16, device=dev)
-    kp = torch.empty((B, H, lay["Nk"], d), dtype=torch.bfloat16, device=dev)
-    vp = torch.empty_like(kp)
-    nqb = lay["Nq_pad"] // 128
-    idx = torch.empty((B, H, nqb, lay["max_blocks"]), dtype=torch.int32, device=dev)
-    count = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
-    routes = (torch.empty((B, H, lay["nwin"], max(topk, 1)), dtype=torch.int32, device=dev)
-              if want_routes else None)
-    ws = torch.empty(max(lay["workspace"], 256), dtype=torch.uint8, device=dev)
+    o = _basa_outputs(q, lay, topk, want_routes, None)
+    ws = torch.empty(max(lay["workspace"], 256), dtype=torch.uint8, device=q.device)
     _check(lib.bsa_basa_plan(_ptr(q), _ptr(k), _ptr(v), B, H, T, Hg, Wg, d, wh, ww, dy, dx, ph,
-                             pw, topk, kv_block, _ptr(qp), _ptr(kp), _ptr(vp), _ptr(idx),
-                             _ptr(count), _ptr(routes), _ptr(ws), ws.numel(), _stream(stream)),
+                             pw, topk, kv_block, _ptr(o["qp"]), _ptr(o["kp"]), _ptr(o["vp"]),
+                             _ptr(o["idx"]), _ptr(o["count"]), _ptr(o["routes"]), _ptr(ws),
+                             ws.numel(), _stream(stream)),
            "bsa_basa_plan")
-    return dict(qp=qp, kp=kp, vp=vp, idx=idx, count=count, routes=routes, **lay)
+    return dict(**o, **lay)
+
+
+def bsa_basa_plan_noalloc(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
+                          want_routes=False, out=None, stream=None):
+    """bsa_basa_plan without a workspace: the library's fixed device scratch
+    replaces it, so the C call allocates nothing.  ``out`` (a dict with the
+    keys qp, kp, vp, idx, count and optionally routes) supplies the outputs;
+    missing ones are allocated here, before the call."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, d = q.shape
+    lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
+    o = _basa_outputs(q, lay, topk, want_routes, out)
+    _check(lib.bsa_basa_plan_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, T, Hg, Wg, d, wh, ww, dy,
+                                     dx, ph, pw, topk, kv_block, _ptr(o["qp"]), _ptr(o["kp"]),
+                                     _ptr(o["vp"]), _ptr(o["idx"]), _ptr(o["count"]),
+                                     _ptr(o["routes"]), _stream(stream)),
+           "bsa_basa_plan_noalloc")
+    return dict(**o, **lay)
 
 
 def bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=None, stream=None):

@@ -29,6 +29,10 @@ int launch_basa_plan(const void *q, const void *k, const void *v, int B, int H, 
                      int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
                      int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
                      int32_t *routes, void *workspace, hipStream_t stream);
+int launch_basa_plan_noalloc(const void *q, const void *k, const void *v, int B, int H, int T,
+                             int Hg, int Wg, int d, int wh, int ww, int dy, int dx, int ph,
+                             int pw, int topk, int kv_block, void *qp, void *kp, void *vp,
+                             int32_t *idx, int32_t *count, int32_t *routes, hipStream_t stream);
 int launch_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg,
                             int Wg, int d, int wh, int ww, int dy, int dx, hipStream_t stream);
 uint64_t sampling_offset(uint64_t seed, uint64_t row);
@@ -70,6 +74,8 @@ const char *bsa_status_string(int status) {
     case BSA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case BSA_ERR_WORKSPACE: return "workspace missing or too small";
     case BSA_ERR_SIZE: return "size product exceeds the supported index range";
+    case BSA_ERR_SCRATCH:
+      return "problem needs more scratch than the allocation-free entry point's fixed array";
     default: return "unknown status";
   }
 }
@@ -161,26 +167,53 @@ int bsa_basa_layout(int T, int Hg, int Wg, int d, int wh, int ww, int ph, int pw
                           max_blocks, workspace);
 }
 
-int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
-                  int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
-                  int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
-                  int32_t *routes, void *workspace, size_t workspace_bytes, void *stream) {
+// Checks shared by bsa_basa_plan and bsa_basa_plan_noalloc; *ws receives the
+// scratch bytes the call needs.
+static int check_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T,
+                           int Hg, int Wg, int d, int wh, int ww, int ph, int pw, int topk,
+                           int kv_block, const void *qp, const void *kp, const void *vp,
+                           const int32_t *idx, const int32_t *count, const int32_t *routes,
+                           size_t *ws) {
   if (!q || !k || !v || !qp || !kp || !vp || !idx || !count) return BSA_ERR_ARG;
   int nwin, nqp, nk, mb;
-  size_t ws;
   int st = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H, &nwin, &nqp, &nk,
-                           &mb, &ws);
+                           &mb, ws);
   if (st != BSA_OK) return st;
   if (topk > nwin - 1) return BSA_ERR_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qp, 16) ||
       !aligned(kp, 16) || !aligned(vp, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
       (routes && !aligned(routes, 4)))
     return BSA_ERR_ALIGN;
+  return BSA_OK;
+}
+
+int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int T, int Hg,
+                  int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw, int topk,
+                  int kv_block, void *qp, void *kp, void *vp, int32_t *idx, int32_t *count,
+                  int32_t *routes, void *workspace, size_t workspace_bytes, void *stream) {
+  size_t ws;
+  const int st = check_basa_plan(q, k, v, B, H, T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, qp,
+                                 kp, vp, idx, count, routes, &ws);
+  if (st != BSA_OK) return st;
   if (!workspace || workspace_bytes < ws) return BSA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;
   return bsa::launch_basa_plan(q, k, v, B, H, T, Hg, Wg, d, wh, ww, dy, dx, ph, pw, topk,
                                kv_block, qp, kp, vp, idx, count, routes, workspace,
                                (hipStream_t)stream);
+}
+
+int bsa_basa_plan_noalloc(const void *q, const void *k, const void *v, int B, int H, int T,
+                          int Hg, int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw,
+                          int topk, int kv_block, void *qp, void *kp, void *vp, int32_t *idx,
+                          int32_t *count, int32_t *routes, void *stream) {
+  size_t ws;
+  const int st = check_basa_plan(q, k, v, B, H, T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, qp,
+                                 kp, vp, idx, count, routes, &ws);
+  if (st != BSA_OK) return st;
+  if (ws > BSA_BASA_NOALLOC_SCRATCH_BYTES) return BSA_ERR_SCRATCH;
+  return bsa::launch_basa_plan_noalloc(q, k, v, B, H, T, Hg, Wg, d, wh, ww, dy, dx, ph, pw, topk,
+                                       kv_block, qp, kp, vp, idx, count, routes,
+                                       (hipStream_t)stream);
 }
 
 int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,

@@ -37,7 +37,8 @@
  *   - Every pointer argument is a DEVICE pointer unless its comment says
  *     host.  The caller allocates and owns every buffer; the library never
  *     allocates, frees or keeps device memory and holds no state between
- *     calls.
+ *     calls (the one exception: the fixed scratch array that
+ *     bsa_basa_plan_noalloc uses instead of a workspace).
  *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *     enqueued asynchronously on it; no entry point synchronises.
  *   - All argument checks run on the host before any HIP call, so an
@@ -69,7 +70,8 @@ enum {
   BSA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned     */
   BSA_ERR_HIP = -5,         /* a HIP runtime call or launch failed         */
   BSA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required  */
-  BSA_ERR_SIZE = -7         /* a size product overflows the index range    */
+  BSA_ERR_SIZE = -7,        /* a size product overflows the index range    */
+  BSA_ERR_SCRATCH = -8      /* more than an allocation-free call's fixed scratch */
 };
 
 enum { BSA_PLAN_SIP = 0, BSA_PLAN_TOPK = 1 };
@@ -260,6 +262,26 @@ int bsa_basa_plan(const void *q, const void *k, const void *v, int B, int H, int
 
 int bsa_window_unpermute(const void *out_perm, void *out, int B, int H, int T, int Hg, int Wg,
                          int d, int wh, int ww, int dy, int dx, void *stream);
+
+/* bsa_basa_plan_noalloc: bsa_basa_plan without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments,
+ * outputs and results are those of bsa_basa_plan.  Its scratch (the fp32
+ * window means and the routes, the bytes bsa_basa_layout reports as
+ * `workspace`) lives in a fixed device array of
+ * BSA_BASA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends; the call allocates and frees nothing.  A problem
+ * whose scratch exceeds that size (B * H * nwin * (2 d + topk) * 4 bytes
+ * plus alignment, so about 60 heads of the 66-window 1664x960 layout at
+ * d = 128) returns BSA_ERR_SCRATCH before any HIP call.  Every call on a GPU
+ * uses the same array: calls that overlap on one GPU (on different streams
+ * or threads) race and must be serialised by the caller. */
+#define BSA_BASA_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+int bsa_basa_plan_noalloc(const void *q, const void *k, const void *v, int B, int H, int T,
+                          int Hg, int Wg, int d, int wh, int ww, int dy, int dx, int ph, int pw,
+                          int topk, int kv_block, void *qp, void *kp, void *vp, int32_t *idx,
+                          int32_t *count, int32_t *routes, void *stream);
 
 /* ------------------------------------------------------------------------
  * BASA shift schedule (BASA page, section "어떻게 동작하나": the window

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(bsa):
 
 
 def test_status_strings(bsa):
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert len(bsa.lib.bsa_status_string(s)) > 0
     assert bsa.lib.bsa_status_string(-99) == b"unknown status"
     assert b"gfx950" in bsa.lib.bsa_version()
