@@ -24,12 +24,12 @@ __all__ = [
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
     "bsa_basa_plan", "bsa_basa_plan_noalloc", "bsa_window_unpermute", "bsa_block_mass",
     "bsa_plan_coverage", "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
-    "PLAN_SIP",
-    "PLAN_TOPK", "LIB_PATH",
+    "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
 PLAN_SIP, PLAN_TOPK = 0, 1
+OK, ERR_NONFINITE = 0, -9   # values of a plan's status word
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
@@ -51,7 +51,7 @@ lib.bsa_select_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i, _psz]
 lib.bsa_select_scores.restype = _i
 lib.bsa_select_scores.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
 lib.bsa_sip_plan.restype = _i
-lib.bsa_sip_plan.argtypes = [_p, _i, _i, _i, _i, _i, _i, _u64, _p, _p, _p, _p, _p, _p]
+lib.bsa_sip_plan.argtypes = [_p, _i, _i, _i, _i, _i, _i, _u64, _p, _p, _p, _p, _p, _p, _p]
 lib.bsa_attn_fwd.restype = _i
 lib.bsa_attn_fwd.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _f, _p, _p, _p]
 lib.bsa_basa_layout.restype = _i
@@ -99,25 +99,36 @@ def _ptr(t):
 
 
 def _stream(stream):
-    import torch
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
 
 
-def _need(t, dtype, name, ndim=None):
-    import torch
+def _need(t, dtype, name, ndim=None, shape=None, device=None):
+    """A device tensor of ``dtype``, contiguous, with ``ndim`` dims or exactly
+    ``shape``, on ``device`` (default: the current device, where the library
+    launches).  Raises ValueError, so a wrong tensor never reaches a kernel."""
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims")
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    want = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if t.device != want:
+        raise ValueError(f"{name} is on {t.device}, expected {want}")
     return t
+
+
+def _opt(t, dtype, name, shape, device):
+    """_need for an optional tensor (None passes)."""
+    return None if t is None else _need(t, dtype, name, shape=shape, device=device)
 
 
 def bsa_sampling_offset(seed: int, row: int) -> int:
@@ -135,20 +146,24 @@ def bsa_select_scores(q, k, q_block=128, kv_block=4, n_clusters=8, kmeans_iters=
                       scores=None, centroids=None, weights=None, workspace=None,
                       want_centroids=False, stream=None):
     """q, k: [B,H,N,d] bf16 -> scores [B,H,nQB,M] fp32 (+ centroids, weights)."""
-    import torch
     _need(q, torch.bfloat16, "q", 4)
-    _need(k, torch.bfloat16, "k", 4)
+    dev = q.device
     B, H, N, d = q.shape
+    _need(k, torch.bfloat16, "k", shape=q.shape, device=dev)
     nqb, M = -(-N // q_block), -(-N // kv_block)
     if scores is None:
-        scores = torch.empty((B, H, nqb, M), dtype=torch.float32, device=q.device)
+        scores = torch.empty((B, H, nqb, M), dtype=torch.float32, device=dev)
+    _need(scores, torch.float32, "scores", shape=(B, H, nqb, M), device=dev)
     if want_centroids and centroids is None:
-        centroids = torch.empty((B, H, nqb, n_clusters, d), dtype=torch.float32, device=q.device)
+        centroids = torch.empty((B, H, nqb, n_clusters, d), dtype=torch.float32, device=dev)
     if want_centroids and weights is None:
-        weights = torch.empty((B, H, nqb, n_clusters), dtype=torch.float32, device=q.device)
+        weights = torch.empty((B, H, nqb, n_clusters), dtype=torch.float32, device=dev)
+    _opt(centroids, torch.float32, "centroids", (B, H, nqb, n_clusters, d), dev)
+    _opt(weights, torch.float32, "weights", (B, H, nqb, n_clusters), dev)
     need = bsa_select_workspace_bytes(B, H, N, d, q_block, kv_block, n_clusters)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", 1, device=dev)
     _check(lib.bsa_select_scores(_ptr(q), _ptr(k), B, H, N, d, q_block, kv_block, n_clusters,
                                  kmeans_iters, _ptr(scores), _ptr(centroids), _ptr(weights),
                                  _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -157,9 +172,12 @@ def bsa_select_scores(q, k, q_block=128, kv_block=4, n_clusters=8, kmeans_iters=
 
 
 def bsa_sip_plan(scores, budget, mode=PLAN_SIP, seed=0, offsets=None, idx=None, bias=None,
-                 count=None, lam=None, want_lambda=False, stream=None):
-    """scores [B,H,nQB,M] fp32 -> (idx, bias, count, lambda) device tensors."""
-    import torch
+                 count=None, lam=None, want_lambda=False, status=None, stream=None):
+    """scores [B,H,nQB,M] fp32 -> (idx, bias, count, lambda) device tensors.
+
+    ``status`` (optional, one int32 on the device) receives BSA_OK, or
+    BSA_ERR_NONFINITE when a row held a NaN, an infinity or a negative score
+    (that row gets count -1)."""
     _need(scores, torch.float32, "scores", 4)
     B, H, nqb, M = scores.shape
     dev = scores.device
@@ -171,35 +189,56 @@ def bsa_sip_plan(scores, budget, mode=PLAN_SIP, seed=0, offsets=None, idx=None, 
         count = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
     if want_lambda and lam is None:
         lam = torch.empty((B, H, nqb), dtype=torch.float64, device=dev)
+    _need(idx, torch.int32, "idx", shape=(B, H, nqb, budget), device=dev)
+    _need(bias, torch.float32, "bias", shape=(B, H, nqb, budget), device=dev)
+    _need(count, torch.int32, "count", shape=(B, H, nqb), device=dev)
+    _opt(lam, torch.float64, "lam", (B, H, nqb), dev)
+    _opt(status, torch.int32, "status", (1,), dev)
     if offsets is not None:
-        _need(offsets, torch.int64, "offsets")
+        _need(offsets, torch.int64, "offsets", device=dev)
+        if offsets.numel() != B * H * nqb:
+            raise ValueError(f"offsets must hold B*H*nQB = {B * H * nqb} values")
     _check(lib.bsa_sip_plan(_ptr(scores), B, H, nqb, M, budget, mode, seed & (2**64 - 1),
                             _ptr(offsets), _ptr(idx), _ptr(bias), _ptr(count), _ptr(lam),
-                            _stream(stream)), "bsa_sip_plan")
+                            _ptr(status), _stream(stream)), "bsa_sip_plan")
     return idx, bias, count, lam
+
+
+def _plan_args(q, k, idx, bias, count, q_block, dev):
+    """Shapes of an attention call: q [B,H,Nq,d], k [B,H,Nk,d], idx / bias
+    [B,H,nQB,L], count [B,H,nQB]; returns (B, H, Nq, Nk, d, L)."""
+    B, H, Nq, d = q.shape
+    if k.dim() != 4 or tuple(k.shape[:2]) != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k must have shape ({B}, {H}, Nk, {d}), got {tuple(k.shape)}")
+    Nk = k.shape[2]
+    nqb = -(-Nq // q_block)
+    _need(idx, torch.int32, "idx", 4, device=dev)
+    if tuple(idx.shape[:3]) != (B, H, nqb):
+        raise ValueError(f"idx must have shape ({B}, {H}, {nqb}, L), got {tuple(idx.shape)}")
+    L = idx.shape[3]
+    _opt(bias, torch.float32, "bias", (B, H, nqb, L), dev)
+    _need(count, torch.int32, "count", shape=(B, H, nqb), device=dev)
+    return B, H, Nq, Nk, d, L
 
 
 def bsa_attn_fwd(q, k, v, idx, bias, count, q_block=128, kv_block=4, softmax_scale=0.0,
                  out=None, lse=None, want_lse=False, stream=None):
     """q [B,H,Nq,d], k/v [B,H,Nk,d] bf16; idx [B,H,nQB,L] int32; bias (optional)
     [B,H,nQB,L] fp32; count [B,H,nQB] int32 -> out [B,H,Nq,d] bf16 (+ lse)."""
-    import torch
     _need(q, torch.bfloat16, "q", 4)
-    _need(k, torch.bfloat16, "k", 4)
-    _need(v, torch.bfloat16, "v", 4)
-    _need(idx, torch.int32, "idx", 4)
-    _need(count, torch.int32, "count", 3)
-    if bias is not None:
-        _need(bias, torch.float32, "bias", 4)
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    dev = q.device
+    _need(k, torch.bfloat16, "k", 4, device=dev)
+    B, H, Nq, Nk, d, L = _plan_args(q, k, idx, bias, count, q_block, dev)
+    _need(v, torch.bfloat16, "v", shape=k.shape, device=dev)
     if out is None:
         out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out", shape=q.shape, device=dev)
     if want_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    _opt(lse, torch.float32, "lse", (B, H, Nq), dev)
     _check(lib.bsa_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, q_block, kv_block,
-                            _ptr(idx), _ptr(bias), _ptr(count), idx.shape[-1],
-                            float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+                            _ptr(idx), _ptr(bias), _ptr(count), L, float(softmax_scale),
+                            _ptr(out), _ptr(lse), _stream(stream)),
            "bsa_attn_fwd")
     return out, lse
 
@@ -208,25 +247,26 @@ def bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_bloc
                  softmax_scale=0.0, dq=None, dk=None, dv=None, stream=None):
     """Gradients of sum(dout * out) for out = bsa_attn_fwd(q, k, v, idx, bias,
     count, ...) with the plan fixed: (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]) fp32."""
-    import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _need(t, torch.bfloat16, n, 4)
-    _need(lse, torch.float32, "lse", 3)
-    _need(idx, torch.int32, "idx", 4)
-    _need(count, torch.int32, "count", 3)
-    if bias is not None:
-        _need(bias, torch.float32, "bias", 4)
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    _need(q, torch.bfloat16, "q", 4)
+    dev = q.device
+    _need(k, torch.bfloat16, "k", 4, device=dev)
+    B, H, Nq, Nk, d, L = _plan_args(q, k, idx, bias, count, q_block, dev)
+    _need(v, torch.bfloat16, "v", shape=k.shape, device=dev)
+    _need(out, torch.bfloat16, "out", shape=q.shape, device=dev)
+    _need(dout, torch.bfloat16, "dout", shape=q.shape, device=dev)
+    _need(lse, torch.float32, "lse", shape=(B, H, Nq), device=dev)
     if dq is None:
-        dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=dev)
     if dk is None:
-        dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=dev)
     if dv is None:
-        dv = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+        dv = torch.empty((B, H, Nk, d), dtype=torch.float32, device=dev)
+    _need(dq, torch.float32, "dq", shape=(B, H, Nq, d), device=dev)
+    _need(dk, torch.float32, "dk", shape=(B, H, Nk, d), device=dev)
+    _need(dv, torch.float32, "dv", shape=(B, H, Nk, d), device=dev)
     _check(lib.bsa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), B, H, Nq,
                             Nk, d, q_block, kv_block, _ptr(idx), _ptr(bias), _ptr(count),
-                            idx.shape[-1], float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                            L, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                             _stream(stream)), "bsa_attn_bwd")
     return dq, dk, dv
 
@@ -247,7 +287,6 @@ def _basa_outputs(q, lay, topk, want_routes, out):
     """Output tensors of the BASA list builder: the caller's (``out``, a dict
     with the keys bsa_basa_plan returns, checked against the layout) or new
     ones."""
-    import torch
     B, H, _, d = q.shape
     nqb = lay["Nq_pad"] // 128
     shapes = dict(qp=((B, H, lay["Nq_pad"], d), torch.bfloat16),
@@ -265,20 +304,24 @@ def _basa_outputs(q, lay, topk, want_routes, out):
                 continue
             t = torch.empty(shape, dtype=dtype, device=q.device)
         else:
-            _need(t, dtype, key)
-            if tuple(t.shape) != shape or t.device != q.device:
-                raise ValueError(f"{key} must have shape {shape} on {q.device}")
+            _need(t, dtype, key, shape=shape, device=q.device)
         res[key] = t
     return res
+
+
+def _basa_inputs(q, k, v, T, Hg, Wg):
+    _need(q, torch.bfloat16, "q", 4)
+    if q.shape[2] != T * Hg * Wg:
+        raise ValueError(f"q holds {q.shape[2]} tokens, the grid {T}x{Hg}x{Wg} {T * Hg * Wg}")
+    _need(k, torch.bfloat16, "k", shape=q.shape, device=q.device)
+    _need(v, torch.bfloat16, "v", shape=q.shape, device=q.device)
+    return q.shape
 
 
 def bsa_basa_plan(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_block=4,
                   want_routes=False, stream=None):
     """Window-major Q/K/V (+ pooled memory) and the block lists of BASA."""
-    import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, torch.bfloat16, n, 4)
-    B, H, N, d = q.shape
+    B, H, N, d = _basa_inputs(q, k, v, T, Hg, Wg)
     lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
     o = _basa_outputs(q, lay, topk, want_routes, None)
     ws = torch.empty(max(lay["workspace"], 256), dtype=torch.uint8, device=q.device)
@@ -296,10 +339,7 @@ def bsa_basa_plan_noalloc(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_b
     replaces it, so the C call allocates nothing.  ``out`` (a dict with the
     keys qp, kp, vp, idx, count and optionally routes) supplies the outputs;
     missing ones are allocated here, before the call."""
-    import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, torch.bfloat16, n, 4)
-    B, H, N, d = q.shape
+    B, H, N, d = _basa_inputs(q, k, v, T, Hg, Wg)
     lay = bsa_basa_layout(T, Hg, Wg, d, wh, ww, ph, pw, topk, kv_block, B, H)
     o = _basa_outputs(q, lay, topk, want_routes, out)
     _check(lib.bsa_basa_plan_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, T, Hg, Wg, d, wh, ww, dy,
@@ -311,11 +351,15 @@ def bsa_basa_plan_noalloc(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kv_b
 
 
 def bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=None, stream=None):
-    import torch
     _need(out_perm, torch.bfloat16, "out_perm", 4)
-    B, H, _, d = out_perm.shape
+    B, H, Np, d = out_perm.shape
+    # the padded window-major row count depends on the windows only
+    nq_pad = bsa_basa_layout(T, Hg, Wg, d, wh, ww, 1, 1, 0, 1, B, H)["Nq_pad"]
+    if Np != nq_pad:
+        raise ValueError(f"out_perm must have {nq_pad} window-major rows, got {Np}")
     if out is None:
         out = torch.empty((B, H, T * Hg * Wg, d), dtype=torch.bfloat16, device=out_perm.device)
+    _need(out, torch.bfloat16, "out", shape=(B, H, T * Hg * Wg, d), device=out_perm.device)
     _check(lib.bsa_window_unpermute(_ptr(out_perm), _ptr(out), B, H, T, Hg, Wg, d, wh, ww, dy,
                                     dx, _stream(stream)), "bsa_window_unpermute")
     return out
@@ -324,7 +368,6 @@ def bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=None, stream=N
 def dense_plan(B, H, Nq, Nk, kv_block=128, device="cuda"):
     """A list of every KV block for every query block (no bias): with it,
     bsa_attn_fwd computes dense attention and its lse is the dense one."""
-    import torch
     nqb, M = -(-Nq // 128), -(-Nk // kv_block)
     idx = torch.arange(M, dtype=torch.int32, device=device).expand(B, H, nqb, M).contiguous()
     count = torch.full((B, H, nqb), M, dtype=torch.int32, device=device)
@@ -335,15 +378,20 @@ def bsa_block_mass(q, k, lse, q_block=128, kv_block=4, softmax_scale=0.0, mass=N
                    stream=None):
     """q [B,H,Nq,d], k [B,H,Nk,d] bf16, lse [B,H,Nq] fp32 (dense) -> mass
     [B,H,nQB,M] fp32: true attention mass of every KV block per query block."""
-    import torch
     _need(q, torch.bfloat16, "q", 4)
-    _need(k, torch.bfloat16, "k", 4)
-    _need(lse, torch.float32, "lse", 3)
+    dev = q.device
     B, H, Nq, d = q.shape
+    _need(k, torch.bfloat16, "k", 4, device=dev)
+    if tuple(k.shape[:2]) != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k must have shape ({B}, {H}, Nk, {d}), got {tuple(k.shape)}")
     Nk = k.shape[2]
+    _need(lse, torch.float32, "lse", shape=(B, H, Nq), device=dev)
+    if kv_block < 1:
+        raise ValueError("kv_block must be positive")
+    shape = (B, H, -(-Nq // q_block), -(-Nk // kv_block))
     if mass is None:
-        mass = torch.empty((B, H, -(-Nq // q_block), -(-Nk // kv_block)), dtype=torch.float32,
-                           device=q.device)
+        mass = torch.empty(shape, dtype=torch.float32, device=dev)
+    _need(mass, torch.float32, "mass", shape=shape, device=dev)
     _check(lib.bsa_block_mass(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, d, q_block, kv_block,
                               float(softmax_scale), _ptr(mass), _stream(stream)), "bsa_block_mass")
     return mass
@@ -352,16 +400,18 @@ def bsa_block_mass(q, k, lse, q_block=128, kv_block=4, softmax_scale=0.0, mass=N
 def bsa_plan_coverage(mass, idx, count, coverage=None, stream=None):
     """mass [..., M] fp32, idx [..., L] int32, count [...] int32 -> retained
     mass [...] fp64."""
-    import torch
     _need(mass, torch.float32, "mass")
-    _need(idx, torch.int32, "idx")
-    _need(count, torch.int32, "count")
+    dev = mass.device
+    _need(idx, torch.int32, "idx", device=dev)
+    _need(count, torch.int32, "count", device=dev)
     lead = tuple(mass.shape[:-1])
     rows = count.numel()
-    if tuple(idx.shape[:-1]) != lead or tuple(count.shape) != lead:
+    if mass.dim() < 1 or idx.dim() != mass.dim() or tuple(idx.shape[:-1]) != lead \
+            or tuple(count.shape) != lead:
         raise ValueError("mass, idx and count must share their leading dims")
     if coverage is None:
-        coverage = torch.empty(lead, dtype=torch.float64, device=mass.device)
+        coverage = torch.empty(lead, dtype=torch.float64, device=dev)
+    _need(coverage, torch.float64, "coverage", shape=lead, device=dev)
     _check(lib.bsa_plan_coverage(_ptr(mass), _ptr(idx), _ptr(count), rows, mass.shape[-1],
                                  idx.shape[-1], _ptr(coverage), _stream(stream)),
            "bsa_plan_coverage")
@@ -370,14 +420,12 @@ def bsa_plan_coverage(mass, idx, count, coverage=None, stream=None):
 
 def bsa_output_error(out, ref, sums=None, stream=None):
     """out, ref [B,H,N,d] bf16 -> sums [B,H,2] fp64: (sum (out-ref)^2, sum ref^2)."""
-    import torch
     _need(out, torch.bfloat16, "out", 4)
-    _need(ref, torch.bfloat16, "ref", 4)
-    if out.shape != ref.shape:
-        raise ValueError("out and ref differ in shape")
+    _need(ref, torch.bfloat16, "ref", shape=out.shape, device=out.device)
     B, H, N, d = out.shape
     if sums is None:
         sums = torch.empty((B, H, 2), dtype=torch.float64, device=out.device)
+    _need(sums, torch.float64, "sums", shape=(B, H, 2), device=out.device)
     _check(lib.bsa_output_error(_ptr(out), _ptr(ref), B * H, N * d, _ptr(sums), _stream(stream)),
            "bsa_output_error")
     return sums

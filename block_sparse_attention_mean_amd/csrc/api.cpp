@@ -17,7 +17,7 @@ int launch_attn_fwd(const void *q, const void *k, const void *v, int B, int H, i
                     hipStream_t stream);
 int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, int mode,
                     uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
-                    int32_t *count, double *lambda, hipStream_t stream);
+                    int32_t *count, double *lambda, int32_t *status, hipStream_t stream);
 int launch_select_scores(const void *q, const void *k, int B, int H, int N, int d, int kv_block,
                          int n_clusters, int kmeans_iters, float *scores, float *centroids,
                          float *weights, void *workspace, hipStream_t stream);
@@ -74,6 +74,7 @@ const char *bsa_status_string(int status) {
     case BSA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case BSA_ERR_WORKSPACE: return "workspace missing or too small";
     case BSA_ERR_SIZE: return "size product exceeds the supported index range";
+    case BSA_ERR_NONFINITE: return "a score row holds a NaN, an infinity or a negative value";
     case BSA_ERR_SCRATCH:
       return "problem needs more scratch than the allocation-free entry point's fixed array";
     default: return "unknown status";
@@ -107,19 +108,20 @@ int bsa_attn_fwd(const void *q, const void *k, const void *v, int B, int H, int 
 
 int bsa_sip_plan(const float *scores, int B, int H, int nQB, int M, int budget, int mode,
                  uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
-                 int32_t *count, double *lambda, void *stream) {
+                 int32_t *count, double *lambda, int32_t *status, void *stream) {
   if (!scores || !idx || !count) return BSA_ERR_ARG;
   if (B < 1 || H < 1 || nQB < 1 || M < 1) return BSA_ERR_ARG;
   if (mode != BSA_PLAN_SIP && mode != BSA_PLAN_TOPK) return BSA_ERR_ARG;
   if (budget < 1 || budget > M) return BSA_ERR_BUDGET;
   if (!aligned(scores, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
       (bias && !aligned(bias, 4)) || (lambda && !aligned(lambda, 8)) ||
-      (offsets && !aligned(offsets, 8)))
+      (offsets && !aligned(offsets, 8)) || (status && !aligned(status, 4)))
     return BSA_ERR_ALIGN;
   if ((long long)B * H * nQB > kMaxIndex) return BSA_ERR_SIZE;
   if (M > (1 << 20)) return BSA_ERR_SIZE;  // one row must fit the on-chip sampler
+  if (mode == BSA_PLAN_SIP && M > BSA_SIP_MAX_BLOCKS) return BSA_ERR_SIZE;
   return bsa::launch_sip_plan(scores, B * H * nQB, nQB, M, budget, mode, seed, offsets, idx,
-                              bias, count, lambda, (hipStream_t)stream);
+                              bias, count, lambda, status, (hipStream_t)stream);
 }
 
 int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_block,

@@ -66,6 +66,7 @@ struct PlanArgs {
   float *bias;
   int32_t *count;
   double *lambda;
+  int32_t *status;  // optional: BSA_ERR_NONFINITE when a row is invalid
 };
 
 // Small on purpose: with the row (M floats) this stays under half of a
@@ -489,6 +490,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
     if (t == 0) {
       a.count[r] = -1;
       if (a.lambda) a.lambda[r] = __builtin_nan("");
+      if (a.status) *a.status = BSA_ERR_NONFINITE;  // every writer stores the same value
     }
     return;
   }
@@ -878,14 +880,19 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   }
 }
 
+__global__ void status_init_kernel(int32_t *status) { *status = BSA_OK; }
+
 }  // namespace
 
 int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, int mode,
                     uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
-                    int32_t *count, double *lambda, hipStream_t stream) {
+                    int32_t *count, double *lambda, int32_t *status, hipStream_t stream) {
   clear_pending_error();
   (void)nqb;
-  PlanArgs a{scores, rows, M, budget, mode, seed, offsets, idx, bias, count, lambda};
+  PlanArgs a{scores, rows, M, budget, mode, seed, offsets, idx, bias, count, lambda, status};
+  // the status word is set by a kernel (not a memset) so that the call can
+  // be captured into a graph and replayed
+  if (status) hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(1), 0, stream, status);
   int dev = 0, max_lds = 65536;
   if (hipGetDevice(&dev) != hipSuccess) return BSA_ERR_HIP;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=

@@ -39,8 +39,9 @@
  *     allocates, frees or keeps device memory and holds no state between
  *     calls (the one exception: the fixed scratch array that
  *     bsa_basa_plan_noalloc uses instead of a workspace).
- *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
- *     enqueued asynchronously on it; no entry point synchronises.
+ *   - `stream` is a hipStream_t passed as `void *`, so that this header
+ *     needs no HIP include (NULL = the null stream).  All work is enqueued
+ *     asynchronously on it; no entry point synchronises.
  *   - All argument checks run on the host before any HIP call, so an
  *     invalid call returns an error code without touching the GPU.  A HIP
  *     launch failure returns BSA_ERR_HIP (an error that an earlier HIP call
@@ -71,7 +72,8 @@ enum {
   BSA_ERR_HIP = -5,         /* a HIP runtime call or launch failed         */
   BSA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required  */
   BSA_ERR_SIZE = -7,        /* a size product overflows the index range    */
-  BSA_ERR_SCRATCH = -8      /* more than an allocation-free call's fixed scratch */
+  BSA_ERR_SCRATCH = -8,     /* more than an allocation-free call's fixed scratch */
+  BSA_ERR_NONFINITE = -9    /* (device status word) a score row is not finite / >= 0 */
 };
 
 enum { BSA_PLAN_SIP = 0, BSA_PLAN_TOPK = 1 };
@@ -131,7 +133,10 @@ int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d,
  *   Pi_j = floor(pi_j * 2^44), C_j = Pi_0 + ... + Pi_j (exact integers);
  *   block j is drawn when some x_k = U + k * 2^44 (k = 0..s-1) falls in
  *   [C_{j-1}, C_j).  Exactly s distinct blocks are drawn; every block with
- *   pi = 1 is among them.
+ *   pi = 1 is among them.  (The floors lose less than one unit per block
+ *   and the fp64 rounding of lambda and pi less than 3 s 2^-9 units in all,
+ *   so C_M >= s 2^44 - 2^16 > x_{s-1} whenever M <= BSA_SIP_MAX_BLOCKS;
+ *   SIP rows longer than that are refused with BSA_ERR_SIZE.)
  * mode BSA_PLAN_TOPK: the s largest scores, ties to the lowest index, pi = 1,
  *   count = s.
  *
@@ -146,15 +151,24 @@ int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d,
  *          block (0 for top-k and for saturated blocks), 0 beyond count.
  *          May be NULL.
  * count    out: [B,H,nQB] int32 blocks drawn.  A row holding a NaN, an
- *          infinity or a negative score gets count = -1 and no blocks.
+ *          infinity or a negative score gets count = -1 and no blocks
+ *          (bsa_attn_fwd then gives its queries zero outputs).
  * lambda   optional out (NULL = not written): [B,H,nQB] fp64; +inf when
- *          every positive block is taken, 0 for top-k.
+ *          every positive block is taken, 0 for top-k, NaN for an invalid
+ *          row.
+ * status   optional out (NULL = not written): one device int32, set to
+ *          BSA_OK by the call and to BSA_ERR_NONFINITE if any row was
+ *          invalid, so that a caller can check a whole call with one read
+ *          once the stream has reached it.
+ * M        at most 2^20; in SIP mode at most BSA_SIP_MAX_BLOCKS.
  * The plan is caller-owned and stays valid for any number of later
  * bsa_attn_fwd calls (the page rebuilds it every 4 denoising steps).
  * --------------------------------------------------------------------- */
+#define BSA_SIP_MAX_BLOCKS 65024
+
 int bsa_sip_plan(const float *scores, int B, int H, int nQB, int M, int budget, int mode,
                  uint64_t seed, const uint64_t *offsets, int32_t *idx, float *bias,
-                 int32_t *count, double *lambda, void *stream);
+                 int32_t *count, double *lambda, int32_t *status, void *stream);
 
 /* Host helper, no GPU needed: U = floor((x >> 20) * (2^44 - 2^16) / 2^44)
  * where x is output number `row` (0-based) of SplitMix64 (Steele, Lea and

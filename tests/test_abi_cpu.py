@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(bsa):
 
 
 def test_status_strings(bsa):
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert len(bsa.lib.bsa_status_string(s)) > 0
     assert bsa.lib.bsa_status_string(-99) == b"unknown status"
     assert b"gfx950" in bsa.lib.bsa_version()
@@ -69,17 +69,20 @@ def test_attn_fwd_rejects_invalid_arguments(bsa, kw, status):
 
 def _plan(bsa, **kw):
     a = dict(S=FAKE, B=1, H=1, nqb=4, M=100, s=10, mode=0, seed=0, off=None, idx=FAKE, bias=FAKE,
-             count=FAKE, lam=None, stream=None)
+             count=FAKE, lam=None, status=None, stream=None)
     a.update(kw)
     return bsa.lib.bsa_sip_plan(a["S"], a["B"], a["H"], a["nqb"], a["M"], a["s"], a["mode"],
                                 a["seed"], a["off"], a["idx"], a["bias"], a["count"], a["lam"],
-                                a["stream"])
+                                a["status"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(S=None), -1), (dict(idx=None), -1), (dict(count=None), -1), (dict(M=0), -1),
     (dict(mode=2), -1), (dict(s=0), -3), (dict(s=101), -3), (dict(S=FAKE + 4), -4),
-    (dict(lam=FAKE + 4), -4), (dict(M=(1 << 20) + 1, s=5), -7),
+    (dict(lam=FAKE + 4), -4), (dict(status=FAKE + 2), -4), (dict(M=(1 << 20) + 1, s=5), -7),
+    (dict(M=(1 << 20) + 1, s=5, mode=1), -7),
+    # SIP rows longer than BSA_SIP_MAX_BLOCKS could draw fewer than s blocks
+    (dict(M=65025, s=5), -7), (dict(M=2**17, s=2**16), -7),
 ])
 def test_sip_plan_rejects_invalid_arguments(bsa, kw, status):
     assert _plan(bsa, **kw) == status

@@ -226,3 +226,55 @@ def test_plan_deterministic(env):
     a2 = _gpu_plan(env, S, 400, opl.SIP, seed=4)
     for x, y in zip(a1, a2):
         assert np.array_equal(x, y)
+
+
+def test_plan_status_word(env):
+    """The optional status word: BSA_OK after a call on valid rows, and
+    BSA_ERR_NONFINITE after a call with one bad row among good ones (the
+    bad row gets count -1, the good rows their plans); it is reset by every
+    call, so a good call after a bad one reads BSA_OK again."""
+    bsa, g, torch = env
+    g.say("case plan status word")
+    rng = np.random.default_rng(5)
+    S = _rows(rng, 6, 500).reshape(1, 2, 3, 500)
+    st = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    t = torch.from_numpy(S.copy()).cuda()
+    for mode in (opl.SIP, opl.TOPK):
+        bsa.bsa_sip_plan(t, 20, mode, seed=1, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == bsa.OK
+        bad = S.copy()
+        bad[0, 1, 2, 17] = np.nan if mode == opl.SIP else -0.5
+        tb = torch.from_numpy(bad).cuda()
+        idx, _, cnt, _ = bsa.bsa_sip_plan(tb, 20, mode, seed=1, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == bsa.ERR_NONFINITE
+        c = cnt.cpu().numpy()
+        assert c[0, 1, 2] == -1 and (np.delete(c.ravel(), 5) == 20).all()
+        want = opl.plan(S[0, 0], 20, mode, seed=1)      # head 0: rows 0..2, all valid
+        assert np.array_equal(idx.cpu().numpy()[0, 0], want[0])
+        bsa.bsa_sip_plan(t, 20, mode, seed=1, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == bsa.OK
+
+
+def test_plan_at_the_sip_row_limit(env):
+    """The longest SIP row the boundary accepts (65,024 blocks, the row
+    re-read from memory since it exceeds the LDS) with the budget that loses
+    the most fixed-point mass to the floors and the largest offset: exactly s
+    blocks, equal to the oracle's.  One block longer is refused."""
+    bsa, g, torch = env
+    M = 65024
+    s_all = np.arange(1, M, dtype=np.int64)
+    Pi = np.floor((s_all.astype(np.float64) / M) * float(1 << 44)).astype(np.int64)
+    s = int(s_all[np.argmax(s_all * (1 << 44) - M * Pi)])
+    g.say(f"case plan at the SIP row limit M={M} s={s}")
+    S = np.ones((1, 1, 2, M), np.float32)
+    S[0, 0, 1, ::7] = 0.5
+    off = np.array([OFFSET_LIMIT - 1, OFFSET_LIMIT - 1], np.uint64)
+    got = _gpu_plan(env, S, s, opl.SIP, offsets=off)
+    want = opl.plan(S, s, opl.SIP, offsets=off)
+    _compare(S, got, want, "row limit")
+    assert (got[2] == s).all()
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_sip_plan(torch.ones((1, 1, 1, M + 1), device="cuda"), 10, bsa.PLAN_SIP)

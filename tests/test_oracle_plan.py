@@ -184,3 +184,36 @@ def test_budgets_reproduce_page_sparsity(golden_dir):
     s = math.floor((1 - 0.9235) * 29700)
     assert round(100 * s / 29700, 2) == g["computed_pct"]["hunyuanvideo"]
     assert math.floor((1 - 0.8916) * 18900) == 2048 and s == 2272
+
+
+def _worst_uniform_budget(M):
+    """The budget s whose uniform row (all scores equal) loses the most
+    fixed-point mass to the floors: pi = s / M for every block, and
+    s 2^44 - M floor(pi 2^44) is largest."""
+    s = np.arange(1, M, dtype=np.int64)
+    lam = s.astype(np.float64) / M                      # one IEEE division, as the oracle
+    Pi = np.floor(lam * float(UNIT)).astype(np.int64)   # exact scaling by 2^44
+    deficit = s * UNIT - M * Pi
+    k = int(np.argmax(deficit))
+    return int(s[k]), int(deficit[k])
+
+
+def test_exactly_s_blocks_up_to_the_sip_row_limit():
+    """The floors of Pi_j lose less than one unit each and fp64 rounding
+    little more, so the fixed-point mass C_M stays above the last point
+    U + (s - 1) 2^44 for every offset U < 2^44 - 2^16 while M <= 65,024
+    (the limit the boundary enforces for SIP rows): the worst uniform row at
+    that M, with the largest offset, still draws exactly s blocks.  At
+    M = 2^17 + 1 the worst uniform row loses more than 2^16 units, and the
+    largest offset's last point falls past C_M."""
+    Umax = UNIT - (1 << 16) - 1
+    M = 65024
+    s, deficit = _worst_uniform_budget(M)
+    assert (1 << 15) < deficit < (1 << 16)
+    j, _, c, _ = opl.sip_row(np.ones(M), s, Umax)
+    assert c == s and len(np.unique(j)) == s
+    M = (1 << 17) + 1
+    s, deficit = _worst_uniform_budget(M)
+    assert deficit > (1 << 16)
+    with pytest.raises(AssertionError):
+        opl.sip_row(np.ones(M), s, Umax)
