@@ -13,6 +13,7 @@ import pytest
 
 from oracle import basa as obasa
 from synth import CONFIGS, bf16_bits_to_f32, bf16_bits_to_f64, make_qkv
+from tests import _pool
 
 pytestmark = pytest.mark.gpu
 
@@ -193,6 +194,68 @@ def test_basa_full_size_sampled_windows(env, name):
     g.assert_attn_close(got[rows], want[rows], f"basa {name} sampled windows")
 
 
+def _route_job(c, h):
+    sh = _pool.shared
+    members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
+    return obasa.route(bf16_bits_to_f32(sh["qb"][0, h]), bf16_bits_to_f32(sh["kb"][0, h]),
+                       members, c["topk"])
+
+
+def _window_job(c, h, wins):
+    """Oracle output rows of windows `wins` of head h against the device's:
+    (max-abs, mean-abs) per window."""
+    sh = _pool.shared
+    want, _ = obasa.basa_attn(sh["qb"][0, h], sh["kb"][0, h], sh["vb"][0, h], c["T"], c["Hg"],
+                              c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"], c["ph"], c["pw"],
+                              c["topk"], windows=wins, routes=sh["routes"][h])
+    members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
+    got = bf16_bits_to_f64(sh["out"][0, h])
+    out = []
+    for w in wins:
+        diff = np.abs(got[members[w]] - want[members[w]])
+        out.append((h, w, float(diff.max()), float(diff.mean())))
+    return out
+
+
+def test_basa_full_size_two_full_heads():
+    """The 1664x960 / 81-frame workload as the benchmark runs it: all 12
+    heads of 21 x 60 x 104 tokens in one call per stage, w = (10, 10),
+    Delta = (3, 7), top-2 routing, 4 x 4 pooling.  Routes of every window
+    of every head exact; output rows of every window of two full heads (the
+    first and the last: 2 x 66 windows) against the definition-based
+    oracle, within the attention tolerances per window."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_mean_amd as bsa
+    from tests import _gpu as g
+    c = CONFIGS["basa_1664x960"]
+    H = c["H"]
+    geo = dict(T=c["T"], Hg=c["Hg"], Wg=c["Wg"], wh=c["wh"], ww=c["ww"], dy=c["dy"], dx=c["dx"],
+               ph=c["ph"], pw=c["pw"], topk=c["topk"], kvb=c["kv_block"])
+    g.say(f"case basa full size, {H} heads, two full heads checked: {geo}")
+    qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], H, c["d"], seed=0, workers=_pool.workers())
+    plan, out = _run_basa((bsa, g, torch), qb, kb, vb, geo)
+    sh = _pool.shared
+    sh.clear()
+    sh.update(qb=qb, kb=kb, vb=vb, out=out.view(torch.int16).cpu().numpy().view(np.uint16))
+    routes = plan["routes"].cpu().numpy()
+    del plan, out
+    try:
+        want = _pool.run(_route_job, [(c, h) for h in range(H)], "basa routes")
+        for h in range(H):
+            np.testing.assert_array_equal(routes[0, h], want[h])
+        sh["routes"] = want
+        jobs = [(c, h, list(range(w, min(66, w + 6)))) for h in (0, H - 1) for w in range(0, 66, 6)]
+        res = [x for r in _pool.run(_window_job, jobs, "basa windows") for x in r]
+    finally:
+        sh.clear()
+    assert len(res) == 2 * 66
+    mx, mean = max(x[2] for x in res), max(x[3] for x in res)
+    g.say(f"  basa 2 x 66 windows: max-abs {mx:.3e}, worst window mean-abs {mean:.3e}")
+    assert mx <= g.ATTN_MAX_ABS and mean <= g.ATTN_MEAN_ABS
+
+
 def test_basa_layer_schedule(env):
     """Per-layer structured plans: four layers (each with its own
     activations) at two denoising steps with step offsets, the roll of each
@@ -220,3 +283,23 @@ def test_basa_layer_schedule(env):
             want, _ = obasa.basa_attn(qb[0, 0], kb[0, 0], vb[0, 0], T, Hg, Wg, wh, ww, oy, ox,
                                       ph, pw, topk, routes=routes)
             g.assert_attn_close(g.from_dev_bf16(out)[0, 0], want, f"layer {l} step {s}")
+
+
+def test_basa_routing_ties_on_the_device(env):
+    """Constructed windows whose relevance ties exactly (the pin of the
+    oracle's tie rule): the device routes equal the stated order -- best
+    first, equal scores by the lowest window id."""
+    bsa, g, torch = env
+    from tests.test_oracle_basa import _tie_inputs
+    from synth import f64_to_bf16_bits
+    g.say("case basa routing ties")
+    q, k, mem = _tie_inputs(d=64)
+    qb = f64_to_bf16_bits(q.astype(np.float64))[None, None]
+    kb = f64_to_bf16_bits(k.astype(np.float64))[None, None]
+    for topk, expect in ((3, [1, 2, 4]), (6, [1, 2, 4, 7, 5, 8])):
+        geo = dict(T=1, Hg=12, Wg=12, wh=4, ww=4, dy=0, dx=0, ph=4, pw=4, topk=topk, kvb=4)
+        plan, _ = _run_basa(env, qb, kb, kb, geo)
+        routes = plan["routes"].cpu().numpy()[0, 0]
+        want = obasa.route(q, k, mem, topk)
+        np.testing.assert_array_equal(routes, want)
+        assert routes[0].tolist() == expect

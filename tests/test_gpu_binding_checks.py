@@ -79,7 +79,7 @@ def test_plan_and_select_checks(env):
         with pytest.raises(ValueError):
             bsa.bsa_sip_plan(S, 10, bsa.PLAN_SIP, **kw)
     q = _t(torch, (1, 2, 256, 128), torch.bfloat16)
-    for kw in (dict(scores=_t(torch, (1, 2, 2, 64), f32)),
+    for kw in (dict(scores=_t(torch, (1, 2, 2, 63), f32)),
                dict(centroids=_t(torch, (1, 2, 2, 4, 128), f32), weights=_t(torch, (1, 2, 2, 8), f32)),
                dict(workspace=_t(torch, (16,), f32))):
         with pytest.raises(ValueError):
@@ -104,7 +104,7 @@ def test_basa_and_diag_checks(env):
     with pytest.raises(ValueError):
         bsa.bsa_block_mass(q, k, _t(torch, (1, 1, 300), f32))
     with pytest.raises(ValueError):
-        bsa.bsa_block_mass(q, k, _t(torch, (1, 1, 1040), f32), mass=_t(torch, (1, 1, 9, 75), f32))
+        bsa.bsa_block_mass(q, k, _t(torch, (1, 1, 1040), f32), mass=_t(torch, (1, 1, 9, 76), f32))
     with pytest.raises(ValueError):
         bsa.bsa_output_error(q, _t(torch, (1, 1, 1040, 32), bf))
     with pytest.raises(ValueError):
