@@ -43,11 +43,19 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --accuracy [--workload wan14b_720p] [--accuracy-heads 40]
        python bench.py --curve [--workload wan14b_720p]
        python bench.py --backward [--workload wan14b_720p]
+       python bench.py --mfma-peak
 
 With ``--backward`` it prints one JSON report of bsa_attn_bwd at the
 workload: the selector's SIP plan, one forward call for the output and its
 LSE, then the backward timed with HIP events (warmup + steps), against the
 algorithmic 10 d flops per (valid query, listed valid key) pair.
+
+With ``--mfma-peak`` it prints one JSON report of the bf16 matrix-instruction
+throughput probe (bsa_mfma_peak_probe: v_mfma_f32_32x32x16_bf16, the
+attention kernel's instruction, from registers) over a sweep of grid sizes.
+The benchmark line runs the same probe at its largest grid after the timed
+region and states the attention kernel's fraction of that measured rate
+beside the fraction of the published peak.
 """
 from __future__ import annotations
 
@@ -92,6 +100,8 @@ def parse():
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--backward", action="store_true",
                    help="print the backward-pass report instead of the benchmark line")
+    p.add_argument("--mfma-peak", action="store_true",
+                   help="print the matrix-instruction throughput report instead of the line")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run one device copy of this size (counter calibration)")
     return p.parse_args()
@@ -144,21 +154,54 @@ def host_cpu_model():
     return None
 
 
-def cpu_baseline(c, seed, heads):
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(c, seed, heads, one_thread_heads=1):
     """The oracle (as it stands) on whole heads 0..heads-1 of the workload:
     pooling, k-means, scores, plan (SIP, or top-k where the workload says
-    so) and attention of every query block.
-    Returns effective TFLOP/s (same definition as the GPU value)."""
+    so) and attention of every query block, on all the host's BLAS threads;
+    then the same on heads 0..one_thread_heads-1 with BLAS limited to one
+    thread.  Returns effective TFLOP/s (same definition as the GPU value),
+    seconds per head, and seconds per head times the workload's head count
+    (an extrapolation, labelled as such)."""
+    rec = _oracle_run(c, seed, heads)
+    rec.update({
+        "kind": "oracle", "cores": rec.pop("threads"),
+        "sample": (f"heads 0..{heads - 1} of {c['name']} (all query blocks): pooling, k-means, "
+                   f"scores, {'top-k' if c.get('mode') == 'topk' else 'SIP'} plan and attention, "
+                   f"fp64 numpy (k-means in its stated fp32 order)"),
+        "seconds_per_head": round(rec["seconds"] / heads, 3),
+        "extrapolated_seconds_all_heads": round(rec["seconds"] / heads * c["H"], 1),
+        "extrapolation": f"seconds per head x {c['H']} heads (not measured)",
+        "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
+    })
+    if one_thread_heads:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            one = _oracle_run(c, seed, one_thread_heads)
+        rec["one_thread"] = {
+            "value": one["value"], "unit": "TFLOP/s", "cores": one["threads"],
+            "sample": f"heads 0..{one_thread_heads - 1} of {c['name']}, the same stages",
+            "seconds": one["seconds"], "stage_seconds": one["stage_seconds"],
+            "seconds_per_head": round(one["seconds"] / one_thread_heads, 3),
+            "extrapolated_seconds_all_heads": round(one["seconds"] / one_thread_heads * c["H"], 1),
+        }
+    return rec
+
+
+def _oracle_run(c, seed, heads):
     import numpy as np
     from oracle import attn as oat
     from oracle import plan as opl
     from oracle import select as osel
     from synth import bf16_bits_to_f32, bf16_bits_to_f64, head_qkv
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     st = {"select": 0.0, "plan": 0.0, "attn": 0.0}
     flops = 0.0
     for h in range(heads):
@@ -182,16 +225,9 @@ def cpu_baseline(c, seed, heads):
         st["attn"] += t3 - t2
         flops += sum(4.0 * d * min(128, N - 128 * i) * int(cnt[i]) * kvb for i in range(nqb))
     total = sum(st.values())
-    return {
-        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"heads 0..{heads - 1} of {c['name']} (all query blocks): pooling, k-means, "
-                   f"scores, {'top-k' if c.get('mode') == 'topk' else 'SIP'} plan and attention, "
-                   f"fp64 numpy (k-means in its stated fp32 order)"),
-        "seconds": round(total, 3),
-        "stage_seconds": {k2: round(v2, 3) for k2, v2 in st.items()},
-        "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
-    }
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "threads": int(threads),
+            "seconds": round(total, 3),
+            "stage_seconds": {k2: round(v2, 3) for k2, v2 in st.items()}}
 
 
 def basa_window_rows(T, Hg, Wg, wh, ww):
@@ -213,11 +249,7 @@ def basa_cpu_baseline(c, seed, heads):
     import numpy as np
     from oracle import basa as obasa
     from synth import bf16_bits_to_f32, head_qkv
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     members = obasa.window_members(c["T"], c["Hg"], c["Wg"], c["wh"], c["ww"], c["dy"], c["dx"])
     npool = c["T"] * -(-c["Hg"] // c["ph"]) * -(-c["Wg"] // c["pw"])
     sec, flops = 0.0, 0.0
@@ -235,7 +267,10 @@ def basa_cpu_baseline(c, seed, heads):
         "value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"heads 0..{heads - 1} of {c['name']}, all {len(members)} windows: routing and "
                    f"attention, fp64 numpy (routing in its stated fp32 order)"),
-        "seconds": round(sec, 3), "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
+        "seconds": round(sec, 3), "seconds_per_head": round(sec / heads, 3),
+        "extrapolated_seconds_all_heads": round(sec / heads * c["H"], 1),
+        "extrapolation": f"seconds per head x {c['H']} heads (not measured)",
+        "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model(),
     }
 
 
@@ -304,9 +339,9 @@ def run_basa(args):
     g1.record(stream)
     torch.cuda.synchronize()
     ms_step = g0.elapsed_time(g1) / args.steps
-    prep = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
-    att = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
-    unp = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    prep = float(np.median([m[0].elapsed_time(m[1]) for m in marks]))
+    att = float(np.median([m[1].elapsed_time(m[2]) for m in marks]))
+    unp = float(np.median([m[2].elapsed_time(m[3]) for m in marks]))
     # algorithmic work: real (unpadded) queries x valid keys of their lists
     wins, _ = basa_window_rows(T, Hg, Wg, wh, ww)
     qvalid = np.zeros(nqb, np.int64)
@@ -481,6 +516,47 @@ def _time(fn, reps, warmup=1):
     return e0.elapsed_time(e1) / reps
 
 
+def mfma_peak(workgroups, iters=2000, reps=3):
+    """Best rate of the matrix-instruction probe over `reps` timed calls
+    (TFLOP/s), and the ms of one call."""
+    import torch
+    import block_sparse_attention_mean_amd as bsa
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    flops = bsa.bsa_mfma_peak_probe(workgroups, iters, sink)      # warmup
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bsa.bsa_mfma_peak_probe(workgroups, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return flops / best / 1e9, best
+
+
+PEAK_PROBE_GRID = 4096   # 16 workgroups of 4 waves per CU: 16 waves per SIMD saturate the units
+PEAK_PROBE_ITERS = 4000
+
+
+def run_mfma_peak(args):
+    """Throughput of v_mfma_f32_32x32x16_bf16 over grid sizes (see the
+    module docstring)."""
+    pts = []
+    for wg in (256, 512, 1024, 2048, PEAK_PROBE_GRID, 8192):
+        tf, ms = mfma_peak(wg, PEAK_PROBE_ITERS, reps=args.reps)
+        pts.append({"workgroups": wg, "waves_per_simd": wg * 4 / 1024, "ms": round(ms, 4),
+                    "tflops": round(tf, 2), "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"[mfma-peak] {pts[-1]}")
+    rep = {"report": "mfma peak", "kernel": "bsa::mfma_peak_kernel",
+           "instruction": "v_mfma_f32_32x32x16_bf16 (32768 flops), 8 independent chains per wave, "
+                          "operands in registers",
+           "iters": PEAK_PROBE_ITERS, "reps": args.reps, "peak_spec": PEAK_BF16_TFLOPS, "points": pts,
+           "best_tflops": max(p["tflops"] for p in pts)}
+    print(json.dumps(rep), flush=True)
+
+
 def run_dense_sdpa(args):
     """torch flash SDPA (no math fallback) at the workload's shape."""
     import torch
@@ -645,6 +721,8 @@ def main():
         return run_curve(args)
     if args.backward:
         return run_backward(args)
+    if args.mfma_peak:
+        return run_mfma_peak(args)
     if args.workload.startswith("basa"):
         return run_basa(args)
     import numpy as np
@@ -720,7 +798,7 @@ def main():
     flops = 4.0 * d * float((cnt_h[0] * kvb * rows[None, :]).sum())
     if not torch.isfinite(out.float()).all():
         raise SystemExit("non-finite attention output")
-    attn_ms = float(np.mean(att))
+    attn_ms = float(np.median(att))
     attn_tf = flops / attn_ms / 1e9
     value = flops / ms_step / 1e9
     traffic = traffic_for_current_kernel() if headline else None
@@ -749,6 +827,7 @@ def main():
             "step": "bsa_select_scores + bsa_sip_plan + bsa_attn_fwd",
         },
         "attn_ms_per_call": round(attn_ms, 4),
+        "attn_ms_mean": round(float(np.mean(att)), 4),
         "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(att, [10, 50, 90])],
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in
                                 np.percentile([m[0].elapsed_time(m[3]) for m in marks], [10, 50, 90])],
@@ -786,6 +865,16 @@ def main():
     torch.cuda.synchronize()
     rec["attn_ms_cold"] = round(c0.elapsed_time(c1), 4)
     del flush
+    # the matrix units' measured rate on the attention kernel's instruction
+    # (outside the timed region)
+    peak_meas, _ = mfma_peak(PEAK_PROBE_GRID, PEAK_PROBE_ITERS)
+    rec["roofline"].update({
+        "peak_measured": round(peak_meas, 2),
+        "frac_measured": round(attn_tf / peak_meas, 4),
+        "peak_measured_by": "bsa_mfma_peak_probe: v_mfma_f32_32x32x16_bf16 from registers, "
+                            f"{PEAK_PROBE_GRID} workgroups of 4 waves x {PEAK_PROBE_ITERS} rounds "
+                            "of 8 chains, best of 3 (bench.py --mfma-peak)",
+    })
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -24,7 +24,7 @@ __all__ = [
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
     "bsa_basa_plan", "bsa_basa_plan_noalloc", "bsa_window_unpermute", "bsa_block_mass",
     "bsa_plan_coverage", "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
-    "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
+    "bsa_mfma_peak_probe", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
@@ -72,6 +72,8 @@ lib.bsa_basa_offsets.restype = _i
 lib.bsa_basa_offsets.argtypes = [_i, _i, _pi]
 lib.bsa_basa_shifts.restype = _i
 lib.bsa_basa_shifts.argtypes = [_i, _i, _i, _i, _pi, _pi, _pi, _pi]
+lib.bsa_mfma_peak_probe.restype = _i
+lib.bsa_mfma_peak_probe.argtypes = [_i, _i, _p, ctypes.POINTER(ctypes.c_longlong), _p]
 lib.bsa_output_error.restype = _i
 lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 
@@ -80,7 +82,7 @@ SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bs
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
            "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
            "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
-           "bsa_basa_plan_noalloc"]
+           "bsa_basa_plan_noalloc", "bsa_mfma_peak_probe"]
 
 
 class BsaError(RuntimeError):
@@ -450,6 +452,16 @@ def bsa_basa_shifts(wh: int, ww: int, L: int, S: int = 1, c_h=None, c_w=None):
     _check(lib.bsa_basa_shifts(wh, ww, L, S, ch, cw, dy, dx), "bsa_basa_shifts")
     return ([list(dy[l * S:(l + 1) * S]) for l in range(L)],
             [list(dx[l * S:(l + 1) * S]) for l in range(L)])
+
+
+def bsa_mfma_peak_probe(workgroups, iters, sink, stream=None) -> int:
+    """Launches the bf16 matrix-instruction throughput probe; returns the
+    flops of the call (time it with events on the stream)."""
+    _need(sink, torch.float32, "sink", shape=(1,))
+    fl = ctypes.c_longlong(0)
+    _check(lib.bsa_mfma_peak_probe(workgroups, iters, _ptr(sink), ctypes.byref(fl),
+                                   _stream(stream)), "bsa_mfma_peak_probe")
+    return fl.value
 
 
 def default_scale(d: int) -> float:

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "plan.hip", "select.hip", "basa.hip",
-           "basa_noalloc.hip", "diag.hip"]
+           "basa_noalloc.hip", "diag.hip", "mfma_peak.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.

@@ -49,6 +49,8 @@ int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *c
                          int M, int max_blocks, double *cov, hipStream_t stream);
 int launch_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
                         hipStream_t stream);
+long long mfma_peak_flops(int workgroups, int iters);
+int launch_mfma_peak(int workgroups, int iters, float *sink, hipStream_t stream);
 }  // namespace bsa
 
 namespace {
@@ -305,6 +307,13 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
   return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, d, kv_block, idx, bias, count,
                               max_blocks, scale, dq, dk, dv, (hipStream_t)stream);
+}
+
+int bsa_mfma_peak_probe(int workgroups, int iters, float *sink, long long *flops, void *stream) {
+  if (!sink || workgroups < 1 || iters < 1) return BSA_ERR_ARG;
+  if (!aligned(sink, 4)) return BSA_ERR_ALIGN;
+  if (flops) *flops = bsa::mfma_peak_flops(workgroups, iters);
+  return bsa::launch_mfma_peak(workgroups, iters, sink, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -361,6 +361,20 @@ int bsa_plan_coverage(const float *mass, const int32_t *idx, const int32_t *coun
 int bsa_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
                      void *stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement helper: throughput probe of the bf16 matrix instruction the
+ * attention kernel uses (v_mfma_f32_32x32x16_bf16).  `workgroups` groups of
+ * 4 waves each run `iters` rounds of 8 independent accumulations from
+ * registers (no memory traffic); *flops (host out, may be NULL) receives the
+ * flops of the call, workgroups * 4 * iters * 8 * 32768.  Timing the call
+ * gives the matrix units' practical peak, against which the benchmark also
+ * states the attention kernel's fraction (beside the published 2516.6
+ * TFLOP/s).  sink: one device float the kernel writes (its result keeps the
+ * computation live).  Not part of the attention path.
+ * --------------------------------------------------------------------- */
+int bsa_mfma_peak_probe(int workgroups, int iters, float *sink, long long *flops /* host out */,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

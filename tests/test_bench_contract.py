@@ -60,10 +60,16 @@ def test_bench_line_on_the_tiny_workload():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["traffic"] is None  # the counter runs cover the headline workload only
+    assert roof["peak_measured"] > 0
+    assert abs(roof["frac_measured"] - roof["achieved"] / roof["peak_measured"]) < 1e-3
+    p10, p50, p90 = rec["attn_ms_p10_p50_p90"]
+    assert rec["attn_ms_per_call"] == p50                     # the median
     cpu = rec["cpu_baseline"]
-    for key in ("value", "unit", "cores", "kind", "sample"):
+    for key in ("value", "unit", "cores", "kind", "sample", "seconds_per_head",
+                "extrapolated_seconds_all_heads", "extrapolation", "one_thread"):
         assert key in cpu, key
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["unit"] == rec["unit"]
+    assert cpu["one_thread"]["cores"] == 1 and cpu["one_thread"]["value"] > 0
 
 
 def test_traffic_record_keyed_on_code(tmp_path, monkeypatch):
@@ -79,3 +85,18 @@ def test_traffic_record_keyed_on_code(tmp_path, monkeypatch):
     assert bench.attn_build_sha() == base
     p.write_text(src.replace("constexpr int NBUF = 3;", "constexpr int NBUF = 4;"))
     assert bench.attn_build_sha() != base
+
+
+@pytest.mark.gpu
+def test_mfma_peak_report():
+    """The matrix-instruction probe's report: a rate per grid size, none
+    above the published peak."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("case bench --mfma-peak", flush=True)
+    r = _run("--mfma-peak", "--reps", "2")
+    assert r.returncode == 0, r.stderr[-2000:]
+    rep = json.loads(r.stdout.strip().splitlines()[-1])
+    assert rep["best_tflops"] > 100
+    assert all(0 < p["tflops"] <= rep["peak_spec"] for p in rep["points"])
