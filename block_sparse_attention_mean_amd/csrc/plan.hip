@@ -69,22 +69,26 @@ struct PlanArgs {
   int32_t *status;  // optional: BSA_ERR_NONFINITE when a row is invalid
 };
 
-// Small on purpose: with the row (M floats) this stays under half of a
-// CU's LDS, so two rows run per CU.
-struct Shared {
-  uint64_t wdig[NW][NDIG + 1];  // per-wave digit sums of an exact sum
-  uint64_t total[NDIG + 1];     // normalised digits of the last exact sum
-  double red_d[NW];
-  long long red_l[NW];
-  unsigned red_u[NW];
-  unsigned red_u2[NW];
-  long long cl[2][NW];          // alternating buffers of the one-barrier reductions
-  double chi[2][NW], clo[2][NW];
+// Workgroup scratch of a row, for NWV waves.  Small on purpose: with the
+// row (M floats) beside it this stays under half of a CU's LDS, so two rows
+// of the LDS-resident kernel run per CU.
+template <int NWV>
+struct SharedT {
+  static constexpr int NW = NWV;
+  uint64_t wdig[NWV][NDIG + 1];  // per-wave digit sums of an exact sum
+  uint64_t total[NDIG + 1];      // normalised digits of the last exact sum
+  double red_d[NWV];
+  long long red_l[NWV];
+  unsigned red_u[NWV];
+  unsigned red_u2[NWV];
+  long long cl[2][NWV];          // alternating buffers of the one-barrier reductions
+  double chi[2][NWV], clo[2][NWV];
   double bcast_d;
   float col[MCAP];  // row values inside the final search bracket
   int cstat[MCAP];  // the condition at each: 1 holds, 0 fails, 2 undecided
   int ncol;
 };
+typedef SharedT<NW> Shared;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
@@ -108,7 +112,8 @@ __device__ __forceinline__ unsigned wave_min_u(unsigned v) {
 }
 
 // Block-wide sums: every thread gets the total (fixed reduction order).
-__device__ double block_sum_d(Shared &sh, double v) {
+template <class SH>
+__device__ __forceinline__ double block_sum_d(SH &sh, double v) {
   v = wave_sum_d(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -116,10 +121,11 @@ __device__ double block_sum_d(Shared &sh, double v) {
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) t += sh.red_d[i];
+  for (int i = 0; i < SH::NW; ++i) t += sh.red_d[i];
   return t;
 }
-__device__ long long block_sum_l(Shared &sh, long long v) {
+template <class SH>
+__device__ __forceinline__ long long block_sum_l(SH &sh, long long v) {
   v = wave_sum_l(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -127,10 +133,11 @@ __device__ long long block_sum_l(Shared &sh, long long v) {
   __syncthreads();
   long long t = 0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) t += sh.red_l[i];
+  for (int i = 0; i < SH::NW; ++i) t += sh.red_l[i];
   return t;
 }
-__device__ void block_minmax_u(Shared &sh, unsigned &mn, unsigned &mx) {
+template <class SH>
+__device__ __forceinline__ void block_minmax_u(SH &sh, unsigned &mn, unsigned &mx) {
   mn = wave_min_u(mn);
   mx = wave_max_u(mx);
   const int w = threadIdx.x >> 6;
@@ -143,13 +150,14 @@ __device__ void block_minmax_u(Shared &sh, unsigned &mn, unsigned &mx) {
   mn = sh.red_u[0];
   mx = sh.red_u2[0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) {
+  for (int i = 1; i < SH::NW; ++i) {
     mn = min(mn, sh.red_u[i]);
     mx = max(mx, sh.red_u2[i]);
   }
 }
 // Exclusive prefix over threads (thread order) of a 64-bit count.
-__device__ uint64_t block_exscan_u64(Shared &sh, uint64_t v, uint64_t &total) {
+template <class SH>
+__device__ __forceinline__ uint64_t block_exscan_u64(SH &sh, uint64_t v, uint64_t &total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t inc = v;
 #pragma unroll
@@ -163,7 +171,7 @@ __device__ uint64_t block_exscan_u64(Shared &sh, uint64_t v, uint64_t &total) {
   uint64_t base = 0;
   total = 0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
+  for (int i = 0; i < SH::NW; ++i) {
     const uint64_t t = (uint64_t)sh.red_l[i];
     if (i < w) base += t;
     total += t;
@@ -191,7 +199,8 @@ __device__ __forceinline__ void dd_add(double &hi, double &lo, double bhi, doubl
   lo = e - (hi - s);
 }
 // The same for a packed count and a plain fp64 sum.
-__device__ void block_reduce(Shared &sh, long long &cnt, double &sum, int &ph) {
+template <class SH>
+__device__ __forceinline__ void block_reduce(SH &sh, long long &cnt, double &sum, int &ph) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     cnt += __shfl_xor(cnt, o, 64);
@@ -206,13 +215,14 @@ __device__ void block_reduce(Shared &sh, long long &cnt, double &sum, int &ph) {
   cnt = sh.cl[ph][0];
   sum = sh.chi[ph][0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) {
+  for (int i = 1; i < SH::NW; ++i) {
     cnt += sh.cl[ph][i];
     sum += sh.chi[ph][i];
   }
   ph ^= 1;
 }
-__device__ void block_reduce(Shared &sh, long long &cnt, double &hi, double &lo, int &ph) {
+template <class SH>
+__device__ __forceinline__ void block_reduce(SH &sh, long long &cnt, double &hi, double &lo, int &ph) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const long long c2 = __shfl_xor(cnt, o, 64);
@@ -231,7 +241,7 @@ __device__ void block_reduce(Shared &sh, long long &cnt, double &hi, double &lo,
   hi = sh.chi[ph][0];
   lo = sh.clo[ph][0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) {
+  for (int i = 1; i < SH::NW; ++i) {
     cnt += sh.cl[ph][i];
     dd_add(hi, lo, sh.chi[ph][i], sh.clo[ph][i]);
   }
@@ -268,7 +278,12 @@ struct RowView {
       p = grow;
     }
   }
-  // f(j, value) over this thread's chunk, ascending j
+  // f(j, value) over this thread's chunk, ascending j; each_mem is the same
+  // here (the register-resident row below reads memory in it instead)
+  template <typename F>
+  __device__ __forceinline__ void each_mem(F f) const { each(f); }
+  template <int G, typename F>
+  __device__ __forceinline__ void each_seq(F f) const { each(f); }
   template <typename F>
   __device__ __forceinline__ void each(F f) const {
     int j = lo;
@@ -285,16 +300,78 @@ struct RowView {
   }
 };
 
+// Row held in registers (the SIP kernel for rows of at most 256 CH - 3
+// values): thread t owns the CH consecutive positions j0 = t CH - a ..
+// j0 + CH - 1, where a (0..3) is the row start's distance in floats from a
+// 16-byte boundary, so that every group of four is one aligned 16-byte
+// load.  Positions outside [0, M) hold 0, which a SIP plan never counts,
+// sums into anything but zero, or draws.  each() runs over the registers
+// (fully unrolled); each_mem() re-reads the thread's positions from memory
+// in a rolled loop, for the rarely taken exact evaluations, whose unrolled
+// code would be large.
+template <int CH>
+struct RegRow {
+  static_assert(CH % 4 == 0, "whole 16-byte groups");
+  mutable float v[CH];
+  int lo, M;
+  const float *g;
+  __device__ __forceinline__ void init(const float *grow, int m) {
+    const int a = (int)(((uintptr_t)grow >> 2) & 3);
+    lo = (int)threadIdx.x * CH - a;
+    M = m;
+    g = grow;
+    // A buffer over positions [-a, M): every group of four is one 16-byte
+    // load with no branch, and buffer loads are range-checked per dword, so
+    // positions at or past M read as zero (a group wholly past M, or the
+    // tail of the one group that straddles M).  Thread 0 zeroes the a
+    // positions before the row, which belong to the previous row.
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(grow - a), 0, (M + a) * 4, 0x00020000);
+    const int b0 = (int)threadIdx.x * CH * 4;
+#pragma unroll
+    for (int i = 0; i < CH; i += 4) {
+      const f32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, b0 + i * 4, 0, 0);
+      v[i] = q[0];
+      v[i + 1] = q[1];
+      v[i + 2] = q[2];
+      v[i + 3] = q[3];
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) v[k] = lo + k < 0 ? 0.f : v[k];
+  }
+  //
+  // Passes run in groups of 8 values with a scheduling barrier between
+  // groups: unbounded, the compiler computes every value's terms (and keeps
+  // every comparison's lane mask) ahead of the accumulations, which takes as
+  // many more registers as the row itself.
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const { each_seq<8>(f); }
+  template <int G, typename F>
+  __device__ __forceinline__ void each_seq(F f) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      asm volatile("" : "+v"(v[i]));
+      f(lo + i, v[i]);
+      if ((i + 1) % G == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  template <typename F>
+  __device__ __forceinline__ void each_mem(F f) const {
+    const int j1 = min(lo + CH, M);
+    for (int j = max(lo, 0); j < j1; ++j) f(j, g[j]);
+  }
+};
+
 // Double-double sum of {S_j < x} (strict) or {S_j <= x} (!strict), with
 // the count of S_j > x.  Per thread: exact two-sums into (hi, lo); then the
 // block reduction.  The result's error is below (chunk^2 + 64) 2^-104 of the
 // sum (chunk = values per thread).
-template <typename Row>
-__device__ void dd_sum(Shared &sh, const Row &row, float x, bool strict, double &hi, double &lo,
+template <class SH, typename Row>
+__device__ __forceinline__ void dd_sum(SH &sh, const Row &row, float x, bool strict, double &hi, double &lo,
                        long long &ngt, int &ph) {
   double h = 0.0, l = 0.0;
   long long c = 0;
-  row.each([&](int, float v) {
+  row.each_mem([&](int, float v) {
     const bool in = strict ? v < x : v <= x;
     c += v > x ? 1 : 0;
     double s2, e;
@@ -314,22 +391,27 @@ __device__ void dd_sum(Shared &sh, const Row &row, float x, bool strict, double 
 // Double-double sum of {S_j <= lo_x} (as dd_sum, same error bound) that also
 // collects the row values in (lo_x, hi_x) into sh.col; the caller knows
 // there are at most MCAP of them and has cleared sh.ncol.
-template <typename Row>
-__device__ void dd_sum_collect(Shared &sh, const Row &row, float lo_x, float hi_x, double &hi,
+template <class SH, typename Row>
+__device__ __forceinline__ void dd_sum_collect(SH &sh, const Row &row, float lo_x, float hi_x, double &hi,
                                double &lo, int &ph) {
   double h = 0.0, l = 0.0;
   long long c = 0;
+  int nin = 0;  // this thread's values inside the bracket (rare)
   row.each([&](int, float v) {
     const bool in = v <= lo_x;
     double s2, e;
     two_sum(h, in ? (double)v : 0.0, s2, e);
     h = s2;
     l += e;
-    if (!in && v < hi_x) {
-      const int slot = atomicAdd(&sh.ncol, 1);
-      if (slot < MCAP) sh.col[slot] = v;
-    }
+    nin += (!in && v < hi_x) ? 1 : 0;
   });
+  if (nin)
+    row.each_mem([&](int, float v) {
+      if (v > lo_x && v < hi_x) {
+        const int slot = atomicAdd(&sh.ncol, 1);
+        if (slot < MCAP) sh.col[slot] = v;
+      }
+    });
   const double n = h + l;
   l = l - (n - h);
   h = n;
@@ -342,12 +424,12 @@ __device__ void dd_sum_collect(Shared &sh, const Row &row, float lo_x, float hi_
 // 11 normalised 32-bit digits (units of 2^-149).  Only digits dlo..dhi can
 // receive a value (the row's exponent range); each thread accumulates them
 // in registers, then waves and workgroup add them up.
-template <typename Row>
-__device__ void exact_sum(Shared &sh, const Row &row, float x, bool strict, int dlo, int dhi) {
+template <class SH, typename Row>
+__device__ __forceinline__ void exact_sum(SH &sh, const Row &row, float x, bool strict, int dlo, int dhi) {
   uint64_t acc[NDIG + 1];
 #pragma unroll
   for (int i = 0; i <= NDIG; ++i) acc[i] = 0ull;
-  row.each([&](int, float v) {
+  row.each_mem([&](int, float v) {
     const bool in = strict ? v < x : v <= x;
     const unsigned b = in ? __builtin_bit_cast(unsigned, v) : 0u;
     const unsigned e = b >> 23;
@@ -377,7 +459,7 @@ __device__ void exact_sum(Shared &sh, const Row &row, float x, bool strict, int 
     for (int i = 0; i <= NDIG; ++i) {
       uint64_t a = carry;
       if (i >= dlo && i <= dhi)
-        for (int k = 0; k < NW; ++k) a += sh.wdig[k][i];
+        for (int k = 0; k < SH::NW; ++k) a += sh.wdig[k][i];
       sh.total[i] = a & 0xffffffffull;
       carry = a >> 32;
     }
@@ -443,6 +525,268 @@ __device__ bool digits_ge(const uint64_t *a, const uint64_t *b) {
   for (int i = NDIG; i >= 0; --i)
     if (a[i] != b[i]) return a[i] > b[i];
   return true;
+}
+
+// The saturation threshold of a SIP row with more than s positive scores,
+// by the decision procedure of the file header: nsat = r = #{S > x*} and
+// Tr = sum_{S <= x*} S correctly rounded to fp64.  PTH threads; every
+// thread's fp32 partial sums cover at most `chunk` row values; npos, mx,
+// mnpos (bit patterns of the largest and the smallest positive value) and
+// the approximate total tot come from the row's first pass.  Both plan
+// kernels take their decisions here, so they agree bit for bit.
+template <int PTH, class SH, typename Row>
+__device__ __forceinline__ void sip_threshold(SH &sh, const Row &row, int M, int s, long long npos, unsigned mx,
+                              unsigned mnpos, double tot, int chunk, long long &nsat,
+                              double &Tr) {
+  const int t = threadIdx.x;
+  // cond(x): (s - #{S >= x}) x <= sum_{S < x} S, decided with a certified
+  // fp64 margin or, inside the margin, from a double-double sum and, if
+  // even that cannot decide, exactly.  The search visits one point per
+  // iteration (a single evaluation site keeps the register footprint of
+  // the unrolled row passes small):
+  //   stage 0  x = max S           (true: no saturated block); needed only
+  //            when max S <= T / s, since cond(x) fails for every x > T / s
+  //   stage 1  secant steps down from T / s towards the threshold
+  //   stage 2  bisection of [blo, bhi) until no row value lies inside
+  // per-thread fp32 partial sums (chunk terms) then an fp64 reduction
+  const double err_bound =
+      (ldexp((double)(chunk + 2), -23) + ldexp((double)(M + 2 * PTH), -50)) * tot;
+  const double dd_rel = ldexp((double)chunk * (double)chunk + 64.0, -104) * 2.0;  // safety x2
+  const int dlo = digit_of(mnpos), dhi = digit_of(mx) + 1;
+  const float fmx = __builtin_bit_cast(float, mx);
+  // nge_lo = #{S >= blo} bounds the values left in (blo, bhi) from above
+  unsigned blo = mnpos, bhi = mx;
+  long long nge_lo = npos, nge_hi = 0;
+  float x = fmx;
+  int stage = 0, secant_left = 12, ph = 0;
+  float xstar = fmx;
+  {
+    const float x0 = (float)(tot / (double)s * (1.0 + 0x1p-20));  // above T / s
+    if (x0 < fmx && __builtin_bit_cast(unsigned, x0) > blo) {
+      x = x0;
+      stage = 1;
+    }
+  }
+  bool collect = false;
+  while (stage != 3) {
+    // ---- one pass at x
+    bool holds = true;
+    long long cnt = 0;
+    double slt = 0.0;
+    {
+      int cge = 0;
+      float sf = 0.f;
+      row.each([&](int, float v) {
+        const bool ge = v >= x;
+        cge += ge ? 1 : 0;
+        sf += ge ? 0.f : v;
+      });
+      cnt = cge;
+      slt = (double)sf;
+      block_reduce(sh, cnt, slt, ph);
+    }
+    const long long nge = cnt;
+    const long long mult = (long long)s - nge;
+    if (mult > 0) {
+      const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
+      const double diff = lhs - slt;
+      if (diff > err_bound) {
+        holds = false;
+      } else if (!(diff < -err_bound)) {
+        // inside the margin: double-double sum of {S < x}
+        double thi, tlo;
+        long long unused;
+        dd_sum(sh, row, x, true, thi, tlo, unused, ph);
+        double p, q;
+        two_sum(lhs, -thi, p, q);  // lhs - thi = p + q exactly
+        const double d = p + (q - tlo);
+        const double margin = dd_rel * thi + 0x1p-100 * (lhs + thi);
+        if (d > margin) {
+          holds = false;
+        } else if (!(d < -margin)) {
+          exact_sum(sh, row, x, true, dlo, dhi);
+          uint64_t ldig[NDIG + 1];
+          scaled_to_digits((unsigned long long)mult, x, ldig);
+          holds = digits_ge(sh.total, ldig);
+        }
+      }
+    }
+    // ---- advance the search
+    const unsigned xb = __builtin_bit_cast(unsigned, x);
+    if (stage == 0) {
+      if (holds) {  // no saturated block: x* = max S
+        xstar = x;
+        stage = 3;
+        continue;
+      }
+      nge_hi = nge;
+      stage = 1;
+      x = fminf(fmx, (float)(tot / (double)s * (1.0 + 0x1p-20)));  // x > T/s never holds
+      if (!(__builtin_bit_cast(unsigned, x) > blo && __builtin_bit_cast(unsigned, x) < bhi)) stage = 2;
+      else continue;
+    } else if (stage == 1) {
+      if (holds) {
+        blo = xb;
+        nge_lo = nge;
+        stage = 2;
+      } else {
+        bhi = xb;
+        nge_hi = nge;
+        // secant step x' = sum_{S<x} / (s - #{S >= x}), aimed 2^-12 low so
+        // that the test at x' is decided by the fp64 margin
+        const float xn = (float)(slt / (double)mult * (1.0 - 0x1p-12));
+        unsigned xnb = xn < x ? __builtin_bit_cast(unsigned, xn) : xb - 1u;
+        xnb = max(blo + 1u, xnb);
+        if (--secant_left > 0 && xnb > blo && xnb < bhi) {
+          x = __builtin_bit_cast(float, xnb);
+          continue;
+        }
+        stage = 2;
+      }
+    } else {  // stage 2: x was a bisection point
+      if (holds) {
+        blo = xb;
+        nge_lo = nge;
+      } else {
+        bhi = xb;
+        nge_hi = nge;
+      }
+    }
+    // stage 2: few enough values left inside the bracket to resolve them
+    // directly (below), else the next bisection point, or done
+    if (stage == 2 && nge_lo > nge_hi && nge_lo - nge_hi <= MCAP) {
+      collect = true;
+      stage = 3;
+      continue;
+    }
+    if (bhi - blo > 1 && nge_lo > nge_hi) {
+      x = __builtin_bit_cast(float, blo + (bhi - blo) / 2);
+      continue;
+    }
+    xstar = __builtin_bit_cast(float, blo);
+    stage = 3;
+  }
+
+  // T_r = sum_{S <= x*} correctly rounded, r = #{S > x*}
+  double thi, tlo;
+  double E;  // bound on |exact sum - (thi + tlo)|
+  if (collect) {
+    // The bracket (blo, bhi) holds m <= MCAP row values (at most
+    // nge_lo - nge_hi).  One pass sums
+    // {S <= blo} and collects them; cond is then taken at each collected
+    // value v (nge(v) = nge_hi + #{collected >= v}, slt(v) = sum_{S <= blo}
+    // + sum of collected values below v) with the certified double-double
+    // margin, and x* is the largest value where it holds (blo if none).
+    // cond is monotone, so this is the partition the bisection would find.
+    const float flo = __builtin_bit_cast(float, blo), fhi = __builtin_bit_cast(float, bhi);
+    if (t == 0) sh.ncol = 0;
+    __syncthreads();
+    double shi, slo;
+    dd_sum_collect(sh, row, flo, fhi, shi, slo, ph);
+    // the values actually collected: nge_lo - nge_hi can count more (it
+    // counts the values equal to blo too)
+    const int m = min(sh.ncol, MCAP);
+    const double mrel = dd_rel + 0x1p-90;  // the sum plus up to MCAP exact-rounded terms
+    if (t < 64) {
+      const float v = t < m ? sh.col[t] : 0.f;
+      double bh = 0.0, bl = 0.0;  // collected values below v
+      long long ge = 0;           // collected values >= v
+      for (int j = 0; j < m; ++j) {
+        const float u = sh.col[j];
+        if (u < v) {
+          double s2, e;
+          two_sum(bh, (double)u, s2, e);
+          bh = s2;
+          bl += e;
+        } else {
+          ++ge;
+        }
+      }
+      if (t < m) {
+        int st = 1;
+        const long long mult = (long long)s - nge_hi - ge;
+        if (mult > 0) {
+          double rh = shi, rl = slo;
+          dd_add(rh, rl, bh, bl);
+          const double lhs = (double)mult * (double)v;  // exact
+          double p, q;
+          two_sum(lhs, -rh, p, q);
+          const double d = p + (q - rl);
+          const double margin = mrel * rh + 0x1p-100 * (lhs + rh);
+          st = d > margin ? 0 : (d < -margin ? 1 : 2);
+        }
+        sh.cstat[t] = st;
+      }
+    }
+    __syncthreads();
+    // certain bounds, then any undecided values between them in ascending
+    // order, each decided exactly (every thread takes the same steps)
+    float vt = flo, vf = fhi;
+    for (int j = 0; j < m; ++j) {
+      const float u = sh.col[j];
+      const int st = sh.cstat[j];
+      if (st == 1 && u > vt) vt = u;
+      if (st == 0 && u < vf) vf = u;
+    }
+    for (;;) {
+      float nxt = vf;
+      for (int j = 0; j < m; ++j) {
+        const float u = sh.col[j];
+        if (sh.cstat[j] == 2 && u > vt && u < nxt) nxt = u;
+      }
+      if (!(nxt < vf)) break;
+      long long ge = nge_hi;
+      for (int j = 0; j < m; ++j) ge += sh.col[j] >= nxt ? 1 : 0;
+      const long long mult = (long long)s - ge;
+      bool holds = true;
+      if (mult > 0) {
+        exact_sum(sh, row, nxt, true, dlo, dhi);
+        uint64_t ldig[NDIG + 1];
+        scaled_to_digits((unsigned long long)mult, nxt, ldig);
+        holds = digits_ge(sh.total, ldig);
+      }
+      if (!holds) break;
+      vt = nxt;
+    }
+    xstar = vt;
+    nsat = nge_hi;
+    thi = shi;
+    tlo = slo;
+    for (int j = 0; j < m; ++j) {
+      const float u = sh.col[j];
+      if (u > xstar) {
+        ++nsat;
+      } else {
+        double s2, e;
+        two_sum(thi, (double)u, s2, e);
+        thi = s2;
+        tlo += e;
+      }
+    }
+    const double n2 = thi + tlo;
+    tlo = tlo - (n2 - thi);
+    thi = n2;
+    E = mrel * thi;
+  } else {
+    dd_sum(sh, row, xstar, false, thi, tlo, nsat, ph);
+    E = dd_rel * thi;
+  }
+  {
+    // thi = RN(thi + tlo); the exact sum lies within E of thi + tlo.  It
+    // rounds to thi when that interval stays strictly inside thi's rounding
+    // interval (half an ulp above, half the ulp below under it).
+    const unsigned long long tb = __builtin_bit_cast(unsigned long long, thi);
+    const double up = __builtin_bit_cast(double, tb + 1ull) - thi;
+    const double down = thi > 0.0 ? thi - __builtin_bit_cast(double, tb - 1ull) : up;
+    if (tlo + E < 0.5 * up && tlo - E > -0.5 * down) {
+      Tr = thi;
+    } else {
+      exact_sum(sh, row, xstar, false, dlo, dhi);
+      if (t == 0) sh.bcast_d = digits_to_double(sh.total);
+      __syncthreads();
+      Tr = sh.bcast_d;
+    }
+  }
 }
 
 template <bool IN_LDS>
@@ -573,256 +917,10 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
     return;
   }
 
-  // cond(x): (s - #{S >= x}) x <= sum_{S < x} S, decided with a certified
-  // fp64 margin or, inside the margin, from a double-double sum and, if
-  // even that cannot decide, exactly.  The search visits one point per
-  // iteration (a single evaluation site keeps the register footprint of
-  // the unrolled row passes small):
-  //   stage 0  x = max S           (true: no saturated block); needed only
-  //            when max S <= T / s, since cond(x) fails for every x > T / s
-  //   stage 1  secant steps down from T / s towards the threshold
-  //   stage 2  bisection of [blo, bhi) until no row value lies inside
-  // per-thread fp32 partial sums (chunk terms) then an fp64 reduction
   const int chunk = ((M + PT - 1) / PT + 3) & ~3;
-  const double err_bound = (ldexp((double)(chunk + 2), -23) + ldexp((double)(M + 2 * PT), -50)) * tot;
-  const double dd_rel = ldexp((double)chunk * (double)chunk + 64.0, -104) * 2.0;  // safety x2
-  const int dlo = digit_of(mnpos), dhi = digit_of(mx) + 1;
-  const float fmx = __builtin_bit_cast(float, mx);
-  unsigned blo = mnpos, bhi = mx;
-  long long ngt_lo = npos, nge_hi = 0;
-  float x = fmx;
-  int stage = 0, secant_left = 12, ph = 0;
-  float xstar = fmx;
-  {
-    const float x0 = (float)(tot / (double)s * (1.0 + 0x1p-20));  // above T / s
-    if (x0 < fmx && __builtin_bit_cast(unsigned, x0) > blo) {
-      x = x0;
-      stage = 1;
-    }
-  }
-  bool collect = false;
-  while (stage != 3) {
-    // ---- one pass at x
-    bool holds = true;
-    long long cnt = 0;
-    double slt = 0.0;
-    {
-      int cge = 0, cgt = 0;
-      float sf = 0.f;
-      row.each([&](int, float v) {
-        const bool ge = v >= x;
-        cge += ge ? 1 : 0;
-        cgt += v > x ? 1 : 0;
-        sf += ge ? 0.f : v;
-      });
-      cnt = ((long long)cge << 32) | (long long)cgt;
-      slt = (double)sf;
-      block_reduce(sh, cnt, slt, ph);
-    }
-    const long long nge = cnt >> 32, ngt = cnt & 0xffffffffll;
-    const long long mult = (long long)s - nge;
-    if (mult > 0) {
-      const double lhs = (double)mult * (double)x;  // exact: < 2^21 times a 24-bit value
-      const double diff = lhs - slt;
-      if (diff > err_bound) {
-        holds = false;
-      } else if (!(diff < -err_bound)) {
-        // inside the margin: double-double sum of {S < x}
-        double thi, tlo;
-        long long unused;
-        dd_sum(sh, row, x, true, thi, tlo, unused, ph);
-        double p, q;
-        two_sum(lhs, -thi, p, q);  // lhs - thi = p + q exactly
-        const double d = p + (q - tlo);
-        const double margin = dd_rel * thi + 0x1p-100 * (lhs + thi);
-        if (d > margin) {
-          holds = false;
-        } else if (!(d < -margin)) {
-          exact_sum(sh, row, x, true, dlo, dhi);
-          uint64_t ldig[NDIG + 1];
-          scaled_to_digits((unsigned long long)mult, x, ldig);
-          holds = digits_ge(sh.total, ldig);
-        }
-      }
-    }
-    // ---- advance the search
-    const unsigned xb = __builtin_bit_cast(unsigned, x);
-    if (stage == 0) {
-      if (holds) {  // no saturated block: x* = max S
-        xstar = x;
-        stage = 3;
-        continue;
-      }
-      nge_hi = nge;
-      stage = 1;
-      x = fminf(fmx, (float)(tot / (double)s * (1.0 + 0x1p-20)));  // x > T/s never holds
-      if (!(__builtin_bit_cast(unsigned, x) > blo && __builtin_bit_cast(unsigned, x) < bhi)) stage = 2;
-      else continue;
-    } else if (stage == 1) {
-      if (holds) {
-        blo = xb;
-        ngt_lo = ngt;
-        stage = 2;
-      } else {
-        bhi = xb;
-        nge_hi = nge;
-        // secant step x' = sum_{S<x} / (s - #{S >= x}), aimed 2^-12 low so
-        // that the test at x' is decided by the fp64 margin
-        const float xn = (float)(slt / (double)mult * (1.0 - 0x1p-12));
-        unsigned xnb = xn < x ? __builtin_bit_cast(unsigned, xn) : xb - 1u;
-        xnb = max(blo + 1u, xnb);
-        if (--secant_left > 0 && xnb > blo && xnb < bhi) {
-          x = __builtin_bit_cast(float, xnb);
-          continue;
-        }
-        stage = 2;
-      }
-    } else {  // stage 2: x was a bisection point
-      if (holds) {
-        blo = xb;
-        ngt_lo = ngt;
-      } else {
-        bhi = xb;
-        nge_hi = nge;
-      }
-    }
-    // stage 2: few enough values left inside the bracket to resolve them
-    // directly (below), else the next bisection point, or done
-    if (stage == 2 && ngt_lo > nge_hi && ngt_lo - nge_hi <= MCAP) {
-      collect = true;
-      stage = 3;
-      continue;
-    }
-    if (bhi - blo > 1 && ngt_lo > nge_hi) {
-      x = __builtin_bit_cast(float, blo + (bhi - blo) / 2);
-      continue;
-    }
-    xstar = __builtin_bit_cast(float, blo);
-    stage = 3;
-  }
-
-  // T_r = sum_{S <= x*} correctly rounded, r = #{S > x*}
   long long nsat;
   double Tr;
-  double thi, tlo;
-  double E;  // bound on |exact sum - (thi + tlo)|
-  if (collect) {
-    // The bracket (blo, bhi) holds m <= MCAP row values (at most
-    // ngt_lo - nge_hi).  One pass sums
-    // {S <= blo} and collects them; cond is then taken at each collected
-    // value v (nge(v) = nge_hi + #{collected >= v}, slt(v) = sum_{S <= blo}
-    // + sum of collected values below v) with the certified double-double
-    // margin, and x* is the largest value where it holds (blo if none).
-    // cond is monotone, so this is the partition the bisection would find.
-    const float flo = __builtin_bit_cast(float, blo), fhi = __builtin_bit_cast(float, bhi);
-    if (t == 0) sh.ncol = 0;
-    __syncthreads();
-    double shi, slo;
-    dd_sum_collect(sh, row, flo, fhi, shi, slo, ph);
-    // the values actually collected: ngt_lo - nge_hi can count more (its
-    // starting value counts the smallest positive values too)
-    const int m = min(sh.ncol, MCAP);
-    const double mrel = dd_rel + 0x1p-90;  // the sum plus up to MCAP exact-rounded terms
-    if (t < 64) {
-      const float v = t < m ? sh.col[t] : 0.f;
-      double bh = 0.0, bl = 0.0;  // collected values below v
-      long long ge = 0;           // collected values >= v
-      for (int j = 0; j < m; ++j) {
-        const float u = sh.col[j];
-        if (u < v) {
-          double s2, e;
-          two_sum(bh, (double)u, s2, e);
-          bh = s2;
-          bl += e;
-        } else {
-          ++ge;
-        }
-      }
-      if (t < m) {
-        int st = 1;
-        const long long mult = (long long)s - nge_hi - ge;
-        if (mult > 0) {
-          double rh = shi, rl = slo;
-          dd_add(rh, rl, bh, bl);
-          const double lhs = (double)mult * (double)v;  // exact
-          double p, q;
-          two_sum(lhs, -rh, p, q);
-          const double d = p + (q - rl);
-          const double margin = mrel * rh + 0x1p-100 * (lhs + rh);
-          st = d > margin ? 0 : (d < -margin ? 1 : 2);
-        }
-        sh.cstat[t] = st;
-      }
-    }
-    __syncthreads();
-    // certain bounds, then any undecided values between them in ascending
-    // order, each decided exactly (every thread takes the same steps)
-    float vt = flo, vf = fhi;
-    for (int j = 0; j < m; ++j) {
-      const float u = sh.col[j];
-      const int st = sh.cstat[j];
-      if (st == 1 && u > vt) vt = u;
-      if (st == 0 && u < vf) vf = u;
-    }
-    for (;;) {
-      float nxt = vf;
-      for (int j = 0; j < m; ++j) {
-        const float u = sh.col[j];
-        if (sh.cstat[j] == 2 && u > vt && u < nxt) nxt = u;
-      }
-      if (!(nxt < vf)) break;
-      long long ge = nge_hi;
-      for (int j = 0; j < m; ++j) ge += sh.col[j] >= nxt ? 1 : 0;
-      const long long mult = (long long)s - ge;
-      bool holds = true;
-      if (mult > 0) {
-        exact_sum(sh, row, nxt, true, dlo, dhi);
-        uint64_t ldig[NDIG + 1];
-        scaled_to_digits((unsigned long long)mult, nxt, ldig);
-        holds = digits_ge(sh.total, ldig);
-      }
-      if (!holds) break;
-      vt = nxt;
-    }
-    xstar = vt;
-    nsat = nge_hi;
-    thi = shi;
-    tlo = slo;
-    for (int j = 0; j < m; ++j) {
-      const float u = sh.col[j];
-      if (u > xstar) {
-        ++nsat;
-      } else {
-        double s2, e;
-        two_sum(thi, (double)u, s2, e);
-        thi = s2;
-        tlo += e;
-      }
-    }
-    const double n2 = thi + tlo;
-    tlo = tlo - (n2 - thi);
-    thi = n2;
-    E = mrel * thi;
-  } else {
-    dd_sum(sh, row, xstar, false, thi, tlo, nsat, ph);
-    E = dd_rel * thi;
-  }
-  {
-    // thi = RN(thi + tlo); the exact sum lies within E of thi + tlo.  It
-    // rounds to thi when that interval stays strictly inside thi's rounding
-    // interval (half an ulp above, half the ulp below under it).
-    const unsigned long long tb = __builtin_bit_cast(unsigned long long, thi);
-    const double up = __builtin_bit_cast(double, tb + 1ull) - thi;
-    const double down = thi > 0.0 ? thi - __builtin_bit_cast(double, tb - 1ull) : up;
-    if (tlo + E < 0.5 * up && tlo - E > -0.5 * down) {
-      Tr = thi;
-    } else {
-      exact_sum(sh, row, xstar, false, dlo, dhi);
-      if (t == 0) sh.bcast_d = digits_to_double(sh.total);
-      __syncthreads();
-      Tr = sh.bcast_d;
-    }
-  }
+  sip_threshold<PT>(sh, row, M, s, npos, mx, mnpos, tot, chunk, nsat, Tr);
   const double lam = (double)(s - nsat) / Tr;
 
   const uint64_t U = a.offsets ? a.offsets[r] : offset_of_row(a.seed, r);
@@ -880,6 +978,138 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
   }
 }
 
+// SIP plan of rows that fit 256 CH - 3 values, the row in registers (no
+// LDS copy, no LDS reads; only the reductions use LDS, so several rows run
+// per CU).  The same definition as plan_kernel (the threshold search is the
+// same function), with two leaner sampling passes:
+//   * sum pass: Pi_j = floor(min(2^44, lambda 2^44 S_j)) summed per thread
+//     in fp64, exact (at most 120 terms below 2^44 stay below 2^52);
+//   * draw pass: with C0 the exclusive prefix of the thread's chunk and the
+//     first sampling point at or above it at C0 + R (R < 2^44 + 2^44,
+//     exact in fp64), block j is drawn when R < L_j, the chunk-local prefix
+//     after it; then R grows by 2^44 (one point per block at most, since
+//     Pi_j <= 2^44), or becomes infinite after the s-th point.
+// Rows in flight per CU for a chunk of CH values (the register budget).
+constexpr int sip_rows_per_cu(int ch) { return ch <= 32 ? 4 : (ch <= 80 ? 3 : 2); }
+
+template <int CH>
+__global__ __launch_bounds__(256, sip_rows_per_cu(CH)) void sip_reg_kernel(PlanArgs a) {
+  constexpr int PTR = 256;
+  __shared__ SharedT<PTR / 64> sh;
+  const int t = threadIdx.x;
+  const size_t r = blockIdx.x;
+  const int M = a.M, s = a.budget;
+  int32_t *out_idx = a.idx + r * (size_t)s;
+  float *out_bias = a.bias ? a.bias + r * (size_t)s : nullptr;
+  const float *grow = a.scores + r * (size_t)M;
+  RegRow<CH> row;
+  row.init(grow, M);
+
+  // ---- validity (NaN, infinities, negative values), positives, extremes,
+  // approximate total
+  int mypos = 0, bad = 0;
+  float mxf = 0.f, mnf = __builtin_inff();
+  double tot = 0.0;
+  row.each([&](int, float v) {
+    bad |= (v < 0.f || !(v <= 3.40282347e38f)) ? 1 : 0;
+    const bool pos = v > 0.f;
+    mypos += pos ? 1 : 0;
+    mxf = fmaxf(mxf, v);
+    mnf = pos ? fminf(mnf, v) : mnf;
+    tot += (double)v;
+  });
+  const long long pk = block_sum_l(sh, ((long long)bad << 32) | (long long)mypos);
+  const long long nbad = pk >> 32;
+  long long npos = pk & 0xffffffffll;
+  tot = block_sum_d(sh, tot);
+  unsigned mx = __builtin_bit_cast(unsigned, mxf), mnpos = __builtin_bit_cast(unsigned, mnf);
+  block_minmax_u(sh, mnpos, mx);
+
+  auto fill_rest = [&](int from) {
+    for (int e = from + t; e < s; e += PTR) {
+      out_idx[e] = -1;
+      if (out_bias) out_bias[e] = 0.f;
+    }
+  };
+  if (nbad) {
+    fill_rest(0);
+    if (t == 0) {
+      a.count[r] = -1;
+      if (a.lambda) a.lambda[r] = __builtin_nan("");
+      if (a.status) *a.status = BSA_ERR_NONFINITE;  // every writer stores the same value
+    }
+    return;
+  }
+  if (npos <= s) {  // every positive block, pi = 1
+    uint64_t total;
+    uint64_t pos = block_exscan_u64(sh, (uint64_t)mypos, total);
+    row.each([&](int j, float x) {
+      if (x > 0.f) {
+        out_idx[pos] = j;
+        if (out_bias) out_bias[pos] = 0.f;
+        ++pos;
+      }
+    });
+    fill_rest((int)npos);
+    if (t == 0) {
+      a.count[r] = (int)npos;
+      if (a.lambda) a.lambda[r] = __builtin_inf();
+    }
+    return;
+  }
+
+  long long nsat;
+  double Tr;
+  sip_threshold<PTR>(sh, row, M, s, npos, mx, mnpos, tot, CH, nsat, Tr);
+  const double lam = (double)(s - nsat) / Tr;
+  const uint64_t U = a.offsets ? a.offsets[r] : offset_of_row(a.seed, r);
+  const double lam44 = lam * (double)UNIT;  // exact: a power-of-two scaling
+  double mysum = 0.0;
+  row.template each_seq<8>([&](int, float v) {
+    mysum += __builtin_floor(fmin((double)UNIT, lam44 * (double)v));
+  });
+  uint64_t total;
+  const uint64_t C0 = block_exscan_u64(sh, (uint64_t)mysum, total);
+  auto below = [&](uint64_t c) -> uint64_t {  // points U + k 2^44 (k < s) below c
+    if (c <= U) return 0;
+    const uint64_t n = ((c - U - 1) >> 44) + 1;
+    return n < (uint64_t)s ? n : (uint64_t)s;
+  };
+  const int drawn = (int)below(total);
+  int q = (int)below(C0);  // points below the chunk: the next one is number q
+  double R = q < s ? (double)((long long)q * (long long)UNIT - ((long long)C0 - (long long)U))
+                   : __builtin_inf();
+  double L = 0.0;
+  row.template each_seq<8>([&](int j, float v) {
+    L += __builtin_floor(fmin((double)UNIT, lam44 * (double)v));
+    if (R < L) {
+      out_idx[q] = j;
+      if (out_bias) out_bias[q] = v;  // the score, turned into its shift below
+      ++q;
+      R = q < s ? R + (double)UNIT : __builtin_inf();
+    }
+  });
+  if (out_bias) {
+    // shifts -ln pi of the drawn blocks, from the scores parked in their
+    // slots (written by this workgroup before the barrier)
+    __syncthreads();
+    constexpr int UB = 8;  // all of a thread's loads (budgets to 2048) before the first wait
+    for (int e0 = t; e0 < drawn; e0 += UB * PTR) {
+      float vv[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) vv[u] = e0 + u * PTR < drawn ? out_bias[e0 + u * PTR] : 1.f;
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        if (e0 + u * PTR < drawn) out_bias[e0 + u * PTR] = (float)(-log(fmin(1.0, lam * (double)vv[u])));
+    }
+  }
+  fill_rest(drawn);
+  if (t == 0) {
+    a.count[r] = drawn;
+    if (a.lambda) a.lambda[r] = lam;
+  }
+}
+
 __global__ void status_init_kernel(int32_t *status) { *status = BSA_OK; }
 
 }  // namespace
@@ -900,7 +1130,16 @@ int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, i
     return BSA_ERR_HIP;
   const size_t base = (sizeof(Shared) + 15) & ~(size_t)15;
   const size_t with_row = base + (size_t)(M + 4) * sizeof(float);
-  if (with_row <= (size_t)max_lds)
+  // SIP rows that fit a register-resident instance (the row's start may sit
+  // up to 3 floats past a 16-byte boundary)
+  const long long span = (long long)M + 3;
+  if (mode == BSA_PLAN_SIP && span <= 256 * 32)
+    hipLaunchKernelGGL(sip_reg_kernel<32>, dim3(rows), dim3(256), 0, stream, a);
+  else if (mode == BSA_PLAN_SIP && span <= 256 * 80)
+    hipLaunchKernelGGL(sip_reg_kernel<80>, dim3(rows), dim3(256), 0, stream, a);
+  else if (mode == BSA_PLAN_SIP && span <= 256 * 120)
+    hipLaunchKernelGGL(sip_reg_kernel<120>, dim3(rows), dim3(256), 0, stream, a);
+  else if (with_row <= (size_t)max_lds)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(rows), dim3(PT), with_row, stream, a);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(rows), dim3(PT), base, stream, a);
