@@ -231,7 +231,21 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
       if (m == 0) continue;  // empty cluster keeps its centroid
       float acc = 0.f;
       const int o = off[c];
-      for (int i = 0; i < m; ++i) acc = __fadd_rn(acc, q_at(order[o + i], dim));
+      // members fetched 8 at a time (their row indices, then their values),
+      // so the chain waits for LDS twice per 8 adds; the adds keep the
+      // ascending member order
+      int i = 0;
+      for (; i + 8 <= m; i += 8) {
+        int rr[8];
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rr[u] = order[o + i + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = q_at(rr[u], dim);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = __fadd_rn(acc, x[u]);
+      }
+      for (; i < m; ++i) acc = __fadd_rn(acc, q_at(order[o + i], dim));
       mu[c * D + dim] = __fdiv_rn(acc, (float)m);
     }
     __syncthreads();
@@ -244,23 +258,38 @@ __global__ __launch_bounds__(256) void kmeans_kernel(SelArgs a) {
     float best = __builtin_inff();
     int bc = 1 << 30;
     if (r < n) {
-      for (int c = par; c < C; c += 2) {
-        if (!active[c]) continue;
-        float dd = 0.f;
-        for (int k0 = 0; k0 < D; k0 += 8) {
-          const u32x4 qv = *(const u32x4 *)&qb16[r * QS + k0];
+      // this thread's clusters c = par, par + 2, .. side by side: one
+      // independent chain each (dims ascending), sharing the query loads
+      constexpr int NJ = CMAX / 2;
+      float dd[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) dd[j] = 0.f;
+      for (int k0 = 0; k0 < D; k0 += 8) {
+        const u32x4 qv = *(const u32x4 *)&qb16[r * QS + k0];
+        float qx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned word = qv[e >> 1];
+          qx[e] = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = par + 2 * j;
+          if (c >= C) break;  // uniform
           const f32x4 m0 = *(const f32x4 *)&mu[c * D + k0];
           const f32x4 m1 = *(const f32x4 *)&mu[c * D + k0 + 4];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const unsigned word = qv[e >> 1];
-            const float qx = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
-            const float df = __fsub_rn(qx, e < 4 ? m0[e] : m1[e - 4]);
-            dd = __fadd_rn(dd, __fmul_rn(df, df));
+            const float df = __fsub_rn(qx[e], e < 4 ? m0[e] : m1[e - 4]);
+            dd[j] = __fadd_rn(dd[j], __fmul_rn(df, df));
           }
         }
-        if (dd < best) {
-          best = dd;
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = par + 2 * j;
+        if (c < C && active[c] && dd[j] < best) {
+          best = dd[j];
           bc = c;
         }
       }
