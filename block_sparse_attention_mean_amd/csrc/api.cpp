@@ -151,6 +151,7 @@ int bsa_select_scores(const void *q, const void *k, int B, int H, int N, int d, 
   const long long M = (N + kv_block - 1) / kv_block;
   if ((long long)B * H * nqb * n_clusters > kMaxIndex) return BSA_ERR_SIZE;
   if ((long long)B * H * M > kMaxIndex) return BSA_ERR_SIZE;
+  if (nqb * M > 0xffffffffLL) return BSA_ERR_SIZE;  // one head's scores, 32-bit offsets
   const size_t need = bsa::select_workspace_bytes(B, H, N, d, kv_block, n_clusters);
   if (!workspace || workspace_bytes < need) return BSA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;

@@ -12,16 +12,17 @@
 //   pool_split  one workgroup per 32 KV blocks (one key tile of the GEMM):
 //               fp32 mean of each block's keys, then a split into two fp16
 //               halves at one power-of-two scale per tile
-//               (x 2^e = hi + lo 2^-11, |x 2^e| < 2^11) so the GEMM below is
-//               fp32-accurate on fp16 matrix cores;
+//               (x 2^e = hi + lo, |x 2^e| < 2^11, lo the fp16 rounding of
+//               the remainder) so the GEMM below is fp32-accurate on fp16
+//               matrix cores;
 //   kmeans      one workgroup per query block; fp32 in a fixed operation
 //               order (ascending-row member sums, IEEE division, distances
 //               summed over ascending dims without fused multiply-add) --
 //               its assignments are discrete decisions and must be
 //               reproducible bit for bit;
-//   score<0>    sweep 1 of pooled keys x centroids (3 fp16 MFMA per product:
-//               hi.hi + (hi.lo + lo.hi) 2^-11): per-row running max and sum
-//               of 2^(logit log2 e), per column chunk;
+//   score<0>    sweep 1 of pooled keys x centroids (3 fp16 MFMA per product,
+//               hi.lo + hi.hi + lo.hi, into one fp32 accumulator): per-row
+//               running max and sum of 2^(logit log2 e), per column chunk;
 //   score<1>    sweep 2: merges the chunk statistics into a per-row offset
 //               beta = max + log2(sum) - log2(share), recomputes the same
 //               logits bit for bit and writes S_ij = sum_c 2^(t_cj - beta_c)
@@ -47,11 +48,15 @@ struct SelArgs {
   float scale_log2;
 };
 
-// Split x (one row, this lane's share) at a row scale 2^e.
+// Split x (one row, this lane's share) at a row scale 2^e: x 2^e = hi + r
+// exactly in fp32, and lo = fp16(r).  With |x 2^e| < 2^11, |r| <= 1/2 ulp
+// of hi keeps 11 bits in lo down to |x 2^e| ~ 2^-3 (2^-13 of the row's
+// largest value); below that r is an fp16 subnormal, with an absolute error
+// under 2^-25 that the dot products cannot see.
 __device__ __forceinline__ void split_f16(float x, int e, half_t &hi, half_t &lo) {
   const float sc = ldexpf(x, e);
   hi = (half_t)sc;
-  lo = (half_t)((sc - (float)hi) * 2048.f);
+  lo = (half_t)(sc - (float)hi);
 }
 
 __device__ __forceinline__ int row_exponent(float amax) {
@@ -345,6 +350,16 @@ __device__ __forceinline__ float add_shr(float x) {
   return x + __builtin_bit_cast(float, y);
 }
 
+// The lane's index, recomputed where it is used (two ALU instructions):
+// values derived from it and kept live through the key loop would take
+// registers the products need, or be spilled and reloaded behind a wait on
+// every outstanding load.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that a
 // contiguous range of logical ids (the row tiles sharing one key chunk) runs
 // on one XCD and its L2.
@@ -360,7 +375,7 @@ __device__ __forceinline__ int xcd_order(int L, int total) {
 // its 64 centroid rows (two 32-row sub-tiles) split in registers as the B
 // operand.  Lane l then owns centroid row l % 32 of each sub-tile and 16 of
 // the 32 keys of a step, so the row statistics are two registers.
-template <int D, int PASS>
+template <int D, int PASS, int CL>
 __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   constexpr int KS = D / 16;
   constexpr int CT = 32;               // keys per step
@@ -372,8 +387,9 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   constexpr int LOADS = 2 * CT / RPI;  // wave loads per step (hi + lo)
   constexpr int LPW = LOADS / 4;       // per wave
   static_assert(LPW >= 1 && LOADS % 4 == 0, "step shape");
-  __shared__ __attribute__((aligned(16))) unsigned char h0[TB], l0[TB], h1[TB], l1[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char h2[TB], l2[TB], h3[TB], l3[TB];
+  // the ring, one array: slot S holds the hi tile at 2 S TB and the lo tile
+  // at (2 S + 1) TB, so both offsets fold into the LDS instructions
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * NB * TB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,19 +411,14 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   typedef const __attribute__((address_space(4))) float cfloat_t;
   cfloat_t *kcs = (cfloat_t *)(a.kb_cs + (size_t)bh * a.ktiles + cbeg / CT);
 
-  auto hslot = [&](auto c) -> unsigned char * {
-    constexpr int S = decltype(c)::value;
-    return S == 0 ? h0 : S == 1 ? h1 : S == 2 ? h2 : h3;
-  };
-  auto lslot = [&](auto c) -> unsigned char * {
-    constexpr int S = decltype(c)::value;
-    return S == 0 ? l0 : S == 1 ? l1 : S == 2 ? l2 : l3;
-  };
+  auto hslot = [&](auto c) -> unsigned char * { return ring + 2 * decltype(c)::value * TB; };
+  auto lslot = [&](auto c) -> unsigned char * { return ring + (2 * decltype(c)::value + 1) * TB; };
 
   // gather of step k into slot S: wave loads u = wave * LPW + j, each lane
   // one 16-byte chunk at a fixed offset inside the 32-key tile.  Keys past
   // the chunk end (ragged last step) read the next rows or the 32-row pad
   // after the split arrays and are masked in the epilogue.
+  const unsigned rd_base = (unsigned)(l32 * ROWB + ((hh ^ swz_k<D>(l32)) << 4));
   unsigned koff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
@@ -424,7 +435,12 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
       const int u = wave * LPW + j;
       const bool hi = u < LOADS / 2;
       const int dst = (u % (LOADS / 2)) * RPI * ROWB;  // wave-uniform
-      __builtin_amdgcn_global_load_lds((const void *)((hi ? khi : klo) + tile_off + koff[j]),
+      // the empty asm keeps the lane offset a 32-bit register added to a
+      // scalar base at each load, instead of a 64-bit address per load
+      // hoisted out of the loop (registers the products need)
+      unsigned o = koff[j];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds((const void *)((hi ? khi : klo) + tile_off + o),
                                        (lds_void_t *)((hi ? ht : lt) + dst), 16, 0, 0);
     }
   };
@@ -489,103 +505,176 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
     }
   }
 
-  // logits of sub-tile u at step k -> statistics (sweep 1) or scores (sweep 2).
-  // Register r holds key 8 (r / 4) + 4 hh + r % 4 of the step.
-  auto epilogue = [&](const f32x16 &acc0, const f32x16 &acc1, float f, int k, int u) {
-    float v[16];
+  // Consecutive steps are software-pipelined: the products of step k + 1
+  // run while the epilogue of step k (its statistics or scores) runs in the
+  // same wave, slice by slice, so that the vector work issues under the
+  // matrix work.  The two steps' accumulators alternate between acc[0] and
+  // acc[1].  Every value keeps the operation order of an unpipelined step,
+  // so the results do not depend on this schedule.
+  f32x16 acc[2][2];                            // [step parity][sub-tile]
+  float *const sc_bh = a.scores + (size_t)bh * a.nqb * M;
+  float ep_mx[2], ep_mn[2], ep_z[2];           // sweep-1 epilogue in flight
+
+  // Epilogue slice j (of KS) of the step k held in acc[P] (key-tile scale
+  // cs), in place.  Register r holds key 8 (r / 4) + 4 hh + r % 4 of the
+  // step; sub-tile u holds centroid rows rho0 + 32 u + l32.
+  auto epi = [&](auto p_c, int k, int j, float cs) {
+    constexpr int P = decltype(p_c)::value;
+    const bool ragged = cbeg + k * CT + CT > cend;
+    if (j == 0 && ragged) {
+      // the last step of the row's last chunk: keys at or past cend (the
+      // next head's rows or the pad) get logit -inf.  The empty asm keeps
+      // this a branch: flattened, it would cost every step two selects per
+      // value.
+      const int lim = cend - (cbeg + k * CT + 4 * (fresh_lane() >> 5));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = __builtin_fmaf(acc1[r], 0x1p-11f, acc0[r]);
-    const int c0 = cbeg + k * CT + 4 * hh;  // key of register 0
-    if (cbeg + k * CT + CT > cend) {       // ragged last step of the chunk
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = c0 + 8 * (r >> 2) + (r & 3) < cend ? v[r] : -__builtin_inff();
+        for (int r = 0; r < 16; ++r)
+          acc[P][u][r] = 8 * (r >> 2) + (r & 3) < lim ? acc[P][u][r] : -__builtin_inff();
     }
-    if (PASS == 0) {
-      float mx = v[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, v[r]);
-      const float mnew = fmaxf(st_m[u], mx * f);  // f > 0
-      float z = st_z[u] * __builtin_amdgcn_exp2f(st_m[u] - mnew);
+    for (int u = 0; u < 2; ++u) {
+      const float f = rs[u] * cs;  // > 0
+      if (PASS == 0) {
+        // slices 0 .. KS/2 - 1: the maximum; the rest: the sum
+        constexpr int HS = KS / 2, PE = 16 / HS;
+        if (j < HS) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], f, -mnew));
-      st_m[u] = mnew;
-      st_z[u] = z;
-    } else {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r], f, -st_m[u]));
-      // a query block's C clusters are C consecutive lanes: prefix sums
-      // inside rows of 16 lanes leave each block's total in its last lane
-      if (C >= 2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = add_shr<1>(e[r]);
-      }
-      if (C >= 4) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = add_shr<2>(e[r]);
-      }
-      if (C >= 8) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = add_shr<4>(e[r]);
-      }
-      if (C >= 16) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = add_shr<8>(e[r]);
-      }
-      const int rho = rho0 + 32 * u + l32;
-      if ((l32 & (C - 1)) == C - 1 && rho < R) {
-        float *dst = a.scores + ((size_t)bh * a.nqb + rho / C) * M;
-        if (c0 - 4 * hh + CT <= cend && (M & 3) == 0) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *(f32x4 *)(dst + c0 + 8 * g) = (f32x4){e[4 * g], e[4 * g + 1], e[4 * g + 2], e[4 * g + 3]};
+          for (int e = 0; e < PE; ++e) {
+            const int r = j * PE + e;
+            ep_mx[u] = r == 0 ? acc[P][u][r] : fmaxf(ep_mx[u], acc[P][u][r]);
+          }
+          if (j == HS - 1) {
+            ep_mn[u] = fmaxf(st_m[u], ep_mx[u] * f);
+            ep_z[u] = st_z[u] * __builtin_amdgcn_exp2f(st_m[u] - ep_mn[u]);
+          }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int col = c0 + 8 * (r >> 2) + (r & 3);
-            if (col < cend) dst[col] = e[r];
+          for (int e = 0; e < PE; ++e) {
+            const int r = (j - HS) * PE + e;
+            ep_z[u] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[P][u][r], f, -ep_mn[u]));
+          }
+          if (j == KS - 1) {
+            st_m[u] = ep_mn[u];
+            st_z[u] = ep_z[u];
+          }
+        }
+      } else {
+        constexpr int PE = 16 / KS;
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+          const int r = j * PE + e;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[P][u][r], f, -st_m[u]));
+          // a query block's C clusters are C consecutive lanes: prefix sums
+          // inside rows of 16 lanes leave each block's total in its last lane
+          if (CL >= 1) x = add_shr<1>(x);
+          if (CL >= 2) x = add_shr<2>(x);
+          if (CL >= 3) x = add_shr<4>(x);
+          if (CL >= 4) x = add_shr<8>(x);
+          acc[P][u][r] = x;
+        }
+        if (j == KS - 1) {
+          // the lane's row, its store offset and the condition are formed
+          // here from the lane index; the head's scores come from a scalar
+          // base plus a 32-bit element offset (a head holds fewer than 2^32
+          // scores)
+          const int ln = fresh_lane(), lw = ln & 31;
+          const int rho = rho0 + 32 * u + lw;
+          const int c0 = cbeg + k * CT + 4 * (ln >> 5);  // key of register 0
+          if ((lw & (C - 1)) == C - 1 && rho < R) {
+            const unsigned off = (unsigned)(rho >> CL) * (unsigned)M + (unsigned)c0;
+            float *dst = sc_bh + off;
+            if (!ragged && (M & 3) == 0) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                *(f32x4 *)(dst + 8 * g) = (f32x4){acc[P][u][4 * g], acc[P][u][4 * g + 1],
+                                                  acc[P][u][4 * g + 2], acc[P][u][4 * g + 3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int col = c0 + 8 * (r >> 2) + (r & 3);
+                if (col < cend) dst[8 * (r >> 2) + (r & 3)] = acc[P][u][r];
+              }
+            }
           }
         }
       }
     }
   };
 
-  // one step: wait for its slot, prefetch NB - 1 steps ahead, compute
-  auto step = [&](auto slot_c, int k) {
-    constexpr int S = decltype(slot_c)::value;
-    constexpr int SN = (S + NB - 1) % NB;
+  // Products of the step in slot S into acc[P] (both sub-tiles), with
+  // epilogue slice ks of the previous step (ep) after each k-step's products.
+  auto products = [&](auto slot_c, auto p_c, auto &&ep) {
+    constexpr int P = decltype(p_c)::value;
+    const unsigned char *ht = hslot(slot_c);
+    const unsigned char *lt = lslot(slot_c);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[P][u][r] = 0.f;
+    // chunk (2 ks + hh) ^ swz of row l32 = (2 ks) ^ (hh ^ swz), and 2 ks
+    // only touches bits the row offset l32 ROWB leaves clear: the offset is
+    // the lane's base XOR a constant, one instruction from one register
+    auto rd = [&](const unsigned char *t, int ks) {
+      unsigned b = rd_base;
+      asm volatile("" : "+v"(b));
+      return as_f16x8(*(const u32x4 *)(t + (b ^ (unsigned)((2 * ks) << 4))));
+    };
+    f16x8 kh[KS], kl[KS];
+    kh[0] = rd(ht, 0);
+    kl[0] = rd(lt, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {  // next k-step's key fragments
+        kh[ks + 1] = rd(ht, ks + 1);
+        kl[ks + 1] = rd(lt, ks + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], clo[u][ks], acc[P][u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], chi[u][ks], acc[P][u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl[ks], chi[u][ks], acc[P][u], 0, 0, 0);
+      ep(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Step k's tile is in its slot, and every wave is done with step k - 1's
+  // slot (the next prefetch overwrites it).
+  auto wait_step = [&](int k) {
     const int ahead = min(NB - 2, nsteps - 1 - k);  // steps after k already requested
     if (ahead >= 2) sc_ring_barrier<2 * LPW>();
     else if (ahead == 1) sc_ring_barrier<LPW>();
     else sc_ring_barrier<0>();
-    if (k + NB - 1 < nsteps) issue(std::integral_constant<int, SN>(), k + NB - 1);
-    const unsigned char *ht = hslot(slot_c);
-    const unsigned char *lt = lslot(slot_c);
-    const float cs = kcs[k];  // key-tile scale (a power of two)
-    f32x16 acc0[2], acc1[2];
+  };
+
+  // The key-tile scale of a step is loaded before the ring barrier that
+  // waits for the step's tile, whose wait covers it: a scalar load in flight
+  // during the products would force every LDS wait there to drain all
+  // outstanding reads (scalar loads return out of order).
+  float cs_cur = 0.f;
+  // iteration k (slot S = k mod NB): products of step k + 1 beside the
+  // epilogue of step k
+  auto step = [&](auto slot_c, int k) {
+    constexpr int S = decltype(slot_c)::value;
+    using SN = std::integral_constant<int, (S + 1) % NB>;
+    using PK = std::integral_constant<int, S & 1>;
+    using PN = std::integral_constant<int, (S + 1) & 1>;
+    const float cs = cs_cur;
+    if (k + 1 < nsteps) {
+      cs_cur = kcs[k + 1];
+      wait_step(k + 1);
+      if (k + NB < nsteps) issue(slot_c, k + NB);
+      products(SN(), PN(), [&](int j) { epi(PK(), k, j, cs); });
+    } else {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc0[u][r] = 0.f;
-        acc1[u][r] = 0.f;
-      }
+      for (int j = 0; j < KS; ++j) epi(PK(), k, j, cs);
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = ((2 * ks + hh) ^ swz_k<D>(l32)) << 4;
-      const f16x8 kh = as_f16x8(*(const u32x4 *)(ht + l32 * ROWB + ch));
-      const f16x8 kl = as_f16x8(*(const u32x4 *)(lt + l32 * ROWB + ch));
-      // the two updates of each acc1 are kept apart in the issue order
-      acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, clo[0][ks], acc1[0], 0, 0, 0);
-      acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, clo[1][ks], acc1[1], 0, 0, 0);
-      acc0[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, chi[0][ks], acc0[0], 0, 0, 0);
-      acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh, chi[1][ks], acc0[1], 0, 0, 0);
-      acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, chi[0][ks], acc1[0], 0, 0, 0);
-      acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, chi[1][ks], acc1[1], 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) epilogue(acc0[u], acc1[u], rs[u] * cs, k, u);
   };
 
   for (int k = 0; k < NB - 1 && k < nsteps; ++k) {
@@ -595,6 +684,13 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
       default: issue(std::integral_constant<int, 2>(), 2); break;
     }
   }
+  if (nsteps > 0) {
+    cs_cur = kcs[0];
+    wait_step(0);
+    if (NB - 1 < nsteps) issue(std::integral_constant<int, NB - 1>(), NB - 1);
+    products(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), [](int) {});
+  }
+  static_assert(NB % 2 == 0, "step parity follows the slot");
   for (int k = 0; k < nsteps; k += NB) {
     step(std::integral_constant<int, 0>(), k);
     if (k + 1 < nsteps) step(std::integral_constant<int, 1>(), k + 1);
@@ -657,6 +753,19 @@ Layout make_layout(int B, int H, int N, int d, int kv_block, int C) {
   return L;
 }
 
+// Sweep 2 with the cluster sum's lane levels fixed at compile time
+// (C = 2^CL clusters per query block).
+template <int D>
+void launch_sweep2(dim3 grid, const SelArgs &a, hipStream_t stream) {
+  switch (a.C) {
+    case 1: hipLaunchKernelGGL((score_kernel<D, 1, 0>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((score_kernel<D, 1, 1>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((score_kernel<D, 1, 2>), grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((score_kernel<D, 1, 3>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((score_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a); break;
+  }
+}
+
 }  // namespace
 
 size_t select_workspace_bytes(int B, int H, int N, int d, int kv_block, int n_clusters) {
@@ -702,14 +811,14 @@ int launch_select_scores(const void *q, const void *k, int B, int H, int N, int 
     hipLaunchKernelGGL(pool_split_kernel<128>, gpool, dim3(256), 0, stream, a);
     if (n_clusters <= 8) hipLaunchKernelGGL((kmeans_kernel<128, 8>), gkm, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((kmeans_kernel<128, 16>), gkm, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((score_kernel<128, 0>), gsc, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((score_kernel<128, 1>), gsc, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((score_kernel<128, 0, 0>), gsc, dim3(256), 0, stream, a);
+    launch_sweep2<128>(gsc, a, stream);
   } else {
     hipLaunchKernelGGL(pool_split_kernel<64>, gpool, dim3(256), 0, stream, a);
     if (n_clusters <= 8) hipLaunchKernelGGL((kmeans_kernel<64, 8>), gkm, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((kmeans_kernel<64, 16>), gkm, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((score_kernel<64, 0>), gsc, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((score_kernel<64, 1>), gsc, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((score_kernel<64, 0, 0>), gsc, dim3(256), 0, stream, a);
+    launch_sweep2<64>(gsc, a, stream);
   }
   return status_of(hipGetLastError());
 }

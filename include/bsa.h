@@ -110,6 +110,9 @@ const char *bsa_version(void);
  * workspace   device scratch of at least bsa_select_workspace_bytes() bytes,
  *             256-byte aligned; its contents are undefined after the call.
  * n_clusters  1, 2, 4, 8 or 16; kmeans_iters 0..16 (0 = segment means).
+ * Sizes: B*H*M and B*H*nQB*n_clusters at most 2^31 - 1, and one head's
+ * score matrix (nQB * M entries) below 2^32; larger problems return
+ * BSA_ERR_SIZE before any HIP call.
  * --------------------------------------------------------------------- */
 int bsa_select_workspace_bytes(int B, int H, int N, int d, int q_block, int kv_block,
                                int n_clusters, size_t *bytes /* host out */);

@@ -110,6 +110,15 @@ def test_select_rejects_invalid_arguments(bsa):
     assert call(13, None) == -6
     assert call(14, 0) == -6
     assert call(13, FAKE + 16) == -4
+    # one head's score matrix must hold fewer than 2^32 entries: N = 750,000
+    # at single-token blocks gives 5,860 x 750,000 (refused before any use of
+    # the pointers); 100,000 tokens pass the size checks and stop at the
+    # one-byte workspace
+    big = list(base)
+    big[4], big[7], big[14] = 750000, 1, 1
+    assert L.bsa_select_scores(*big) == -7
+    big[4] = 100000
+    assert L.bsa_select_scores(*big) == -6
 
 
 def test_basa_layout_of_the_1664x960_grid(bsa):
