@@ -52,8 +52,10 @@ algorithmic 10 d flops per (valid query, listed valid key) pair.
 
 With ``--mfma-peak`` it prints one JSON report of the bf16 matrix-instruction
 throughput probe (bsa_mfma_peak_probe: v_mfma_f32_32x32x16_bf16, the
-attention kernel's instruction, from registers) over a sweep of grid sizes.
-The benchmark line runs the same probe at its largest grid after the timed
+attention kernel's instruction, from registers) over a sweep of grid sizes,
+with random operands and with low-entropy operands: the rate the matrix
+units sustain drops with the operands' toggling (the clock falls under the
+power).  The benchmark line runs the random-operand probe after the timed
 region and states the attention kernel's fraction of that measured rate
 beside the fraction of the published peak.
 """
@@ -516,19 +518,20 @@ def _time(fn, reps, warmup=1):
     return e0.elapsed_time(e1) / reps
 
 
-def mfma_peak(workgroups, iters=2000, reps=3):
+def mfma_peak(workgroups, iters=2000, reps=3, operands=0):
     """Best rate of the matrix-instruction probe over `reps` timed calls
-    (TFLOP/s), and the ms of one call."""
+    (TFLOP/s), and the ms of one call; operands 0 = random, 1 = low
+    entropy."""
     import torch
     import block_sparse_attention_mean_amd as bsa
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    flops = bsa.bsa_mfma_peak_probe(workgroups, iters, sink)      # warmup
+    flops = bsa.bsa_mfma_peak_probe(workgroups, iters, sink, operands)      # warmup
     stream = torch.cuda.current_stream()
     best = None
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        bsa.bsa_mfma_peak_probe(workgroups, iters, sink)
+        bsa.bsa_mfma_peak_probe(workgroups, iters, sink, operands)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
@@ -536,24 +539,34 @@ def mfma_peak(workgroups, iters=2000, reps=3):
     return flops / best / 1e9, best
 
 
-PEAK_PROBE_GRID = 4096   # 16 workgroups of 4 waves per CU: 16 waves per SIMD saturate the units
+# The probe holds 3 waves per SIMD (about 150 registers each): 768
+# workgroups of 4 waves fill the chip once; 3072 run four such rounds.
+PEAK_PROBE_GRID = 3072
 PEAK_PROBE_ITERS = 4000
+PROBE_RESIDENT_WAVES = 3
 
 
 def run_mfma_peak(args):
-    """Throughput of v_mfma_f32_32x32x16_bf16 over grid sizes (see the
-    module docstring)."""
+    """Throughput of v_mfma_f32_32x32x16_bf16 over grid sizes and operand
+    modes (see the module docstring)."""
     pts = []
-    for wg in (256, 512, 1024, 2048, PEAK_PROBE_GRID, 8192):
-        tf, ms = mfma_peak(wg, PEAK_PROBE_ITERS, reps=args.reps)
-        pts.append({"workgroups": wg, "waves_per_simd": wg * 4 / 1024, "ms": round(ms, 4),
-                    "tflops": round(tf, 2), "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4)})
-        log(f"[mfma-peak] {pts[-1]}")
+    for mode, name in ((0, "random"), (1, "low entropy")):
+        for wg in (256, 512, 768, PEAK_PROBE_GRID):
+            tf, ms = mfma_peak(wg, PEAK_PROBE_ITERS, reps=args.reps, operands=mode)
+            pts.append({"operands": name, "workgroups": wg,
+                        "resident_waves_per_simd": min(PROBE_RESIDENT_WAVES, wg * 4 // 1024),
+                        "ms": round(ms, 4), "tflops": round(tf, 2),
+                        "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4)})
+            log(f"[mfma-peak] {pts[-1]}")
+    best = {n: max(p["tflops"] for p in pts if p["operands"] == n) for n in ("random", "low entropy")}
     rep = {"report": "mfma peak", "kernel": "bsa::mfma_peak_kernel",
            "instruction": "v_mfma_f32_32x32x16_bf16 (32768 flops), 8 independent chains per wave, "
                           "operands in registers",
+           "operands": {"random": "bf16 in +-[1/4, 4), random sign and mantissa, three sets that "
+                                  "consecutive instructions alternate between",
+                        "low entropy": "a few small values with short mantissas, fixed per lane"},
            "iters": PEAK_PROBE_ITERS, "reps": args.reps, "peak_spec": PEAK_BF16_TFLOPS, "points": pts,
-           "best_tflops": max(p["tflops"] for p in pts)}
+           "best_tflops": best}
     print(json.dumps(rep), flush=True)
 
 
@@ -867,13 +880,15 @@ def main():
     del flush
     # the matrix units' measured rate on the attention kernel's instruction
     # (outside the timed region)
-    peak_meas, _ = mfma_peak(PEAK_PROBE_GRID, PEAK_PROBE_ITERS)
+    peak_meas, _ = mfma_peak(PEAK_PROBE_GRID, PEAK_PROBE_ITERS, operands=0)
+    peak_low, _ = mfma_peak(PEAK_PROBE_GRID, PEAK_PROBE_ITERS, operands=1)
     rec["roofline"].update({
         "peak_measured": round(peak_meas, 2),
         "frac_measured": round(attn_tf / peak_meas, 4),
-        "peak_measured_by": "bsa_mfma_peak_probe: v_mfma_f32_32x32x16_bf16 from registers, "
-                            f"{PEAK_PROBE_GRID} workgroups of 4 waves x {PEAK_PROBE_ITERS} rounds "
-                            "of 8 chains, best of 3 (bench.py --mfma-peak)",
+        "peak_measured_by": "bsa_mfma_peak_probe, random bf16 operands: v_mfma_f32_32x32x16_bf16 "
+                            f"from registers, {PEAK_PROBE_GRID} workgroups of 4 waves x "
+                            f"{PEAK_PROBE_ITERS} rounds of 8 chains, best of 3 (bench.py --mfma-peak)",
+        "peak_measured_low_entropy": round(peak_low, 2),
     })
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20

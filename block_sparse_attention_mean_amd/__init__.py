@@ -25,11 +25,13 @@ __all__ = [
     "bsa_basa_plan", "bsa_basa_plan_noalloc", "bsa_window_unpermute", "bsa_block_mass",
     "bsa_plan_coverage", "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
     "bsa_mfma_peak_probe", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
+    "PROBE_RANDOM", "PROBE_LOW_ENTROPY",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
 PLAN_SIP, PLAN_TOPK = 0, 1
 OK, ERR_NONFINITE = 0, -9   # values of a plan's status word
+PROBE_RANDOM, PROBE_LOW_ENTROPY = 0, 1   # operand modes of the matrix probe
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
@@ -73,7 +75,7 @@ lib.bsa_basa_offsets.argtypes = [_i, _i, _pi]
 lib.bsa_basa_shifts.restype = _i
 lib.bsa_basa_shifts.argtypes = [_i, _i, _i, _i, _pi, _pi, _pi, _pi]
 lib.bsa_mfma_peak_probe.restype = _i
-lib.bsa_mfma_peak_probe.argtypes = [_i, _i, _p, ctypes.POINTER(ctypes.c_longlong), _p]
+lib.bsa_mfma_peak_probe.argtypes = [_i, _i, _i, _p, ctypes.POINTER(ctypes.c_longlong), _p]
 lib.bsa_output_error.restype = _i
 lib.bsa_output_error.argtypes = [_p, _p, _i, ctypes.c_longlong, _p, _p]
 
@@ -454,12 +456,14 @@ def bsa_basa_shifts(wh: int, ww: int, L: int, S: int = 1, c_h=None, c_w=None):
             [list(dx[l * S:(l + 1) * S]) for l in range(L)])
 
 
-def bsa_mfma_peak_probe(workgroups, iters, sink, stream=None) -> int:
-    """Launches the bf16 matrix-instruction throughput probe; returns the
-    flops of the call (time it with events on the stream)."""
+def bsa_mfma_peak_probe(workgroups, iters, sink, operands=None, stream=None) -> int:
+    """Launches the bf16 matrix-instruction throughput probe (operands:
+    PROBE_RANDOM, the default, or PROBE_LOW_ENTROPY); returns the flops of
+    the call (time it with events on the stream)."""
     _need(sink, torch.float32, "sink", shape=(1,))
     fl = ctypes.c_longlong(0)
-    _check(lib.bsa_mfma_peak_probe(workgroups, iters, _ptr(sink), ctypes.byref(fl),
+    mode = PROBE_RANDOM if operands is None else operands
+    _check(lib.bsa_mfma_peak_probe(workgroups, iters, mode, _ptr(sink), ctypes.byref(fl),
                                    _stream(stream)), "bsa_mfma_peak_probe")
     return fl.value
 

@@ -50,7 +50,7 @@ int launch_plan_coverage(const float *mass, const int32_t *idx, const int32_t *c
 int launch_output_error(const void *out, const void *ref, int slabs, long long n, double *sums,
                         hipStream_t stream);
 long long mfma_peak_flops(int workgroups, int iters);
-int launch_mfma_peak(int workgroups, int iters, float *sink, hipStream_t stream);
+int launch_mfma_peak(int workgroups, int iters, int operands, float *sink, hipStream_t stream);
 }  // namespace bsa
 
 namespace {
@@ -310,11 +310,13 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
                               max_blocks, scale, dq, dk, dv, (hipStream_t)stream);
 }
 
-int bsa_mfma_peak_probe(int workgroups, int iters, float *sink, long long *flops, void *stream) {
+int bsa_mfma_peak_probe(int workgroups, int iters, int operands, float *sink, long long *flops,
+                        void *stream) {
   if (!sink || workgroups < 1 || iters < 1) return BSA_ERR_ARG;
+  if (operands != BSA_PROBE_RANDOM && operands != BSA_PROBE_LOW_ENTROPY) return BSA_ERR_ARG;
   if (!aligned(sink, 4)) return BSA_ERR_ALIGN;
   if (flops) *flops = bsa::mfma_peak_flops(workgroups, iters);
-  return bsa::launch_mfma_peak(workgroups, iters, sink, (hipStream_t)stream);
+  return bsa::launch_mfma_peak(workgroups, iters, operands, sink, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -369,14 +369,24 @@ int bsa_output_error(const void *out, const void *ref, int slabs, long long n, d
  * attention kernel uses (v_mfma_f32_32x32x16_bf16).  `workgroups` groups of
  * 4 waves each run `iters` rounds of 8 independent accumulations from
  * registers (no memory traffic); *flops (host out, may be NULL) receives the
- * flops of the call, workgroups * 4 * iters * 8 * 32768.  Timing the call
- * gives the matrix units' practical peak, against which the benchmark also
- * states the attention kernel's fraction (beside the published 2516.6
- * TFLOP/s).  sink: one device float the kernel writes (its result keeps the
- * computation live).  Not part of the attention path.
+ * flops of the call, workgroups * 4 * iters * 8 * 32768.  The rate the
+ * matrix units sustain depends on the operand data (the clock drops under
+ * the power of toggling operands), so `operands` selects:
+ *   BSA_PROBE_RANDOM       random bf16 operands in +-[1/4, 4), four sets that
+ *                          consecutive instructions alternate between (the
+ *                          practical peak for real data, against which the
+ *                          benchmark also states the attention kernel's
+ *                          fraction, beside the published 2516.6 TFLOP/s);
+ *   BSA_PROBE_LOW_ENTROPY  a few small operands with short mantissas, fixed
+ *                          per lane (the most favourable case).
+ * sink: one device float the kernel writes (its result keeps the
+ * computation live).  Errors: BSA_ERR_ARG for a null sink, workgroups or
+ * iters < 1 or an unknown mode.  Not part of the attention path.
  * --------------------------------------------------------------------- */
-int bsa_mfma_peak_probe(int workgroups, int iters, float *sink, long long *flops /* host out */,
-                        void *stream);
+enum { BSA_PROBE_RANDOM = 0, BSA_PROBE_LOW_ENTROPY = 1 };
+
+int bsa_mfma_peak_probe(int workgroups, int iters, int operands, float *sink,
+                        long long *flops /* host out */, void *stream);
 
 #ifdef __cplusplus
 }

@@ -232,3 +232,16 @@ def test_binding_loads_the_library_into_torchs_hip_runtime():
     assert r.returncode == 0, r.stderr
     libs = eval(r.stdout.strip().splitlines()[-1])
     assert len(libs) == 1 and "torch" in libs[0], libs
+
+
+def test_mfma_probe_rejects_invalid_arguments(bsa):
+    """The matrix probe refuses a null or misaligned sink, empty grids or
+    rounds and unknown operand modes before any HIP call."""
+    L = bsa.lib
+    assert bsa.PROBE_RANDOM == 0 and bsa.PROBE_LOW_ENTROPY == 1
+    assert L.bsa_mfma_peak_probe(1, 1, 0, None, None, None) == -1
+    assert L.bsa_mfma_peak_probe(0, 1, 0, FAKE, None, None) == -1
+    assert L.bsa_mfma_peak_probe(1, 0, 1, FAKE, None, None) == -1
+    assert L.bsa_mfma_peak_probe(1, 1, 2, FAKE, None, None) == -1
+    assert L.bsa_mfma_peak_probe(1, 1, -1, FAKE, None, None) == -1
+    assert L.bsa_mfma_peak_probe(1, 1, 0, FAKE + 2, None, None) == -4

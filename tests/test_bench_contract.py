@@ -60,7 +60,7 @@ def test_bench_line_on_the_tiny_workload():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["traffic"] is None  # the counter runs cover the headline workload only
-    assert roof["peak_measured"] > 0
+    assert roof["peak_measured"] > 0 and roof["peak_measured_low_entropy"] > 0
     assert abs(roof["frac_measured"] - roof["achieved"] / roof["peak_measured"]) < 1e-3
     p10, p50, p90 = rec["attn_ms_p10_p50_p90"]
     assert rec["attn_ms_per_call"] == p50                     # the median
@@ -98,5 +98,7 @@ def test_mfma_peak_report():
     r = _run("--mfma-peak", "--reps", "2")
     assert r.returncode == 0, r.stderr[-2000:]
     rep = json.loads(r.stdout.strip().splitlines()[-1])
-    assert rep["best_tflops"] > 100
+    assert set(rep["best_tflops"]) == {"random", "low entropy"}
+    assert all(v > 100 for v in rep["best_tflops"].values())
     assert all(0 < p["tflops"] <= rep["peak_spec"] for p in rep["points"])
+    assert {p["operands"] for p in rep["points"]} == {"random", "low entropy"}
