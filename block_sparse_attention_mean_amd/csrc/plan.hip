@@ -989,13 +989,24 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs a) {
 //     exact in fp64), block j is drawn when R < L_j, the chunk-local prefix
 //     after it; then R grows by 2^44 (one point per block at most, since
 //     Pi_j <= 2^44), or becomes infinite after the s-th point.
+//   * STAGED (budgets to kStageMax): the draw pass puts each drawn block and
+//     its score into LDS, and after one barrier a last pass writes the index
+//     and shift lists in order, coalesced (the shifts -ln pi computed there);
+//     otherwise the draw pass writes the indices and parks the scores in the
+//     shift slots, and a last pass turns those into shifts.
 // Rows in flight per CU for a chunk of CH values (the register budget).
 constexpr int sip_rows_per_cu(int ch) { return ch <= 32 ? 4 : (ch <= 80 ? 3 : 2); }
+// Largest budget whose staged draws (8 bytes each) leave LDS for every row
+// in flight: 4 rows of 32 KB at the smallest chunk.
+constexpr int kStageMax = 4096;
 
-template <int CH>
+template <int CH, bool STAGED>
 __global__ __launch_bounds__(256, sip_rows_per_cu(CH)) void sip_reg_kernel(PlanArgs a) {
   constexpr int PTR = 256;
   __shared__ SharedT<PTR / 64> sh;
+  extern __shared__ __attribute__((aligned(16))) unsigned char stage_raw[];
+  int32_t *st_idx = (int32_t *)stage_raw;                         // [budget]
+  float *st_val = (float *)(stage_raw + 4 * (size_t)a.budget);  // [budget]
   const int t = threadIdx.x;
   const size_t r = blockIdx.x;
   const int M = a.M, s = a.budget;
@@ -1083,12 +1094,30 @@ __global__ __launch_bounds__(256, sip_rows_per_cu(CH)) void sip_reg_kernel(PlanA
   row.template each_seq<8>([&](int j, float v) {
     L += __builtin_floor(fmin((double)UNIT, lam44 * (double)v));
     if (R < L) {
-      out_idx[q] = j;
-      if (out_bias) out_bias[q] = v;  // the score, turned into its shift below
+      if (STAGED) {
+        st_idx[q] = j;
+        st_val[q] = v;
+      } else {
+        out_idx[q] = j;
+        if (out_bias) out_bias[q] = v;  // the score, turned into its shift below
+      }
       ++q;
       R = q < s ? R + (double)UNIT : __builtin_inf();
     }
   });
+  if (STAGED) {
+    __syncthreads();
+    for (int e = t; e < s; e += PTR) {
+      const bool d = e < drawn;
+      out_idx[e] = d ? st_idx[e] : -1;
+      if (out_bias) out_bias[e] = d ? (float)(-log(fmin(1.0, lam * (double)st_val[e]))) : 0.f;
+    }
+    if (t == 0) {
+      a.count[r] = drawn;
+      if (a.lambda) a.lambda[r] = lam;
+    }
+    return;
+  }
   if (out_bias) {
     // shifts -ln pi of the drawn blocks, from the scores parked in their
     // slots (written by this workgroup before the barrier)
@@ -1133,13 +1162,18 @@ int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, i
   // SIP rows that fit a register-resident instance (the row's start may sit
   // up to 3 floats past a 16-byte boundary)
   const long long span = (long long)M + 3;
-  if (mode == BSA_PLAN_SIP && span <= 256 * 32)
-    hipLaunchKernelGGL(sip_reg_kernel<32>, dim3(rows), dim3(256), 0, stream, a);
-  else if (mode == BSA_PLAN_SIP && span <= 256 * 80)
-    hipLaunchKernelGGL(sip_reg_kernel<80>, dim3(rows), dim3(256), 0, stream, a);
-  else if (mode == BSA_PLAN_SIP && span <= 256 * 120)
-    hipLaunchKernelGGL(sip_reg_kernel<120>, dim3(rows), dim3(256), 0, stream, a);
-  else if (with_row <= (size_t)max_lds)
+  const bool staged = budget <= kStageMax;
+  const size_t stage = staged ? (size_t)budget * 8 : 0;
+  if (mode == BSA_PLAN_SIP && span <= 256 * 32) {
+    if (staged) hipLaunchKernelGGL((sip_reg_kernel<32, true>), dim3(rows), dim3(256), stage, stream, a);
+    else hipLaunchKernelGGL((sip_reg_kernel<32, false>), dim3(rows), dim3(256), 0, stream, a);
+  } else if (mode == BSA_PLAN_SIP && span <= 256 * 80) {
+    if (staged) hipLaunchKernelGGL((sip_reg_kernel<80, true>), dim3(rows), dim3(256), stage, stream, a);
+    else hipLaunchKernelGGL((sip_reg_kernel<80, false>), dim3(rows), dim3(256), 0, stream, a);
+  } else if (mode == BSA_PLAN_SIP && span <= 256 * 120) {
+    if (staged) hipLaunchKernelGGL((sip_reg_kernel<120, true>), dim3(rows), dim3(256), stage, stream, a);
+    else hipLaunchKernelGGL((sip_reg_kernel<120, false>), dim3(rows), dim3(256), 0, stream, a);
+  } else if (with_row <= (size_t)max_lds)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(rows), dim3(PT), with_row, stream, a);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(rows), dim3(PT), base, stream, a);
