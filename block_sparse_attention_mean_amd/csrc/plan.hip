@@ -155,6 +155,41 @@ __device__ __forceinline__ void block_minmax_u(SH &sh, unsigned &mn, unsigned &m
     mx = max(mx, sh.red_u2[i]);
   }
 }
+// The row's first reductions in one: a packed count, a sum, a minimum and a
+// maximum, each combined in the order block_sum_l / block_sum_d /
+// block_minmax_u use (so the results are theirs), with one barrier.  Only
+// for the first reduction of a kernel: nothing has read the buffers before.
+template <class SH>
+__device__ __forceinline__ void block_reduce_first(SH &sh, long long &pk, double &tot, unsigned &mn,
+                                                   unsigned &mx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    pk += __shfl_xor(pk, o, 64);
+    tot += __shfl_xor(tot, o, 64);
+    mn = min(mn, (unsigned)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (unsigned)__shfl_xor((int)mx, o, 64));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh.red_l[w] = pk;
+    sh.red_d[w] = tot;
+    sh.red_u[w] = mn;
+    sh.red_u2[w] = mx;
+  }
+  __syncthreads();
+  pk = sh.red_l[0];
+  tot = 0.0 + sh.red_d[0];
+  mn = sh.red_u[0];
+  mx = sh.red_u2[0];
+#pragma unroll
+  for (int i = 1; i < SH::NW; ++i) {
+    pk += sh.red_l[i];
+    tot += sh.red_d[i];
+    mn = min(mn, sh.red_u[i]);
+    mx = max(mx, sh.red_u2[i]);
+  }
+}
+
 // Exclusive prefix over threads (thread order) of a 64-bit count.
 template <class SH>
 __device__ __forceinline__ uint64_t block_exscan_u64(SH &sh, uint64_t v, uint64_t &total) {
@@ -397,21 +432,33 @@ __device__ __forceinline__ void dd_sum_collect(SH &sh, const Row &row, float lo_
   double h = 0.0, l = 0.0;
   long long c = 0;
   int nin = 0;  // this thread's values inside the bracket (rare)
+  // their smallest and largest (positive values): with at most two of them
+  // these are the values themselves; only a thread holding more re-reads
+  // its part of the row from memory
+  float cmin = 3.40282347e38f, cmax = 0.f;
   row.each([&](int, float v) {
     const bool in = v <= lo_x;
     double s2, e;
     two_sum(h, in ? (double)v : 0.0, s2, e);
     h = s2;
     l += e;
-    nin += (!in && v < hi_x) ? 1 : 0;
+    const bool cand = !in && v < hi_x;
+    cmin = fminf(cmin, cand ? v : 3.40282347e38f);
+    cmax = fmaxf(cmax, cand ? v : 0.f);
+    nin += cand ? 1 : 0;
   });
-  if (nin)
+  if (nin > 2) {
     row.each_mem([&](int, float v) {
       if (v > lo_x && v < hi_x) {
         const int slot = atomicAdd(&sh.ncol, 1);
         if (slot < MCAP) sh.col[slot] = v;
       }
     });
+  } else if (nin > 0) {
+    const int slot = atomicAdd(&sh.ncol, nin);
+    if (slot < MCAP) sh.col[slot] = cmin;
+    if (nin == 2 && slot + 1 < MCAP) sh.col[slot + 1] = cmax;
+  }
   const double n = h + l;
   l = l - (n - h);
   h = n;
@@ -1029,12 +1076,11 @@ __global__ __launch_bounds__(256, sip_rows_per_cu(CH)) void sip_reg_kernel(PlanA
     mnf = pos ? fminf(mnf, v) : mnf;
     tot += (double)v;
   });
-  const long long pk = block_sum_l(sh, ((long long)bad << 32) | (long long)mypos);
+  long long pk = ((long long)bad << 32) | (long long)mypos;
+  unsigned mx = __builtin_bit_cast(unsigned, mxf), mnpos = __builtin_bit_cast(unsigned, mnf);
+  block_reduce_first(sh, pk, tot, mnpos, mx);
   const long long nbad = pk >> 32;
   long long npos = pk & 0xffffffffll;
-  tot = block_sum_d(sh, tot);
-  unsigned mx = __builtin_bit_cast(unsigned, mxf), mnpos = __builtin_bit_cast(unsigned, mnf);
-  block_minmax_u(sh, mnpos, mx);
 
   auto fill_rest = [&](int from) {
     for (int e = from + t; e < s; e += PTR) {
