@@ -710,7 +710,12 @@ __device__ __forceinline__ void sip_threshold(SH &sh, const Row &row, int M, int
       x = __builtin_bit_cast(float, blo + (bhi - blo) / 2);
       continue;
     }
+    // no row value inside (blo, bhi): x* = blo, and #{S > blo} = #{S >= bhi}
+    // = nge_hi (bhi has been tested here: by stage 0, or as a failing secant
+    // or bisection point).  The collect pass below (registers only) gives
+    // T_r, with nothing to collect.
     xstar = __builtin_bit_cast(float, blo);
+    collect = true;
     stage = 3;
   }
 
