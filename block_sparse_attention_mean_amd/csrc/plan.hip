@@ -342,8 +342,9 @@ struct RowView {
 // load.  Positions outside [0, M) hold 0, which a SIP plan never counts,
 // sums into anything but zero, or draws.  each() runs over the registers
 // (fully unrolled); each_mem() re-reads the thread's positions from memory
-// in a rolled loop, for the rarely taken exact evaluations, whose unrolled
-// code would be large.
+// in a rolled loop, for the rarely taken double-double and exact
+// evaluations and a collection of more than two bracket values per thread,
+// whose unrolled code would be large.
 template <int CH>
 struct RegRow {
   static_assert(CH % 4 == 0, "whole 16-byte groups");
@@ -640,7 +641,20 @@ __device__ __forceinline__ void sip_threshold(SH &sh, const Row &row, int M, int
       if (diff > err_bound) {
         holds = false;
       } else if (!(diff < -err_bound)) {
-        // inside the margin: double-double sum of {S < x}
+        // inside the fp32 margin (common at high budgets): the sum again in
+        // fp64, from the row's own copy (registers or LDS), whose error is
+        // below (chunk - 1 + 6 + NW) u per term of the total (sequential sum,
+        // then the butterfly and the waves); bounded here with room to spare
+        double s64 = 0.0;
+        row.each([&](int, float v) { s64 += v < x ? (double)v : 0.0; });
+        long long none = 0;
+        block_reduce(sh, none, s64, ph);
+        const double d64 = lhs - s64;
+        const double err64 = ldexp((double)(chunk + 16), -52) * tot * (1.0 + 0x1p-30);
+        if (d64 > err64) {
+          holds = false;
+        } else if (!(d64 < -err64)) {
+        // inside that margin too: double-double sum of {S < x}
         double thi, tlo;
         long long unused;
         dd_sum(sh, row, x, true, thi, tlo, unused, ph);
@@ -655,6 +669,7 @@ __device__ __forceinline__ void sip_threshold(SH &sh, const Row &row, int M, int
           uint64_t ldig[NDIG + 1];
           scaled_to_digits((unsigned long long)mult, x, ldig);
           holds = digits_ge(sh.total, ldig);
+        }
         }
       }
     }
@@ -1215,7 +1230,18 @@ int launch_sip_plan(const float *scores, int rows, int nqb, int M, int budget, i
   const long long span = (long long)M + 3;
   const bool staged = budget <= kStageMax;
   const size_t stage = staged ? (size_t)budget * 8 : 0;
-  if (mode == BSA_PLAN_SIP && span <= 256 * 32) {
+  // Budgets of half the row or more (but below the whole row, which needs no
+  // search), past the staged range, go to the 512-thread kernel when the row
+  // fits its LDS: there the searches take more passes and the sampling
+  // writes most of the row, and twice the threads with the row in LDS
+  // measured faster (40 heads of 18,900 blocks: 2.80 against 2.94 ms at
+  // half the row, 3.31 against 4.14 at three quarters, 3.91 against 4.93 at
+  // 90 %).
+  const bool wide = mode == BSA_PLAN_SIP && !staged && 2 * (long long)budget >= M && budget < M &&
+                    with_row <= (size_t)max_lds;
+  if (wide) {
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(rows), dim3(PT), with_row, stream, a);
+  } else if (mode == BSA_PLAN_SIP && span <= 256 * 32) {
     if (staged) hipLaunchKernelGGL((sip_reg_kernel<32, true>), dim3(rows), dim3(256), stage, stream, a);
     else hipLaunchKernelGGL((sip_reg_kernel<32, false>), dim3(rows), dim3(256), 0, stream, a);
   } else if (mode == BSA_PLAN_SIP && span <= 256 * 80) {
