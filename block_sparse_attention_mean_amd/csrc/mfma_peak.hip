@@ -7,10 +7,11 @@
 // they sustain depends on the operand data as well as on the instruction
 // count: the chip lowers its clock under the power of toggling operands.
 // Two operand modes:
-//   random       four sets of random bf16 operands (random sign, exponent
-//                spanning [1/4, 4), random mantissa; a per-lane xorshift
-//                from the seed), consecutive instructions taking different
-//                sets, as the attention kernel's gathered keys do;
+//   random       three sets of random bf16 operands (random sign, exponent
+//                spanning [1/4, 4), random mantissa; a per-lane hash of
+//                the seed and register index), consecutive instructions
+//                taking different sets, as the attention kernel's gathered
+//                keys do;
 //   low entropy  the same small operands for every instruction of a lane
 //                (a few distinct values with short mantissas), the most
 //                favourable case.
