@@ -45,10 +45,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --backward [--workload wan14b_720p]
        python bench.py --mfma-peak
 
-With ``--backward`` it prints one JSON report of bsa_attn_bwd at the
+With ``--backward`` it prints one JSON report of the backward at the
 workload: the selector's SIP plan, one forward call for the output and its
-LSE, then the backward timed with HIP events (warmup + steps), against the
-algorithmic 10 d flops per (valid query, listed valid key) pair.
+LSE, then bsa_attn_bwd (atomic adds) and bsa_attn_bwd_ws (per-entry
+partial rows, ``--bwd-slabs`` (b, h) slabs of workspace per pass) timed
+with HIP events (warmup + steps), against the algorithmic 10 d flops per
+(valid query, listed valid key) pair, and the two results compared.
 
 With ``--mfma-peak`` it prints one JSON report of the bf16 matrix-instruction
 throughput probe (bsa_mfma_peak_probe: v_mfma_f32_32x32x16_bf16, the
@@ -102,6 +104,8 @@ def parse():
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--backward", action="store_true",
                    help="print the backward-pass report instead of the benchmark line")
+    p.add_argument("--bwd-slabs", type=int, default=8,
+                   help="(b, h) slabs of workspace per pass of bsa_attn_bwd_ws")
     p.add_argument("--mfma-peak", action="store_true",
                    help="print the matrix-instruction throughput report instead of the line")
     p.add_argument("--copy-calib-mib", type=int, default=0,
@@ -616,7 +620,23 @@ def run_backward(args):
     for t in (dq, dk, dv):
         if not torch.isfinite(t).all():
             raise SystemExit("non-finite gradient")
-    tf = 10.0 * d * pairs / bwd_ms / 1e9
+    # the workspace variant: per-entry partial rows, summed per KV block
+    slab = bsa.bsa_attn_bwd_workspace_bytes(N, N, d, s, 128, kvb)
+    nslab = max(1, min(args.bwd_slabs, H))
+    log(f"[backward] workspace variant: {nslab} slabs of {slab / 2**30:.2f} GiB per pass")
+    ws = torch.empty(slab * nslab, dtype=torch.uint8, device=q.device)
+    wq, wk, wv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    fw = lambda: bsa.bsa_attn_bwd_ws(q, k, v, out, dout, lse, idx, bias, cnt, 128, kvb,  # noqa: E731
+                                     dq=wq, dk=wk, dv=wv, workspace=ws)
+    ws_ms = _time(fw, args.steps, args.warmup)
+    for t in (wq, wk, wv):
+        if not torch.isfinite(t).all():
+            raise SystemExit("non-finite gradient (workspace variant)")
+    diff = {n: float(((a.double() - b.double()).norm() / a.double().norm()).item())
+            for n, a, b in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv))}
+    del ws
+    flop = 10.0 * d * pairs
+    tf, tfw = flop / bwd_ms / 1e9, flop / ws_ms / 1e9
     rep = {
         "report": "backward",
         "workload": f"{args.workload}: latent {T}x{Hg}x{Wg} = {N} tokens, B=1, H={H}, d={d}, "
@@ -624,10 +644,17 @@ def run_backward(args):
         "data": "synthetic", "seed": args.seed, "steps": args.steps, "warmup": args.warmup,
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "bwd_over_fwd": round(bwd_ms / fwd_ms, 3),
-        "bwd_flop_per_call": 10.0 * d * pairs,
+        "bwd_ws_ms": round(ws_ms, 4), "bwd_ws_over_fwd": round(ws_ms / fwd_ms, 3),
+        "bwd_ws_slabs_per_pass": nslab, "bwd_ws_bytes": slab * nslab,
+        "ws_vs_atomic_rel_fro": {n: float(f"{x:.3e}") for n, x in diff.items()},
+        "bwd_flop_per_call": flop,
         "roofline": {"kernel": "bsa_attn_bwd (zero + dq + dkdv kernels)", "bound": "mfma",
                      "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+        "roofline_ws": {"kernel": "bsa_attn_bwd_ws (dq + key-major lists + dkdv partial rows + "
+                                  "per-block sum)", "bound": "mfma",
+                        "achieved": round(tfw, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tfw / PEAK_BF16_TFLOPS, 4)},
     }
     print(json.dumps(rep), flush=True)
 

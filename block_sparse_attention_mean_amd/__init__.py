@@ -24,7 +24,7 @@ __all__ = [
     "bsa_sampling_offset", "bsa_select_workspace_bytes", "bsa_basa_layout",
     "bsa_basa_plan", "bsa_basa_plan_noalloc", "bsa_window_unpermute", "bsa_block_mass",
     "bsa_plan_coverage", "bsa_output_error", "dense_plan", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
-    "bsa_mfma_peak_probe", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
+    "bsa_attn_bwd_workspace_bytes", "bsa_attn_bwd_ws", "bsa_mfma_peak_probe", "PLAN_SIP", "PLAN_TOPK", "LIB_PATH", "OK", "ERR_NONFINITE",
     "PROBE_RANDOM", "PROBE_LOW_ENTROPY",
 ]
 
@@ -70,6 +70,10 @@ lib.bsa_plan_coverage.restype = _i
 lib.bsa_plan_coverage.argtypes = [_p, _p, _p, _i, _i, _i, _p, _p]
 lib.bsa_attn_bwd.restype = _i
 lib.bsa_attn_bwd.argtypes = [_p] * 6 + [_i] * 7 + [_p, _p, _p, _i, _f, _p, _p, _p, _p]
+lib.bsa_attn_bwd_workspace_bytes.restype = _i
+lib.bsa_attn_bwd_workspace_bytes.argtypes = [_i] * 6 + [_psz]
+lib.bsa_attn_bwd_ws.restype = _i
+lib.bsa_attn_bwd_ws.argtypes = [_p] * 6 + [_i] * 7 + [_p, _p, _p, _i, _f, _p, _p, _p, _p, _sz, _p]
 lib.bsa_basa_offsets.restype = _i
 lib.bsa_basa_offsets.argtypes = [_i, _i, _pi]
 lib.bsa_basa_shifts.restype = _i
@@ -84,7 +88,8 @@ SYMBOLS = ["bsa_status_string", "bsa_version", "bsa_select_workspace_bytes", "bs
            "bsa_sip_plan", "bsa_sampling_offset", "bsa_attn_fwd", "bsa_basa_layout",
            "bsa_basa_plan", "bsa_window_unpermute", "bsa_block_mass", "bsa_plan_coverage",
            "bsa_output_error", "bsa_basa_offsets", "bsa_basa_shifts", "bsa_attn_bwd",
-           "bsa_basa_plan_noalloc", "bsa_mfma_peak_probe"]
+           "bsa_attn_bwd_workspace_bytes", "bsa_attn_bwd_ws", "bsa_basa_plan_noalloc",
+           "bsa_mfma_peak_probe"]
 
 
 class BsaError(RuntimeError):
@@ -247,10 +252,7 @@ def bsa_attn_fwd(q, k, v, idx, bias, count, q_block=128, kv_block=4, softmax_sca
     return out, lse
 
 
-def bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_block=4,
-                 softmax_scale=0.0, dq=None, dk=None, dv=None, stream=None):
-    """Gradients of sum(dout * out) for out = bsa_attn_fwd(q, k, v, idx, bias,
-    count, ...) with the plan fixed: (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]) fp32."""
+def _bwd_outputs(q, k, v, out, dout, lse, idx, bias, count, q_block, dq, dk, dv):
     _need(q, torch.bfloat16, "q", 4)
     dev = q.device
     _need(k, torch.bfloat16, "k", 4, device=dev)
@@ -268,10 +270,49 @@ def bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_bloc
     _need(dq, torch.float32, "dq", shape=(B, H, Nq, d), device=dev)
     _need(dk, torch.float32, "dk", shape=(B, H, Nk, d), device=dev)
     _need(dv, torch.float32, "dv", shape=(B, H, Nk, d), device=dev)
+    return (B, H, Nq, Nk, d, L), dq, dk, dv
+
+
+def bsa_attn_bwd(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_block=4,
+                 softmax_scale=0.0, dq=None, dk=None, dv=None, stream=None):
+    """Gradients of sum(dout * out) for out = bsa_attn_fwd(q, k, v, idx, bias,
+    count, ...) with the plan fixed: (dq [B,H,Nq,d], dk, dv [B,H,Nk,d]) fp32."""
+    (B, H, Nq, Nk, d, L), dq, dk, dv = _bwd_outputs(q, k, v, out, dout, lse, idx, bias, count,
+                                                    q_block, dq, dk, dv)
     _check(lib.bsa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), B, H, Nq,
                             Nk, d, q_block, kv_block, _ptr(idx), _ptr(bias), _ptr(count),
                             L, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                             _stream(stream)), "bsa_attn_bwd")
+    return dq, dk, dv
+
+
+def bsa_attn_bwd_workspace_bytes(Nq, Nk, d, max_blocks, q_block=128, kv_block=4) -> int:
+    """Workspace bytes bsa_attn_bwd_ws needs per (b, h) slab."""
+    out = ctypes.c_size_t(0)
+    _check(lib.bsa_attn_bwd_workspace_bytes(Nq, Nk, d, q_block, kv_block, max_blocks,
+                                            ctypes.byref(out)), "bsa_attn_bwd_workspace_bytes")
+    return out.value
+
+
+def bsa_attn_bwd_ws(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_block=4,
+                    softmax_scale=0.0, dq=None, dk=None, dv=None, workspace=None, slabs=None,
+                    stream=None):
+    """bsa_attn_bwd without atomic adds, through a workspace of per-entry
+    partial rows.  Without ``workspace`` one of ``slabs`` (b, h) slabs
+    (default all B*H) is allocated; the call runs as many slabs at a time
+    as the workspace holds."""
+    (B, H, Nq, Nk, d, L), dq, dk, dv = _bwd_outputs(q, k, v, out, dout, lse, idx, bias, count,
+                                                    q_block, dq, dk, dv)
+    if workspace is None:
+        per = bsa_attn_bwd_workspace_bytes(Nq, Nk, d, L, q_block, kv_block)
+        n = B * H if slabs is None else max(1, min(int(slabs), B * H))
+        workspace = torch.empty(per * n, dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace", 1, device=q.device)
+    _check(lib.bsa_attn_bwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), B, H,
+                               Nq, Nk, d, q_block, kv_block, _ptr(idx), _ptr(bias), _ptr(count),
+                               L, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(workspace), workspace.numel(), _stream(stream)),
+           "bsa_attn_bwd_ws")
     return dq, dk, dv
 
 

@@ -41,6 +41,12 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
                     const float *lse, int B, int H, int Nq, int Nk, int d, int kv_block,
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream);
+size_t attn_bwd_slab_bytes(int Nq, int Nk, int d, int kv_block, int max_blocks);
+int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, int B, int H, int Nq, int Nk, int d,
+                       int kv_block, const int32_t *idx, const float *bias, const int32_t *count,
+                       int max_blocks, float scale, float *dq, float *dk, float *dv,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 void basa_offsets(int w, int L, int *b);
 void basa_shifts(int wh, int ww, int L, int S, const int *c_h, const int *c_w, int *dy, int *dx);
 int launch_block_mass(const void *q, const void *k, const float *lse, int B, int H, int Nq, int Nk,
@@ -61,6 +67,32 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 bool pow2_block(int b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool clusters_ok(int c) { return c >= 1 && c <= 16 && (c & (c - 1)) == 0; }
+
+// Checks shared by both backward entry points.
+int attn_bwd_check(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, int B, int H, int Nq, int Nk, int d, int q_block,
+                   int kv_block, const int32_t *idx, const float *bias, const int32_t *count,
+                   int max_blocks, float softmax_scale, float *dq, float *dk, float *dv) {
+  if (!q || !k || !v || !o || !dout || !lse || !idx || !count || !dq || !dk || !dv)
+    return BSA_ERR_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
+  if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
+  if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
+  if (dk == dv || dq == dk || dq == dv) return BSA_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)))
+    return BSA_ERR_ALIGN;
+  const long long nqb = (Nq + 127) / 128;
+  if ((long long)B * H * nqb > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
+  return BSA_OK;
+}
+
+float bwd_scale(float softmax_scale, int d) {
+  return softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
+}
 
 }  // namespace
 
@@ -291,23 +323,43 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
                  const float *lse, int B, int H, int Nq, int Nk, int d, int q_block, int kv_block,
                  const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                  float softmax_scale, float *dq, float *dk, float *dv, void *stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !idx || !count || !dq || !dk || !dv)
-    return BSA_ERR_ARG;
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
-  if (!std::isfinite(softmax_scale)) return BSA_ERR_ARG;
+  const int st = attn_bwd_check(q, k, v, o, dout, lse, B, H, Nq, Nk, d, q_block, kv_block, idx,
+                                bias, count, max_blocks, softmax_scale, dq, dk, dv);
+  if (st != BSA_OK) return st;
+  return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, d, kv_block, idx, bias, count,
+                              max_blocks, bwd_scale(softmax_scale, d), dq, dk, dv,
+                              (hipStream_t)stream);
+}
+
+int bsa_attn_bwd_workspace_bytes(int Nq, int Nk, int d, int q_block, int kv_block,
+                                 int max_blocks, size_t *bytes) {
+  if (!bytes) return BSA_ERR_ARG;
+  if (Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
   if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
-  if (dk == dv || dq == dk || dq == dv) return BSA_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(idx, 4) || !aligned(count, 4) || (bias && !aligned(bias, 4)))
-    return BSA_ERR_ALIGN;
   const long long nqb = (Nq + 127) / 128;
-  if ((long long)B * H * nqb > kMaxIndex) return BSA_ERR_SIZE;
+  if (nqb * max_blocks > kMaxIndex - 63) return BSA_ERR_SIZE;
   if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
   if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d);
-  return bsa::launch_attn_bwd(q, k, v, o, dout, lse, B, H, Nq, Nk, d, kv_block, idx, bias, count,
-                              max_blocks, scale, dq, dk, dv, (hipStream_t)stream);
+  *bytes = bsa::attn_bwd_slab_bytes(Nq, Nk, d, kv_block, max_blocks);
+  return BSA_OK;
+}
+
+int bsa_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                    const float *lse, int B, int H, int Nq, int Nk, int d, int q_block,
+                    int kv_block, const int32_t *idx, const float *bias, const int32_t *count,
+                    int max_blocks, float softmax_scale, float *dq, float *dk, float *dv,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  const int st = attn_bwd_check(q, k, v, o, dout, lse, B, H, Nq, Nk, d, q_block, kv_block, idx,
+                                bias, count, max_blocks, softmax_scale, dq, dk, dv);
+  if (st != BSA_OK) return st;
+  if ((long long)(Nq + 127) / 128 * max_blocks > kMaxIndex - 63) return BSA_ERR_SIZE;
+  if (!workspace) return BSA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;
+  if (workspace_bytes < bsa::attn_bwd_slab_bytes(Nq, Nk, d, kv_block, max_blocks))
+    return BSA_ERR_WORKSPACE;
+  return bsa::launch_attn_bwd_ws(q, k, v, o, dout, lse, B, H, Nq, Nk, d, kv_block, idx, bias,
+                                 count, max_blocks, bwd_scale(softmax_scale, d), dq, dk, dv,
+                                 workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int bsa_mfma_peak_probe(int workgroups, int iters, int operands, float *sink, long long *flops,

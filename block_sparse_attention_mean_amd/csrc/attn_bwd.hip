@@ -23,9 +23,25 @@
 //     from LDS and the wave's K and V rows loaded straight into registers,
 //     then dV += P^T dO and dK += dS^T Q with dO and Q through the
 //     transposing read.  Each key's rows are then added into fp32 dK and dV
-//     in global memory (atomic adds: a key is listed by many query blocks).
+//     in global memory (atomic adds: a key is listed by many query blocks),
+//     or, in the workspace variant, stored as that list entry's partial rows.
 // Outputs are fp32: dQ is written, dK and dV are zeroed by the entry point
 // first.  Head dims 64 and 128.
+//
+// Workspace variant.  A fp32 atomic add runs at a fixed rate of about one
+// dword per clock per L2 channel, whatever the locality, and at the 720p
+// shape the adds (one per key value per listing query block) take most of
+// the backward's time.  The variant removes them: per chunk of (b, h)
+// slabs that fits the caller's workspace,
+//   * a key-major copy of the lists is built: per KV block, the (query
+//     block, entry) pairs that list it (count with integer atomics, an
+//     exclusive scan per slab, a fill through per-block cursors);
+//   * the dkdv kernel stores each listed key's dK and dV rows with plain
+//     stores into the entry's own slot of a partial buffer;
+//   * one wave per KV block sums its entries' partial rows in fp32 and
+//     writes dK and dV, zero for a block no query block lists.
+// The order in which a block's entries are summed is the fill's, which
+// varies from run to run, as the atomic adds' order does.
 #include <type_traits>
 
 #include "common.h"
@@ -121,6 +137,12 @@ struct BwdArgs {
   int Nq, Nk, nqb, max_blocks, kv_shift, M;
   int total_wg;
   float scale, scale_log2;
+  // workspace variant: slabs bh0 .. bh0 + nslab of this chunk, their
+  // partial rows, and the key-major lists (per slab: kstart and kcur of
+  // Ms ints, ent of cap ints)
+  int bh0, nslab, Ms, cap;
+  float *part;
+  int32_t *kstart, *kcur, *ent;
 };
 
 namespace {
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool PART>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;        // row bytes
   constexpr int NCH = D / 8;         // 16-byte chunks per row
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int wg = xcd_order(blockIdx.x, a.total_wg);
   const int qb = wg % a.nqb;
-  const int bh = wg / a.nqb;
+  const int bh = a.bh0 + wg / a.nqb;
   const size_t row_id = (size_t)bh * a.nqb + qb;
   const int32_t *idx_row = a.idx + row_id * a.max_blocks;
   const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
@@ -380,6 +402,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
   const int kvb = 1 << a.kv_shift;
   const int nrow = min(128, a.Nq - qb * 128);
+  // partial rows of this row's entries: key position p of the list (entry
+  // p >> kv_shift, token p & (kvb - 1)) owns 2 D floats, dK then dV
+  float *const prow = PART ? a.part + ((size_t)wg * a.max_blocks << a.kv_shift) * (2 * D) : nullptr;
 
   // Q and dO of the block into LDS (swizzled; rows past Nq are zero)
   {
@@ -529,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
           }
         }
       }
-      // add the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
+      // the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
       // of the wave, lane <-> dim 32 dt + l32
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -538,12 +563,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
           if (row >= 0) {
-            float *dkp = a.dk + ((size_t)bh * a.Nk + row) * D + l32;
-            float *dvp = a.dv + ((size_t)bh * a.Nk + row) * D + l32;
+            if (PART) {
+              // plain stores into the entry's partial rows
+              const int p = (base << a.kv_shift) + t * KT + wave * 32 + 8 * g + 4 * hh + j;
+              float *dst = prow + (size_t)p * (2 * D) + l32;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              unsafeAtomicAdd(dkp + dt * 32, dkacc[dt][4 * g + j] * a.scale);
-              unsafeAtomicAdd(dvp + dt * 32, dvacc[dt][4 * g + j]);
+              for (int dt = 0; dt < DT; ++dt) {
+                dst[dt * 32] = dkacc[dt][4 * g + j] * a.scale;
+                dst[D + dt * 32] = dvacc[dt][4 * g + j];
+              }
+            } else {
+              float *dkp = a.dk + ((size_t)bh * a.Nk + row) * D + l32;
+              float *dvp = a.dv + ((size_t)bh * a.Nk + row) * D + l32;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) {
+                unsafeAtomicAdd(dkp + dt * 32, dkacc[dt][4 * g + j] * a.scale);
+                unsafeAtomicAdd(dvp + dt * 32, dvacc[dt][4 * g + j]);
+              }
             }
           }
         }
@@ -557,6 +593,131 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4 *p, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) p[i] = z;
 }
 
+// Block of list entry e when it contributes keys (inside [0, M), shift
+// above -inf: the rule the staging of the dkdv kernel applies), else -1.
+__device__ __forceinline__ int entry_block(const BwdArgs &a, const int32_t *idx_row,
+                                           const float *bias_row, int e) {
+  const int blk = idx_row[e];
+  const float sh = bias_row ? bias_row[e] * kLog2e : 0.f;
+  return (blk >= 0 && blk < a.M && sh > -__builtin_inff()) ? blk : -1;
+}
+
+// Key-major lists, pass 1 (FILL = false): count the entries listing each
+// block; pass 2 (FILL = true): write (row of the chunk) * max_blocks +
+// entry at the block's cursor.  One workgroup per row of the chunk.
+template <bool FILL>
+__global__ __launch_bounds__(256) void csr_pass_kernel(BwdArgs a) {
+  const int r = blockIdx.x;
+  const int s = r / a.nqb;
+  const size_t row_id = (size_t)(a.bh0 + s) * a.nqb + r % a.nqb;
+  const int32_t *idx_row = a.idx + row_id * a.max_blocks;
+  const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
+  int cnt = a.count[row_id];
+  cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
+  for (int e = threadIdx.x; e < cnt; e += 256) {
+    const int blk = entry_block(a, idx_row, bias_row, e);
+    if (blk < 0) continue;
+    if (FILL) {
+      const int pos = atomicAdd(&a.kcur[(size_t)s * a.Ms + blk], 1);
+      a.ent[(size_t)s * a.cap + pos] = r * a.max_blocks + e;
+    } else {
+      atomicAdd(&a.kstart[(size_t)s * a.Ms + blk], 1);
+    }
+  }
+}
+
+// Exclusive scan of one slab's counts, in place: kstart[b] = entries of
+// blocks before b, kstart[M] = all; kcur = kstart.  One workgroup per slab.
+__global__ __launch_bounds__(1024) void csr_scan_kernel(BwdArgs a) {
+  __shared__ int part[1024];
+  int32_t *ks = a.kstart + (size_t)blockIdx.x * a.Ms;
+  int32_t *kc = a.kcur + (size_t)blockIdx.x * a.Ms;
+  const int t = threadIdx.x;
+  const int per = (a.M + 1023) / 1024;
+  const int lo = min(a.M, t * per), hi = min(a.M, lo + per);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += ks[b];
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int b = lo; b < hi; ++b) {
+    const int c = ks[b];
+    ks[b] = run;
+    kc[b] = run;
+    run += c;
+  }
+  if (t == 1023) ks[a.M] = part[1023];
+}
+
+// dK and dV of one KV block (one wave): the sum, in fp32, of the partial
+// rows of every entry that lists it; rows at or past Nk are not written.
+// Lane l handles the 16-byte pieces c = c0 + l + 64 u of the block's
+// kvb * 2D floats (token c / (D/2); dK for the first D/4 pieces of a
+// token, dV for the rest).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63;
+  const long long gw = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= (long long)a.nslab * a.M) return;
+  const int s = (int)(gw / a.M), b = (int)(gw % a.M);
+  const int32_t *ks = a.kstart + (size_t)s * a.Ms;
+  const int beg = ks[b], end = ks[b + 1];
+  const int32_t *ent = a.ent + (size_t)s * a.cap;
+  const int kvb = 1 << a.kv_shift;
+  const size_t F4 = (size_t)kvb * (D / 2);                // pieces per entry
+  const int ntok = min(kvb, a.Nk - b * kvb);
+  const int nv = ntok * (D / 2);                          // pieces written
+  const f32x4 *part = (const f32x4 *)a.part;
+  const size_t key0 = (size_t)(a.bh0 + s) * a.Nk + (size_t)b * kvb;
+  for (int c0 = 0; c0 < nv; c0 += 64 * U) {
+    f32x4 acc[U];
+    bool on[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      on[u] = c0 + lane + 64 * u < nv;
+    }
+    const size_t cl = (size_t)(c0 + lane);
+    int p = beg;
+    for (; p + 4 <= end; p += 4) {
+      f32x4 x[4][U];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 *src = part + (size_t)ent[p + i] * F4 + cl;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u]) x[i][u] = src[64 * u];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u]) acc[u] += x[i][u];
+    }
+    for (; p < end; ++p) {
+      const f32x4 *src = part + (size_t)ent[p] * F4 + cl;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (on[u]) acc[u] += src[64 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!on[u]) continue;
+      const int c = c0 + lane + 64 * u;
+      const int j = c / (D / 2), w = c % (D / 2);
+      float *dst = w < D / 4 ? a.dk + (key0 + j) * D + 4 * w : a.dv + (key0 + j) * D + 4 * (w - D / 4);
+      *(f32x4 *)dst = acc[u];
+    }
+  }
+}
+
 }  // namespace
 
 int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -564,7 +725,7 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream) {
   clear_pending_error();
-  BwdArgs a;
+  BwdArgs a{};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v;
@@ -593,10 +754,108 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
   hipLaunchKernelGGL(zero_kernel, dim3(zg), dim3(256), 0, stream, (f32x4 *)dv, n4);
   if (d == 128) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), dim3((unsigned)total), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), dim3((unsigned)total), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, false>), dim3((unsigned)total), dim3(256), 0,
+                       stream, a);
   } else {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), dim3((unsigned)total), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), dim3((unsigned)total), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, false>), dim3((unsigned)total), dim3(256), 0,
+                       stream, a);
+  }
+  return status_of(hipGetLastError());
+}
+
+namespace {
+
+struct SlabLayout {
+  size_t part_bytes;  // partial rows of one slab
+  int Ms, cap;        // ints per slab of kstart / kcur, and of ent
+  size_t bytes;       // all of one slab
+};
+
+SlabLayout slab_layout(int Nq, int Nk, int d, int kv_block, int max_blocks) {
+  SlabLayout L;
+  const size_t nqb = (size_t)(Nq + 127) / 128;
+  const size_t M = ((size_t)Nk + kv_block - 1) / kv_block;
+  L.part_bytes = nqb * max_blocks * kv_block * 2 * d * sizeof(float);  // a multiple of 512
+  L.Ms = (int)((M + 1 + 63) / 64 * 64);
+  L.cap = (int)((nqb * max_blocks + 63) / 64 * 64);
+  L.bytes = L.part_bytes + 2 * (size_t)L.Ms * 4 + (size_t)L.cap * 4;  // 256-byte multiples
+  return L;
+}
+
+}  // namespace
+
+size_t attn_bwd_slab_bytes(int Nq, int Nk, int d, int kv_block, int max_blocks) {
+  return slab_layout(Nq, Nk, d, kv_block, max_blocks).bytes;
+}
+
+int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, int B, int H, int Nq, int Nk, int d,
+                       int kv_block, const int32_t *idx, const float *bias, const int32_t *count,
+                       int max_blocks, float scale, float *dq, float *dk, float *dv,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_pending_error();
+  const SlabLayout L = slab_layout(Nq, Nk, d, kv_block, max_blocks);
+  const int BH = B * H;
+  long long per = (long long)(workspace_bytes / L.bytes);
+  per = per < BH ? per : BH;
+  const long long by_index = 0x7fffffffLL / L.cap;  // ent values and the fill's positions
+  per = per < by_index ? per : by_index;
+  if (per < 1) return BSA_ERR_WORKSPACE;
+  BwdArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout;
+  a.lse = lse;
+  a.idx = idx;
+  a.bias = bias;
+  a.count = count;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.nqb = (Nq + 127) / 128;
+  a.max_blocks = max_blocks;
+  a.kv_shift = __builtin_ctz((unsigned)kv_block);
+  a.M = (Nk + kv_block - 1) / kv_block;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.Ms = L.Ms;
+  a.cap = L.cap;
+  a.total_wg = BH * a.nqb;
+  if (d == 128)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
+  unsigned char *ws = (unsigned char *)workspace;
+  for (int bh0 = 0; bh0 < BH; bh0 += (int)per) {
+    const int n = (int)(BH - bh0 < per ? BH - bh0 : per);
+    a.bh0 = bh0;
+    a.nslab = n;
+    a.part = (float *)ws;
+    a.kstart = (int32_t *)(ws + (size_t)n * L.part_bytes);
+    a.kcur = a.kstart + (size_t)n * L.Ms;
+    a.ent = a.kcur + (size_t)n * L.Ms;
+    a.total_wg = n * a.nqb;
+    const size_t z4 = (size_t)n * L.Ms / 4;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)min((size_t)8192, (z4 + 255) / 256)), dim3(256),
+                       0, stream, (f32x4 *)a.kstart, z4);
+    hipLaunchKernelGGL((csr_pass_kernel<false>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)n), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL((csr_pass_kernel<true>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
+    const unsigned rg = (unsigned)(((long long)n * a.M + 3) / 4);
+    if (d == 128) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, true>), dim3((unsigned)a.total_wg), dim3(256),
+                         0, stream, a);
+      hipLaunchKernelGGL((bwd_reduce_kernel<128>), dim3(rg), dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, true>), dim3((unsigned)a.total_wg), dim3(256),
+                         0, stream, a);
+      hipLaunchKernelGGL((bwd_reduce_kernel<64>), dim3(rg), dim3(256), 0, stream, a);
+    }
   }
   return status_of(hipGetLastError());
 }

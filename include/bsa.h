@@ -231,6 +231,34 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
                  float softmax_scale, float *dq, float *dk, float *dv, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The same gradients as bsa_attn_bwd (same definition, arguments and
+ * outputs), with no atomic adds: each listed key's dK and dV rows go into
+ * a per-entry slot of the caller's workspace, and one pass per KV block
+ * sums the slots of every entry that lists it and writes dk and dv (every
+ * row; zero for a block no query block lists).  The order of that sum
+ * varies from run to run, so the last bits of dk and dv may too.
+ *
+ * bsa_attn_bwd_workspace_bytes (host, no GPU) reports the bytes one
+ * (b, h) slab needs:
+ *   nQB * max_blocks * kv_block * 2 * d * 4   partial rows (fp32),
+ * plus the slab's key-major lists (about 4 * (2 M + nQB * max_blocks)).
+ * The call processes as many slabs at a time as workspace_bytes holds
+ * (all B*H when it holds that many) and returns BSA_ERR_WORKSPACE when it
+ * holds less than one, or workspace is NULL; workspace must be 256-byte
+ * aligned (BSA_ERR_ALIGN) and its contents are undefined after the call.
+ * nQB * max_blocks above 2^31 - 64 returns BSA_ERR_SIZE.  Other errors are
+ * bsa_attn_bwd's.
+ * --------------------------------------------------------------------- */
+int bsa_attn_bwd_workspace_bytes(int Nq, int Nk, int d, int q_block, int kv_block,
+                                 int max_blocks, size_t *bytes /* host out */);
+
+int bsa_attn_bwd_ws(const void *q, const void *k, const void *v, const void *out,
+                    const void *dout, const float *lse, int B, int H, int Nq, int Nk, int d,
+                    int q_block, int kv_block, const int32_t *idx, const float *bias,
+                    const int32_t *count, int max_blocks, float softmax_scale, float *dq,
+                    float *dk, float *dv, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * BASA-structured lists (BASA page, onedev.kr/papers/688).
  *
  * Geometry: a latent grid T x Hg x Wg (token n = (t*Hg + y)*Wg + x) is

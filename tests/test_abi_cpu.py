@@ -217,6 +217,49 @@ def test_attn_bwd_rejects_invalid_arguments(bsa, kw, status):
     assert _bwd(bsa, **kw) == status
 
 
+def _bwd_ws(bsa, ws=FAKE + 65536, ws_bytes=1 << 40, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, Nq=300, Nk=300, d=128,
+             qb=128, kvb=4, idx=FAKE, bias=None, cnt=FAKE, L=8, scale=0.0, dq=FAKE,
+             dk=FAKE + 4096, dv=FAKE + 8192)
+    a.update(kw)
+    return bsa.lib.bsa_attn_bwd_ws(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["B"],
+                                   a["H"], a["Nq"], a["Nk"], a["d"], a["qb"], a["kvb"], a["idx"],
+                                   a["bias"], a["cnt"], a["L"], a["scale"], a["dq"], a["dk"],
+                                   a["dv"], ws, ws_bytes, None)
+
+
+def test_attn_bwd_workspace_bytes(bsa):
+    """One (b, h) slab: nQB * max_blocks * kv_block * 2d fp32 partial rows,
+    plus the key-major lists (two arrays of M + 1 ints and one of nQB *
+    max_blocks ints, each padded to 64 ints)."""
+    for Nq, Nk, d, kvb, L in [(300, 300, 128, 4, 8), (75600, 75600, 128, 4, 2048),
+                              (256, 260, 64, 1, 70), (1000, 1000, 128, 128, 3)]:
+        got = bsa.bsa_attn_bwd_workspace_bytes(Nq, Nk, d, L, 128, kvb)
+        nqb, M = -(-Nq // 128), -(-Nk // kvb)
+        pad = lambda n: -(-n // 64) * 64  # noqa: E731
+        assert got == nqb * L * kvb * 2 * d * 4 + 4 * (2 * pad(M + 1) + pad(nqb * L))
+        assert got % 256 == 0
+    out = ctypes.c_size_t(0)
+    L = bsa.lib
+    assert L.bsa_attn_bwd_workspace_bytes(300, 300, 128, 128, 4, 8, None) == -1
+    assert L.bsa_attn_bwd_workspace_bytes(0, 300, 128, 128, 4, 8, ctypes.byref(out)) == -1
+    assert L.bsa_attn_bwd_workspace_bytes(300, 300, 96, 128, 4, 8, ctypes.byref(out)) == -2
+    assert L.bsa_attn_bwd_workspace_bytes(300, 300, 128, 128, 3, 8, ctypes.byref(out)) == -2
+    assert L.bsa_attn_bwd_workspace_bytes(2**24, 300, 128, 128, 1, 2**20, ctypes.byref(out)) == -7
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), -1), (dict(dk=None), -1), (dict(dv=FAKE + 4096), -1), (dict(d=96), -2),
+    (dict(dq=FAKE + 4), -4), (dict(ws=None), -6), (dict(ws_bytes=4096), -6),
+    (dict(ws=FAKE + 65536 + 128), -4), (dict(Nq=2**24, kvb=1, L=2**20), -7),
+])
+def test_attn_bwd_ws_rejects_invalid_arguments(bsa, kw, status):
+    """The workspace backward refuses what bsa_attn_bwd refuses, a missing,
+    misaligned or too small workspace, and lists whose entry count exceeds
+    the index range, before any HIP call."""
+    assert _bwd_ws(bsa, **kw) == status
+
+
 def test_binding_loads_the_library_into_torchs_hip_runtime():
     """Importing the binding in a fresh process maps a single HIP runtime:
     the one torch carries.  (Loaded before torch, libbsa.so would bring in

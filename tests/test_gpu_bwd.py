@@ -1,5 +1,5 @@
-"""GPU parity of bsa_attn_bwd against the fp64 oracle (oracle/attn.py:
-attn_bwd) on plans built by the oracle.  The device gets the oracle's
+"""GPU parity of bsa_attn_bwd and bsa_attn_bwd_ws against the fp64 oracle
+(oracle/attn.py: attn_bwd) on plans built by the oracle.  The device gets the oracle's
 forward output rounded to bf16 and its log-sum-exp rounded to fp32 (the
 inputs the forward kernel would hand over); the oracle keeps its exact
 values.
@@ -9,7 +9,8 @@ Tolerance (per tensor, over the rows checked): relative Frobenius error
 device rounds P and dS to bf16 before the two products that use them (a
 random relative error of 2^-9 per term, averaged over the contraction),
 takes D = dO . O from the bf16 forward output, and sums in fp32; dK and dV
-add contributions of many query blocks with fp32 atomics."""
+add contributions of many query blocks with fp32 atomics (bsa_attn_bwd) or
+sum per-entry partial rows in fp32 (bsa_attn_bwd_ws)."""
 import numpy as np
 import pytest
 
@@ -22,6 +23,14 @@ pytestmark = pytest.mark.gpu
 
 REL_FRO = 1e-2
 MAX_ABS_FRAC = 2e-2
+VARIANTS = ("atomic", "ws")
+
+
+def _bwd(bsa, variant, *args, slabs=None, **kw):
+    """One backward call through the atomic or the workspace entry point."""
+    if variant == "atomic":
+        return bsa.bsa_attn_bwd(*args, **kw)
+    return bsa.bsa_attn_bwd_ws(*args, slabs=slabs, **kw)
 
 
 @pytest.fixture(scope="module")
@@ -60,17 +69,17 @@ def _oracle_fwd(q, k, v, kvb, idx, bias, cnt):
     return np.nan_to_num(O), np.where(np.isnan(lse), -np.inf, lse)
 
 
-def _run(env, q, k, v, dout, kvb, idx, bias, cnt):
+def _run(env, variant, q, k, v, dout, kvb, idx, bias, cnt):
     """Device backward of one head (B = H = 1) with the oracle's forward
     (valid list entries only)."""
     bsa, g, torch = env
     O, lse = _oracle_fwd(q, k, v, kvb, idx, bias, cnt)
     ob = f64_to_bf16_bits(O)
     dev = lambda x: g.to_dev_bf16(f64_to_bf16_bits(x)[None, None])  # noqa: E731
-    dq, dk, dv = bsa.bsa_attn_bwd(dev(q), dev(k), dev(v), g.to_dev_bf16(ob[None, None]), dev(dout),
-                                  g.dev_f32(lse[None, None]), g.dev_i32(idx[None, None]),
-                                  None if bias is None else g.dev_f32(bias[None, None]),
-                                  g.dev_i32(cnt[None, None]), 128, kvb)
+    dq, dk, dv = _bwd(bsa, variant, dev(q), dev(k), dev(v), g.to_dev_bf16(ob[None, None]),
+                      dev(dout), g.dev_f32(lse[None, None]), g.dev_i32(idx[None, None]),
+                      None if bias is None else g.dev_f32(bias[None, None]),
+                      g.dev_i32(cnt[None, None]), 128, kvb)
     torch.cuda.synchronize()
     return dq.cpu().numpy()[0, 0], dk.cpu().numpy()[0, 0], dv.cpu().numpy()[0, 0]
 
@@ -90,28 +99,32 @@ def _inputs(Nq, Nk, seed, d=128):
     (300, 300, 4, 20, opl.SIP, 64), (256, 260, 1, 70, opl.SIP, 64), (640, 2048, 64, 8, opl.TOPK, 64),
     (130, 2048, 2, 600, opl.SIP, 64),
 ])
-def test_bwd_matches_oracle(env, Nq, Nk, kvb, s, mode, d):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bwd_matches_oracle(env, variant, Nq, Nk, kvb, s, mode, d):
     """Ragged query and key counts (a partial last KV block), block sizes 1-128,
     SIP shifts and top-k, lists longer than one staging phase, d = 64 and 128."""
     bsa, g, torch = env
-    g.say(f"case bwd Nq={Nq} Nk={Nk} kv={kvb} s={s} mode={mode} d={d}")
+    g.say(f"case bwd {variant} Nq={Nq} Nk={Nk} kv={kvb} s={s} mode={mode} d={d}")
     q, k, v, dout = _inputs(Nq, Nk, seed=Nq + kvb, d=d)
     nqb, M = -(-Nq // 128), -(-Nk // kvb)
     idx, bias, cnt, _ = _plan(nqb, M, s, mode, seed=Nk)
-    gq, gk, gv = _run(env, q, k, v, dout, kvb, idx, bias if mode == opl.SIP else None, cnt)
+    gq, gk, gv = _run(env, variant, q, k, v, dout, kvb, idx, bias if mode == opl.SIP else None,
+                      cnt)
     wq, wk, wv = oat.attn_bwd(q, k, v, dout, 128, kvb, idx, bias if mode == opl.SIP else None, cnt)
     _close(g, gq, wq, "dq")
     _close(g, gk, wk, "dk")
     _close(g, gv, wv, "dv")
 
 
-def test_bwd_edge_lists(env):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bwd_edge_lists(env, variant):
     """Invalid entries (negative, past M), a repeated block (two sets of keys),
     an empty list, count beyond the list and a block holding keys past Nk:
     the device on the raw list against the oracle, whose forward (for the
-    device's inputs) runs on the list's valid entries."""
+    device's inputs) runs on the list's valid entries.  dk and dv start as
+    NaN: every row, listed or not, must be written."""
     bsa, g, torch = env
-    g.say("case bwd edge lists")
+    g.say(f"case bwd {variant} edge lists")
     Nq, Nk, kvb = 384, 257, 4
     q, k, v, dout = _inputs(Nq, Nk, seed=5)
     M = -(-Nk // kvb)
@@ -129,9 +142,11 @@ def test_bwd_edge_lists(env):
         ci[i, :len(keep)], cb[i, :len(keep)], cc[i] = idx[i, keep], bias[i, keep], len(keep)
     O, lse = _oracle_fwd(q, k, v, kvb, ci, cb, cc)
     dev = lambda x: g.to_dev_bf16(f64_to_bf16_bits(x)[None, None])  # noqa: E731
-    gq, gk, gv = bsa.bsa_attn_bwd(dev(q), dev(k), dev(v), dev(O), dev(dout),
-                                  g.dev_f32(lse[None, None]), g.dev_i32(idx[None, None]),
-                                  g.dev_f32(bias[None, None]), g.dev_i32(cnt[None, None]), 128, kvb)
+    nan = torch.full((1, 1, Nk, 128), float("nan"), dtype=torch.float32, device="cuda")
+    gq, gk, gv = _bwd(bsa, variant, dev(q), dev(k), dev(v), dev(O), dev(dout),
+                      g.dev_f32(lse[None, None]), g.dev_i32(idx[None, None]),
+                      g.dev_f32(bias[None, None]), g.dev_i32(cnt[None, None]), 128, kvb,
+                      dk=nan.clone(), dv=nan.clone())
     torch.cuda.synchronize()
     gq, gk, gv = (x.cpu().numpy()[0, 0] for x in (gq, gk, gv))
     wq, wk, wv = oat.attn_bwd(q, k, v, dout, 128, kvb, idx, bias, cnt)
@@ -141,10 +156,13 @@ def test_bwd_edge_lists(env):
     _close(g, gv, wv, "dv")
 
 
-def test_bwd_batch_heads(env):
-    """B = 2, H = 2 in one call: every (b, h) against the oracle."""
+@pytest.mark.parametrize("variant,slabs", [("atomic", None), ("ws", None), ("ws", 1), ("ws", 3)])
+def test_bwd_batch_heads(env, variant, slabs):
+    """B = 2, H = 2 in one call: every (b, h) against the oracle.  The
+    workspace variant also runs with room for one slab (four passes) and
+    for three (a pass of three, then one)."""
     bsa, g, torch = env
-    g.say("case bwd batch and heads")
+    g.say(f"case bwd {variant} slabs={slabs} batch and heads")
     B, H, N, kvb, s = 2, 2, 400, 4, 25
     nqb, M = -(-N // 128), N // 4
     qs, ks, vs, ds, Os, ls, ids, bs, cs = ([] for _ in range(9))
@@ -158,8 +176,9 @@ def test_bwd_batch_heads(env):
                 lst.append(x)
     st = lambda xs: np.stack(xs).reshape((B, H) + xs[0].shape)  # noqa: E731
     bf = lambda xs: g.to_dev_bf16(f64_to_bf16_bits(st(xs)))  # noqa: E731
-    dq, dk, dv = bsa.bsa_attn_bwd(bf(qs), bf(ks), bf(vs), bf(Os), bf(ds), g.dev_f32(st(ls)),
-                                  g.dev_i32(st(ids)), g.dev_f32(st(bs)), g.dev_i32(st(cs)), 128, kvb)
+    dq, dk, dv = _bwd(bsa, variant, bf(qs), bf(ks), bf(vs), bf(Os), bf(ds), g.dev_f32(st(ls)),
+                      g.dev_i32(st(ids)), g.dev_f32(st(bs)), g.dev_i32(st(cs)), 128, kvb,
+                      slabs=slabs)
     torch.cuda.synchronize()
     for b in range(B):
         for h in range(H):
@@ -175,7 +194,9 @@ def test_bwd_full_size_sampled(env):
     18,900 4-token blocks): the device forward's output and LSE feed the
     device backward; dQ of sampled query blocks (including the 80-row last)
     and dK/dV of sampled KV blocks (all query blocks that list them) against
-    the oracle."""
+    the oracle.  The workspace variant against the oracle on the same
+    samples, and against the atomic one on every row: dq bit for bit (the
+    same kernel), dk and dv to fp32 summation-order error."""
     bsa, g, torch = env
     c = CONFIGS["wan14b_720p"]
     g.say("case bwd full size wan14b_720p head 0")
@@ -187,8 +208,15 @@ def test_bwd_full_size_sampled(env):
     di, dbias, dc = g.dev_i32(idx[None, None]), g.dev_f32(bias[None, None]), g.dev_i32(cnt[None, None])
     out, lse = bsa.bsa_attn_fwd(q, k, v, di, dbias, dc, 128, 4, want_lse=True)
     gq, gk, gv = bsa.bsa_attn_bwd(q, k, v, out, dq_, lse, di, dbias, dc, 128, 4)
+    g.say("  workspace variant")
+    sq, sk, sv = bsa.bsa_attn_bwd_ws(q, k, v, out, dq_, lse, di, dbias, dc, 128, 4)
     torch.cuda.synchronize()
-    gq, gk, gv = (x.cpu().numpy()[0, 0] for x in (gq, gk, gv))
+    gq, gk, gv, sq, sk, sv = (x.cpu().numpy()[0, 0] for x in (gq, gk, gv, sq, sk, sv))
+    assert np.array_equal(gq, sq)
+    for a_, b_, what in ((gk, sk, "dk"), (gv, sv, "dv")):
+        fro = float(np.sqrt(((a_.astype(np.float64) - b_) ** 2).sum() / (a_.astype(np.float64) ** 2).sum()))
+        g.say(f"  {what} workspace vs atomic: rel fro {fro:.2e}")
+        assert fro <= 1e-5, f"{what}: workspace and atomic variants differ by {fro}"
     q64, k64, v64, d64 = (bf16_bits_to_f64(x[0, 0]) for x in (qb, kb, vb, db))
     nqb = idx.shape[0]
     qblocks = [0, 1, 300, nqb - 1]
@@ -202,3 +230,5 @@ def test_bwd_full_size_sampled(env):
     krows = np.concatenate([np.arange(j * 4, j * 4 + 4) for j in kvblocks])
     _close(g, gk, wk, "dk sampled KV blocks", krows)
     _close(g, gv, wv, "dv sampled KV blocks", krows)
+    _close(g, sk, wk, "dk (workspace) sampled KV blocks", krows)
+    _close(g, sv, wv, "dv (workspace) sampled KV blocks", krows)
