@@ -60,12 +60,23 @@ def test_attn_bwd_checks(env):
     bad = [dict(dout=_t(torch, (1, 1, 255, 64), bf)), dict(lse=_t(torch, (1, 1, 128), f32)),
            dict(out=_t(torch, (1, 1, 256, 64), f32)), dict(v=_t(torch, (1, 1, 129, 64), bf)),
            dict(dk=_t(torch, (1, 1, 256, 64), f32)), dict(dq=_t(torch, (1, 1, 256, 64), bf))]
+    names = ("q", "k", "v", "out", "dout", "lse", "idx", "bias", "count")
     for b in bad:
         kw = dict(base, **b)
         extra = {x: kw.pop(x) for x in ("dq", "dk", "dv") if x in kw}
+        for fn in (bsa.bsa_attn_bwd, bsa.bsa_attn_bwd_ws):
+            with pytest.raises(ValueError):
+                fn(*[kw[n] for n in names], 128, 4, **extra)
+    # the workspace form: a workspace of the wrong dtype or device is refused
+    # by the binding; one smaller than a slab by the library (no launch)
+    args = [base[n] for n in names]
+    for ws in (_t(torch, (4096,), f32), _t(torch, (4096,), torch.uint8).cpu()):
         with pytest.raises(ValueError):
-            bsa.bsa_attn_bwd(*[kw[n] for n in ("q", "k", "v", "out", "dout", "lse", "idx", "bias",
-                                               "count")], 128, 4, **extra)
+            bsa.bsa_attn_bwd_ws(*args, 128, 4, workspace=ws)
+    need = bsa.bsa_attn_bwd_workspace_bytes(256, 128, 64, 4, 128, 4)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_attn_bwd_ws(*args, 128, 4, workspace=_t(torch, (need - 256,), torch.uint8))
+    assert e.value.status == -6
 
 
 def test_plan_and_select_checks(env):
