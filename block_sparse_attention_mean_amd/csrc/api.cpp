@@ -353,6 +353,9 @@ int bsa_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o, 
                                 bias, count, max_blocks, softmax_scale, dq, dk, dv);
   if (st != BSA_OK) return st;
   if ((long long)(Nq + 127) / 128 * max_blocks > kMaxIndex - 63) return BSA_ERR_SIZE;
+  // one wave per KV block of every slab in the per-block sums' grid
+  if ((long long)B * H * (((long long)Nk + kv_block - 1) / kv_block) > kMaxIndex * 4)
+    return BSA_ERR_SIZE;
   if (!workspace) return BSA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BSA_ERR_ALIGN;
   if (workspace_bytes < bsa::attn_bwd_slab_bytes(Nq, Nk, d, kv_block, max_blocks))

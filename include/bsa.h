@@ -18,7 +18,9 @@
  *                      blocks into full tiles, shifts logits by -log pi,
  *                      and runs online softmax with P.V accumulation (same
  *                      page, section "전제와 한계", first paragraph);
- *   bsa_attn_bwd       its gradients dQ, dK, dV with the plan held fixed;
+ *   bsa_attn_bwd,      its gradients dQ, dK, dV with the plan held fixed
+ *   bsa_attn_bwd_ws    (dK and dV by atomic adds, or by sums of per-entry
+ *                      partial rows in a caller's workspace);
  *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
  *                      structure of the BASA page (onedev.kr/papers/688,
  *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
@@ -246,8 +248,8 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
  * (all B*H when it holds that many) and returns BSA_ERR_WORKSPACE when it
  * holds less than one, or workspace is NULL; workspace must be 256-byte
  * aligned (BSA_ERR_ALIGN) and its contents are undefined after the call.
- * nQB * max_blocks above 2^31 - 64 returns BSA_ERR_SIZE.  Other errors are
- * bsa_attn_bwd's.
+ * nQB * max_blocks above 2^31 - 64, or B * H * M above 2^33 (M = KV
+ * blocks of Nk), returns BSA_ERR_SIZE.  Other errors are bsa_attn_bwd's.
  * --------------------------------------------------------------------- */
 int bsa_attn_bwd_workspace_bytes(int Nq, int Nk, int d, int q_block, int kv_block,
                                  int max_blocks, size_t *bytes /* host out */);

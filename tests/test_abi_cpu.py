@@ -252,6 +252,7 @@ def test_attn_bwd_workspace_bytes(bsa):
     (dict(o=None), -1), (dict(dk=None), -1), (dict(dv=FAKE + 4096), -1), (dict(d=96), -2),
     (dict(dq=FAKE + 4), -4), (dict(ws=None), -6), (dict(ws_bytes=4096), -6),
     (dict(ws=FAKE + 65536 + 128), -4), (dict(Nq=2**24, kvb=1, L=2**20), -7),
+    (dict(B=2**12, H=2**12, Nk=2**20, kvb=1, Nq=128), -7),
 ])
 def test_attn_bwd_ws_rejects_invalid_arguments(bsa, kw, status):
     """The workspace backward refuses what bsa_attn_bwd refuses, a missing,
