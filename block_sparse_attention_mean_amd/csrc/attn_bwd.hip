@@ -341,6 +341,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     if (t + 2 < ntiles) issue(std::integral_constant<int, (S + 2) % NBUF>(), t + 2);
     compute(slot_c);
   };
+  // while tile t + 2 exists: the same step without conditions, under the
+  // backend's hint to interleave LDS reads and matrix operations (at the
+  // Wan2.1-14B 720p shape, interleaved on one box, the whole workspace
+  // backward 110.2 against 110.9 ms, dQ unchanged bit for bit)
+  auto step_full = [&](auto slot_c, int t) {
+    constexpr int S = decltype(slot_c)::value;
+    __builtin_amdgcn_iglp_opt(0);
+    ring_barrier<LPT>();
+    issue(std::integral_constant<int, (S + 2) % NBUF>(), t + 2);
+    compute(slot_c);
+  };
 
   for (int base = 0; base < cnt; base += CAP) {
     const int pc = min(CAP, cnt - base);
@@ -351,7 +362,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
     if (ntiles > 0) issue(std::integral_constant<int, 0>(), 0);
     if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
-    for (int t = 0; t < ntiles; t += 3) {
+    int t = 0;
+    for (; t + 4 < ntiles; t += 3) {
+      step_full(std::integral_constant<int, 0>(), t);
+      step_full(std::integral_constant<int, 1>(), t + 1);
+      step_full(std::integral_constant<int, 2>(), t + 2);
+    }
+    for (; t < ntiles; t += 3) {
       step(std::integral_constant<int, 0>(), t);
       if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
       if (t + 2 < ntiles) step(std::integral_constant<int, 2>(), t + 2);
