@@ -25,8 +25,8 @@
 //     transposing read.  Each key's rows are then added into fp32 dK and dV
 //     in global memory (atomic adds: a key is listed by many query blocks),
 //     or, in the workspace variant, stored as that list entry's partial rows.
-// Outputs are fp32: dQ is written, dK and dV are zeroed by the entry point
-// first.  Head dims 64 and 128.
+// Outputs are fp32: dQ is written; the atomic form zeroes dK and dV first,
+// the workspace form writes every row of them.  Head dims 64 and 128.
 //
 // Workspace variant.  A fp32 atomic add runs at a fixed rate of about one
 // dword per clock per L2 channel, whatever the locality, and at the 720p
