@@ -19,7 +19,7 @@ Follows the BASA page (onedev.kr/papers/688):
   raw keys and values; window i attends to W_i U R_i U G; queries and output
   keep their length.
 
-Readings (listed in the design doc): roll by -Delta means y' = (y - dy) mod Hg,
+Readings where the page is silent: roll by -Delta means y' = (y - dy) mod Hg,
 x' = (x - dx) mod Wg; a ragged last window row/column keeps its smaller
 size; the candidate set is every other window; key descriptor = mean key of
 the window over all frames; ties go to the lowest window index; pooling is

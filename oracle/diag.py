@@ -13,7 +13,7 @@ Follows the AB-Attention page (onedev.kr/papers/1521):
   means instead of clustering, no pi weighting, uniform sampling, selection
   at the execution tile).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * the attention mass of KV block j for query block i is the mean, over the
   block's queries n, of the dense softmax probability (all Nk keys, scale

@@ -13,7 +13,7 @@ Follows the AB-Attention page (onedev.kr/papers/1521), section "무엇과 다른
 * a KV block's score is the share-weighted average, over the clusters, of the
   softmax mass that the centroid puts on that block's pooled key.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
 
 * pooled key = mean of the block's keys (the last block averages its valid
   rows only);
