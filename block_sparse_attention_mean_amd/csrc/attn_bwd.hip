@@ -36,10 +36,14 @@
 //   * a key-major copy of the lists is built: per KV block, the (query
 //     block, entry) pairs that list it (count with integer atomics, an
 //     exclusive scan per slab, a fill through per-block cursors);
-//   * the dkdv kernel stores each listed key's dK and dV rows with plain
-//     stores into the entry's own slot of a partial buffer;
+//   * the dkdv kernel stores each listed key's dK (unscaled) and dV rows
+//     with plain stores into the entry's own slot of a partial buffer, a
+//     pass's rows during the next pass (two sets of accumulators), so the
+//     stores spread over the products instead of ending each pass in a
+//     burst;
 //   * one wave per KV block sums its entries' partial rows in fp32 and
-//     writes dK and dV, zero for a block no query block lists.
+//     writes dK (times the softmax scale) and dV, zero for a block no
+//     query block lists.
 // The order in which a block's entries are summed is the fill's, which
 // varies from run to run, as the atomic adds' order does.
 #include <type_traits>
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
   __shared__ __attribute__((aligned(16))) float sh_s[CAP];
   __shared__ __attribute__((aligned(16))) float dq_s[128], lq_s[128];
-  __shared__ __attribute__((aligned(16))) int32_t keyrow_s[NW][32];
+  __shared__ __attribute__((aligned(16))) int32_t keyrow2_s[PART ? 2 : 1][NW][32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -420,7 +424,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int kvb = 1 << a.kv_shift;
   const int nrow = min(128, a.Nq - qb * 128);
   // partial rows of this row's entries: key position p of the list (entry
-  // p >> kv_shift, token p & (kvb - 1)) owns 2 D floats, dK then dV
+  // p >> kv_shift, token p & (kvb - 1)) owns 2 D floats, dK (without the
+  // softmax scale, which the per-block sums apply) then dV
   float *const prow = PART ? a.part + ((size_t)wg * a.max_blocks << a.kv_shift) * (2 * D) : nullptr;
 
   // Q and dO of the block into LDS (swizzled; rows past Nq are zero)
@@ -470,138 +475,193 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   // per-lane LDS offsets: rows of Q/dO (A operands, query row l32 of
   // sub-tile qs, dims 16 ds + 8 hh ..) and transposing reads (B operands,
-  // dim 32 dt + l32, queries 32 qs + 16 ks + 8 p + 4 hh + 0..3)
-  int roff[DS], toff[DT][2][2];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hh) ^ swz<D>(l32)) << 4);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) toff[dt][ks][p] = tr_off<D>(16 * ks + 8 * p + 4 * hh, dt, lane);
+  // dim 32 dt + l32, queries 32 qs + 16 ks + 8 p + 4 hh + 0..3).  The
+  // swizzle XORs the chunk field, which lies below the row bits, so each
+  // family is one base register: row offset (ds) = rbo ^ 32 ds, transposing
+  // offset (dt, ks, p) = (tbo ^ (64 dt + 32 p)) + (16 ks + 8 p) rows.  Kept
+  // as 8 + 16 registers they left no room for a second set of accumulators
+  // (50 spills against 12).
+  int rbo = l32 * ROWB + ((hh ^ swz<D>(l32)) << 4);
+  int tbo = tr_off<D>(4 * hh, 0, lane);
 
   const uint16_t *kbase = a.k + (size_t)bh * a.Nk * D;
   const uint16_t *vbase = a.v + (size_t)bh * a.Nk * D;
 
-  for (int base = 0; base < cnt; base += CAP) {
+  // one query sub-step (32 queries) of a pass: S = Q K^T and dP = dO V^T,
+  // then P and dS, then dV += P^T dO and dK += dS^T Q
+  auto qs_step = [&](int qs, const bf16x8 *kf, const bf16x8 *vf, float sh, f32x16 *dkacc,
+                     f32x16 *dvacc) {
+    const unsigned char *qt = q_s + qs * 32 * ROWB;
+    const unsigned char *dt_ = do_s + qs * 32 * ROWB;
+    asm volatile("" : "+v"(rbo), "+v"(tbo));
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 qa = as_bf16x8(*(const u32x4 *)(qt + (rbo ^ (32 * ds))));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
+      const bf16x8 da = as_bf16x8(*(const u32x4 *)(dt_ + (rbo ^ (32 * ds))));
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ds], dp, 0, 0, 0);
+    }
+    bf16x8 pa[2], ga[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float pv[8], gv[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int q0 = qs * 32 + 16 * ks + 8 * hf + 4 * hh;
+        const f32x4 L = *(const f32x4 *)&lq_s[q0];
+        const f32x4 Dv = *(const f32x4 *)&dq_s[q0];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * ks + 4 * hf + j;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, sh - L[j]));
+          pv[4 * hf + j] = p;
+          gv[4 * hf + j] = p * (dp[r] - Dv[j]);
+        }
+      }
+      u32x4 wp, wg2;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        wp[e2] = pack_bf16x2(pv[2 * e2], pv[2 * e2 + 1]);
+        wg2[e2] = pack_bf16x2(gv[2 * e2], gv[2 * e2 + 1]);
+      }
+      pa[ks] = as_bf16x8(wp);
+      ga[ks] = as_bf16x8(wg2);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 dob = tr_pair(dt_, (tbo ^ (64 * dt)) + 16 * ks * ROWB, (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
+        dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], dob, dvacc[dt], 0, 0, 0);
+        const bf16x8 qbm = tr_pair(qt, (tbo ^ (64 * dt)) + 16 * ks * ROWB, (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
+        dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], qbm, dkacc[dt], 0, 0, 0);
+      }
+    }
+  };
+  f32x16 dka[PART ? 2 : 1][DT], dva[PART ? 2 : 1][DT];
+  int base = 0;
+  // the rows of keys 8 g + 4 hh + j of pass t (register 4 g + j, lane <->
+  // dim 32 dt + l32) from accumulator set P, into their entries' slots
+  auto store_group = [&](auto P_c, int t, int g) {
+    constexpr int P = decltype(P_c)::value;
+    const int4 kr = *(const int4 *)&keyrow2_s[P][wave][8 * g + 4 * hh];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
+      if (row >= 0) {
+        const int p = (base << a.kv_shift) + t * KT + wave * 32 + 8 * g + 4 * hh + j;
+        float *dst = prow + (size_t)p * (2 * D) + l32;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          __builtin_nontemporal_store(dka[P][dt][4 * g + j], dst + dt * 32);
+          __builtin_nontemporal_store(dva[P][dt][4 * g + j], dst + D + dt * 32);
+        }
+      }
+    }
+  };
+  for (base = 0; base < cnt; base += CAP) {
     const int pc = min(CAP, cnt - base);
     const int ntiles = ((pc << a.kv_shift) + KT - 1) / KT;
     __syncthreads();
     stage_list(a, idx_row, bias_row, base, pc, min(CAP, ((ntiles * KT) >> a.kv_shift) + 1), idx_s,
                sh_s, tid);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      // this wave's key (lane column l32) of the pass
-      const int pos = t * KT + wave * 32 + l32;
-      const int e = pos >> a.kv_shift;
-      const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
-      const float shv = sh_s[e];
-      const bool ok = kk < a.Nk && shv > -__builtin_inff();
-      const float sh = ok ? shv : -__builtin_inff();
-      if (hh == 0) keyrow_s[wave][l32] = ok ? kk : -1;
-      const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
-      const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
-      bf16x8 kf[DS], vf[DS];
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        kf[ds] = as_bf16x8(ld16(krp + ds * 16 + hh * 8));
-        vf[ds] = as_bf16x8(ld16(vrp + ds * 16 + hh * 8));
-      }
-      f32x16 dkacc[DT], dvacc[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dkacc[dt][r] = 0.f;
-          dvacc[dt][r] = 0.f;
-        }
-#pragma unroll
-      for (int qs = 0; qs < 4; ++qs) {
-        const unsigned char *qt = q_s + qs * 32 * ROWB;
-        const unsigned char *dt_ = do_s + qs * 32 * ROWB;
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
+    if constexpr (PART) {
+      // workspace form: tile t's rows are stored during tile t + 1 (one
+      // group of 8 keys after each of its 4 query sub-steps), so the stores
+      // spread over the products instead of ending each tile in a burst;
+      // the accumulators and the key rows alternate between two sets
+      auto tile = [&](auto P_c, int t, bool prev) {
+        constexpr int P = decltype(P_c)::value, O = 1 - P;
+        const int pos = t * KT + wave * 32 + l32;
+        const int e = pos >> a.kv_shift;
+        const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
+        const float shv = sh_s[e];
+        const bool ok = kk < a.Nk && shv > -__builtin_inff();
+        const float sh = ok ? shv : -__builtin_inff();
+        if (hh == 0) keyrow2_s[P][wave][l32] = ok ? kk : -1;
+        const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
+        const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
+        bf16x8 kf[DS], vf[DS];
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const bf16x8 qa = as_bf16x8(*(const u32x4 *)(qt + roff[ds]));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
-          const bf16x8 da = as_bf16x8(*(const u32x4 *)(dt_ + roff[ds]));
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ds], dp, 0, 0, 0);
-        }
-        // register r <-> query 32 qs + 8 (r >> 2) + 4 hh + (r & 3)
-        bf16x8 pa[2], ga[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float pv[8], gv[8];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int q0 = qs * 32 + 16 * ks + 8 * hf + 4 * hh;
-            const f32x4 L = *(const f32x4 *)&lq_s[q0];
-            const f32x4 Dv = *(const f32x4 *)&dq_s[q0];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int r = 8 * ks + 4 * hf + j;
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, sh - L[j]));
-              pv[4 * hf + j] = p;
-              gv[4 * hf + j] = p * (dp[r] - Dv[j]);
-            }
-          }
-          u32x4 wp, wg2;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            wp[e2] = pack_bf16x2(pv[2 * e2], pv[2 * e2 + 1]);
-            wg2[e2] = pack_bf16x2(gv[2 * e2], gv[2 * e2 + 1]);
-          }
-          pa[ks] = as_bf16x8(wp);
-          ga[ks] = as_bf16x8(wg2);
+          kf[ds] = as_bf16x8(ld16(krp + ds * 16 + hh * 8));
+          vf[ds] = as_bf16x8(ld16(vrp + ds * 16 + hh * 8));
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 dob = tr_pair(dt_, toff[dt][ks][0], toff[dt][ks][1]);
-            dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], dob, dvacc[dt], 0, 0, 0);
-            const bf16x8 qbm = tr_pair(qt, toff[dt][ks][0], toff[dt][ks][1]);
-            dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], qbm, dkacc[dt], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) {
+            dka[P][dt][r] = 0.f;
+            dva[P][dt][r] = 0.f;
           }
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+          qs_step(qs, kf, vf, sh, dka[P], dva[P]);
+          if (prev) store_group(std::integral_constant<int, O>(), t - 1, qs);
         }
+      };
+      int t = 0;
+      for (; t + 1 < ntiles; t += 2) {
+        tile(std::integral_constant<int, 0>(), t, t > 0);
+        tile(std::integral_constant<int, 1>(), t + 1, true);
       }
-      // the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
-      // of the wave, lane <-> dim 32 dt + l32
+      if (t < ntiles) {
+        tile(std::integral_constant<int, 0>(), t, t > 0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int4 kr = *(const int4 *)&keyrow_s[wave][8 * g + 4 * hh];
+        for (int g = 0; g < 4; ++g) store_group(std::integral_constant<int, 0>(), t, g);
+      } else if (ntiles > 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
-          if (row >= 0) {
-            if (PART) {
-              // plain stores into the entry's partial rows, each half-wave
-              // writing one whole 128-byte line, marked non-temporal (read
-              // once, by a later kernel): 4 % faster at the 720p shape than
-              // without the hint.  16-byte stores of dK^T and dV^T rows (a
-              // lane per key, 32-byte pieces of 32 lines per instruction)
-              // were slower, and running the per-block sums of one pass on
-              // a second stream beside the next pass gained nothing.
-              const int p = (base << a.kv_shift) + t * KT + wave * 32 + 8 * g + 4 * hh + j;
-              float *dst = prow + (size_t)p * (2 * D) + l32;
+        for (int g = 0; g < 4; ++g) store_group(std::integral_constant<int, 1>(), t - 1, g);
+      }
+    } else {
+      // atomic form: each tile's rows are added into dK and dV at its end
+      for (int t = 0; t < ntiles; ++t) {
+        const int pos = t * KT + wave * 32 + l32;
+        const int e = pos >> a.kv_shift;
+        const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
+        const float shv = sh_s[e];
+        const bool ok = kk < a.Nk && shv > -__builtin_inff();
+        const float sh = ok ? shv : -__builtin_inff();
+        if (hh == 0) keyrow2_s[0][wave][l32] = ok ? kk : -1;
+        const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
+        const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
+        bf16x8 kf[DS], vf[DS];
 #pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                __builtin_nontemporal_store(dkacc[dt][4 * g + j] * a.scale, dst + dt * 32);
-                __builtin_nontemporal_store(dvacc[dt][4 * g + j], dst + D + dt * 32);
-              }
-            } else {
+        for (int ds = 0; ds < DS; ++ds) {
+          kf[ds] = as_bf16x8(ld16(krp + ds * 16 + hh * 8));
+          vf[ds] = as_bf16x8(ld16(vrp + ds * 16 + hh * 8));
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dka[0][dt][r] = 0.f;
+            dva[0][dt][r] = 0.f;
+          }
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) qs_step(qs, kf, vf, sh, dka[0], dva[0]);
+        // the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
+        // of the wave, lane <-> dim 32 dt + l32
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int4 kr = *(const int4 *)&keyrow2_s[0][wave][8 * g + 4 * hh];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
+            if (row >= 0) {
               float *dkp = a.dk + ((size_t)bh * a.Nk + row) * D + l32;
               float *dvp = a.dv + ((size_t)bh * a.Nk + row) * D + l32;
 #pragma unroll
               for (int dt = 0; dt < DT; ++dt) {
-                unsafeAtomicAdd(dkp + dt * 32, dkacc[dt][4 * g + j] * a.scale);
-                unsafeAtomicAdd(dvp + dt * 32, dvacc[dt][4 * g + j]);
+                unsafeAtomicAdd(dkp + dt * 32, dka[0][dt][4 * g + j] * a.scale);
+                unsafeAtomicAdd(dvp + dt * 32, dva[0][dt][4 * g + j]);
               }
             }
           }
@@ -735,8 +795,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
       if (!on[u]) continue;
       const int c = c0 + lane + 64 * u;
       const int j = c / (D / 2), w = c % (D / 2);
-      float *dst = w < D / 4 ? a.dk + (key0 + j) * D + 4 * w : a.dv + (key0 + j) * D + 4 * (w - D / 4);
-      *(f32x4 *)dst = acc[u];
+      if (w < D / 4)
+        *(f32x4 *)(a.dk + (key0 + j) * D + 4 * w) = acc[u] * a.scale;
+      else
+        *(f32x4 *)(a.dv + (key0 + j) * D + 4 * (w - D / 4)) = acc[u];
     }
   }
 }
