@@ -634,6 +634,16 @@ def run_backward(args):
             raise SystemExit("non-finite gradient (workspace variant)")
     diff = {n: float(((a.double() - b.double()).norm() / a.double().norm()).item())
             for n, a, b in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv))}
+    # partial rows the workspace form stores: one per entry of the union of
+    # the lists of query blocks 2m and 2m + 1, against one per list entry
+    ih = idx.cpu().numpy()[0]
+    listed = union = 0
+    for h in range(H):
+        for m in range(0, nqb, 2):
+            a_ = ih[h, m, : ch[0, h, m]]
+            b_ = ih[h, m + 1, : ch[0, h, m + 1]] if m + 1 < nqb else a_[:0]
+            listed += a_.size + b_.size
+            union += np.union1d(a_, b_).size
     del ws
     flop = 10.0 * d * pairs
     tf, tfw = flop / bwd_ms / 1e9, flop / ws_ms / 1e9
@@ -647,6 +657,7 @@ def run_backward(args):
         "bwd_ws_ms": round(ws_ms, 4), "bwd_ws_over_fwd": round(ws_ms / fwd_ms, 3),
         "bwd_ws_slabs_per_pass": nslab, "bwd_ws_bytes": slab * nslab,
         "ws_vs_atomic_rel_fro": {n: float(f"{x:.3e}") for n, x in diff.items()},
+        "ws_partial_rows_per_list_entry": round(union / max(listed, 1), 4),
         "bwd_flop_per_call": flop,
         "roofline": {"kernel": "bsa_attn_bwd (zero + dq + dkdv kernels)", "bound": "mfma",
                      "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

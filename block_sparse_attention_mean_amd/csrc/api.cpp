@@ -42,6 +42,7 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
                     const int32_t *idx, const float *bias, const int32_t *count, int max_blocks,
                     float scale, float *dq, float *dk, float *dv, hipStream_t stream);
 size_t attn_bwd_slab_bytes(int Nq, int Nk, int d, int kv_block, int max_blocks);
+long long attn_bwd_union_entries(int Nq, int kv_block, int max_blocks);
 int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o,
                        const void *dout, const float *lse, int B, int H, int Nq, int Nk, int d,
                        int kv_block, const int32_t *idx, const float *bias, const int32_t *count,
@@ -331,13 +332,21 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *o, con
                               (hipStream_t)stream);
 }
 
+// The workspace form's index space: slot numbers of one slab's union
+// entries (pairs of query blocks x (2 max_blocks + 3 passes' padding)) and
+// key positions inside one pair's union list stay below 2^31.
+static bool bwd_ws_sizes_ok(int Nq, int kv_block, int max_blocks) {
+  const long long bpp = kv_block >= 128 ? 1 : 128 / kv_block;
+  if (bsa::attn_bwd_union_entries(Nq, kv_block, max_blocks) > kMaxIndex - 63) return false;
+  return (2LL * max_blocks + 3 * bpp) * kv_block <= kMaxIndex;
+}
+
 int bsa_attn_bwd_workspace_bytes(int Nq, int Nk, int d, int q_block, int kv_block,
                                  int max_blocks, size_t *bytes) {
   if (!bytes) return BSA_ERR_ARG;
   if (Nq < 1 || Nk < 1 || max_blocks < 1) return BSA_ERR_ARG;
   if (!head_dim_ok(d) || q_block != 128 || !pow2_block(kv_block)) return BSA_ERR_UNSUPPORTED;
-  const long long nqb = (Nq + 127) / 128;
-  if (nqb * max_blocks > kMaxIndex - 63) return BSA_ERR_SIZE;
+  if (!bwd_ws_sizes_ok(Nq, kv_block, max_blocks)) return BSA_ERR_SIZE;
   if ((long long)max_blocks * kv_block > kMaxIndex) return BSA_ERR_SIZE;
   if ((long long)Nk + kv_block > kMaxIndex) return BSA_ERR_SIZE;
   *bytes = bsa::attn_bwd_slab_bytes(Nq, Nk, d, kv_block, max_blocks);
@@ -352,7 +361,7 @@ int bsa_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o, 
   const int st = attn_bwd_check(q, k, v, o, dout, lse, B, H, Nq, Nk, d, q_block, kv_block, idx,
                                 bias, count, max_blocks, softmax_scale, dq, dk, dv);
   if (st != BSA_OK) return st;
-  if ((long long)(Nq + 127) / 128 * max_blocks > kMaxIndex - 63) return BSA_ERR_SIZE;
+  if (!bwd_ws_sizes_ok(Nq, kv_block, max_blocks)) return BSA_ERR_SIZE;
   // one wave per KV block of every slab in the per-block sums' grid
   if ((long long)B * H * (((long long)Nk + kv_block - 1) / kv_block) > kMaxIndex * 4)
     return BSA_ERR_SIZE;

@@ -147,6 +147,12 @@ struct BwdArgs {
   int bh0, nslab, Ms, cap;
   float *part;
   int32_t *kstart, *kcur, *ent;
+  // pairs of query blocks per slab, union entries per pair, and the union
+  // lists: block (-1 = empty), the two base-2 shifts (float2), class ends
+  int npairs, ucap;
+  int32_t *ublk;
+  float *ush;
+  int32_t *ucls;
 };
 
 namespace {
@@ -393,63 +399,104 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool PART>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int ROWB = D * 2;        // row bytes
-  constexpr int NCH = D / 8;         // 16-byte chunks per row
-  constexpr int DS = D / 16;         // k-steps over the head dim
-  constexpr int DT = D / 32;         // 32-wide dim tiles
-  constexpr int NW = 4;
-  constexpr int KT = 128;            // gathered keys per pass (32 per wave)
-  constexpr int QTB = 128 * ROWB;    // bytes of the Q (or dO) block
-
-  __shared__ __attribute__((aligned(16))) unsigned char q_s[QTB], do_s[QTB];
-  __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
-  __shared__ __attribute__((aligned(16))) float sh_s[CAP];
-  __shared__ __attribute__((aligned(16))) float dq_s[128], lq_s[128];
-  __shared__ __attribute__((aligned(16))) int32_t keyrow2_s[PART ? 2 : 1][NW][32];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int wg = xcd_order(blockIdx.x, a.total_wg);
-  const int qb = wg % a.nqb;
-  const int bh = a.bh0 + wg / a.nqb;
-  const size_t row_id = (size_t)bh * a.nqb + qb;
-  const int32_t *idx_row = a.idx + row_id * a.max_blocks;
-  const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
-  int cnt = a.count[row_id];
-  cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
-  const int kvb = 1 << a.kv_shift;
-  const int nrow = min(128, a.Nq - qb * 128);
-  // partial rows of this row's entries: key position p of the list (entry
-  // p >> kv_shift, token p & (kvb - 1)) owns 2 D floats, dK (without the
-  // softmax scale, which the per-block sums apply) then dV
-  float *const prow = PART ? a.part + ((size_t)wg * a.max_blocks << a.kv_shift) * (2 * D) : nullptr;
-
-  // Q and dO of the block into LDS (swizzled; rows past Nq are zero)
-  {
-    const uint16_t *qg = a.q + ((size_t)bh * a.Nq + (size_t)qb * 128) * D;
-    const uint16_t *dg = a.dout + ((size_t)bh * a.Nq + (size_t)qb * 128) * D;
+// One query sub-step (32 queries) of a dkdv pass: S = Q K^T and dP = dO V^T,
+// then P and dS, then dV += P^T dO and dK += dS^T Q.  qt / dt_ point at the
+// sub-step's 32 rows of the swizzled Q and dO blocks in LDS, lq / dd at its
+// 32 base-2 normalisers and D values; kf / vf hold the lane's key and value
+// row (B operands), sh its base-2 shift.  rbo / tbo are the lane's row and
+// transposing-read offset bases (see the kernels).
+template <int D>
+__device__ __forceinline__ void dkdv_substep(const unsigned char *qt, const unsigned char *dt_,
+                                             const float *lq, const float *dd, int &rbo, int &tbo,
+                                             int hh, const bf16x8 *kf, const bf16x8 *vf, float sh,
+                                             float scale_log2, f32x16 *dkacc, f32x16 *dvacc) {
+  constexpr int ROWB = D * 2;
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  asm volatile("" : "+v"(rbo), "+v"(tbo));
+  f32x16 s, dp;
 #pragma unroll
-    for (int i = 0; i < 128 * NCH / 256; ++i) {
-      const int c = i * 256 + tid;
-      const int r = c / NCH, ch = c % NCH;
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (r < nrow) {
-        x = ld16(qg + (size_t)r * D + ch * 8);
-        y = ld16(dg + (size_t)r * D + ch * 8);
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = 0.f;
+  }
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    const bf16x8 qa = as_bf16x8(*(const u32x4 *)(qt + (rbo ^ (32 * ds))));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
+    const bf16x8 da = as_bf16x8(*(const u32x4 *)(dt_ + (rbo ^ (32 * ds))));
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ds], dp, 0, 0, 0);
+  }
+  bf16x8 pa[2], ga[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float pv[8], gv[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int q0 = 16 * ks + 8 * hf + 4 * hh;
+      const f32x4 L = *(const f32x4 *)&lq[q0];
+      const f32x4 Dv = *(const f32x4 *)&dd[q0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * ks + 4 * hf + j;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, sh - L[j]));
+        pv[4 * hf + j] = p;
+        gv[4 * hf + j] = p * (dp[r] - Dv[j]);
       }
-      const int off = r * ROWB + ((ch ^ swz<D>(r)) << 4);
-      st16(q_s + off, x);
-      st16(do_s + off, y);
     }
-    // D and the base-2 normaliser per query (two lanes per query)
-    const int qr = tid >> 1, half = tid & 1;
+    u32x4 wp, wg2;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      wp[e2] = pack_bf16x2(pv[2 * e2], pv[2 * e2 + 1]);
+      wg2[e2] = pack_bf16x2(gv[2 * e2], gv[2 * e2 + 1]);
+    }
+    pa[ks] = as_bf16x8(wp);
+    ga[ks] = as_bf16x8(wg2);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 dob = tr_pair(dt_, (tbo ^ (64 * dt)) + 16 * ks * ROWB,
+                                 (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
+      dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], dob, dvacc[dt], 0, 0, 0);
+      const bf16x8 qbm = tr_pair(qt, (tbo ^ (64 * dt)) + 16 * ks * ROWB,
+                                 (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
+      dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], qbm, dkacc[dt], 0, 0, 0);
+    }
+  }
+}
+
+// Q and dO of `nrows` consecutive query rows starting at global row `q0row`
+// of the slab into LDS (swizzled; rows at or past Nq are zero), with each
+// row's D = dO . O and base-2 normaliser (+inf for rows past Nq or with lse
+// = -inf, so that their P vanishes).  nrows is a multiple of 128.
+template <int D>
+__device__ __forceinline__ void load_query_rows(const BwdArgs &a, int bh, int q0row, int nrows,
+                                                unsigned char *q_s, unsigned char *do_s,
+                                                float *dq_s, float *lq_s, int tid) {
+  constexpr int ROWB = D * 2;
+  constexpr int NCH = D / 8;
+  const int nrow = min(nrows, a.Nq - q0row);
+  const uint16_t *qg = a.q + ((size_t)bh * a.Nq + (size_t)q0row) * D;
+  const uint16_t *dg = a.dout + ((size_t)bh * a.Nq + (size_t)q0row) * D;
+  for (int c = tid; c < nrows * NCH; c += 256) {
+    const int r = c / NCH, ch = c % NCH;
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (r < nrow) {
+      x = ld16(qg + (size_t)r * D + ch * 8);
+      y = ld16(dg + (size_t)r * D + ch * 8);
+    }
+    const int off = r * ROWB + ((ch ^ swz<D>(r)) << 4);
+    st16(q_s + off, x);
+    st16(do_s + off, y);
+  }
+  // two lanes per query, each over half the dims
+  for (int qr0 = 0; qr0 < nrows; qr0 += 128) {
+    const int qr = qr0 + (tid >> 1), half = tid & 1;
     float part = 0.f;
     if (qr < nrow) {
-      const size_t off = ((size_t)bh * a.Nq + (size_t)qb * 128 + qr) * D + half * (D / 2);
+      const size_t off = ((size_t)bh * a.Nq + (size_t)q0row + qr) * D + half * (D / 2);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const u32x4 x = ld16(a.o + off + c * 8), y = ld16(a.dout + off + c * 8);
@@ -466,85 +513,167 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
       dq_s[qr] = part;
       float L = __builtin_inff();
       if (qr < nrow) {
-        const float l = a.lse[(size_t)bh * a.Nq + (size_t)qb * 128 + qr];
+        const float l = a.lse[(size_t)bh * a.Nq + (size_t)q0row + qr];
         if (l > -__builtin_inff()) L = l * kLog2e;
       }
       lq_s[qr] = L;
     }
   }
+}
+
+// Atomic form: one workgroup per query block; each pass's 128 keys are
+// added into dK and dV at the pass's end.
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;        // row bytes
+  constexpr int DS = D / 16;         // k-steps over the head dim
+  constexpr int DT = D / 32;         // 32-wide dim tiles
+  constexpr int NW = 4;
+  constexpr int KT = 128;            // gathered keys per pass (32 per wave)
+  constexpr int QTB = 128 * ROWB;    // bytes of the Q (or dO) block
+
+  __shared__ __attribute__((aligned(16))) unsigned char q_s[QTB], do_s[QTB];
+  __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
+  __shared__ __attribute__((aligned(16))) float sh_s[CAP];
+  __shared__ __attribute__((aligned(16))) float dq_s[128], lq_s[128];
+  __shared__ __attribute__((aligned(16))) int32_t keyrow_s[NW][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wg = xcd_order(blockIdx.x, a.total_wg);
+  const int qb = wg % a.nqb;
+  const int bh = a.bh0 + wg / a.nqb;
+  const size_t row_id = (size_t)bh * a.nqb + qb;
+  const int32_t *idx_row = a.idx + row_id * a.max_blocks;
+  const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
+  int cnt = a.count[row_id];
+  cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
+  const int kvb = 1 << a.kv_shift;
+
+  load_query_rows<D>(a, bh, qb * 128, 128, q_s, do_s, dq_s, lq_s, tid);
 
   // per-lane LDS offsets: rows of Q/dO (A operands, query row l32 of
   // sub-tile qs, dims 16 ds + 8 hh ..) and transposing reads (B operands,
   // dim 32 dt + l32, queries 32 qs + 16 ks + 8 p + 4 hh + 0..3).  The
   // swizzle XORs the chunk field, which lies below the row bits, so each
   // family is one base register: row offset (ds) = rbo ^ 32 ds, transposing
-  // offset (dt, ks, p) = (tbo ^ (64 dt + 32 p)) + (16 ks + 8 p) rows.  Kept
-  // as 8 + 16 registers they left no room for a second set of accumulators
-  // (50 spills against 12).
+  // offset (dt, ks, p) = (tbo ^ (64 dt + 32 p)) + (16 ks + 8 p) rows.
   int rbo = l32 * ROWB + ((hh ^ swz<D>(l32)) << 4);
   int tbo = tr_off<D>(4 * hh, 0, lane);
 
   const uint16_t *kbase = a.k + (size_t)bh * a.Nk * D;
   const uint16_t *vbase = a.v + (size_t)bh * a.Nk * D;
-
-  // one query sub-step (32 queries) of a pass: S = Q K^T and dP = dO V^T,
-  // then P and dS, then dV += P^T dO and dK += dS^T Q
-  auto qs_step = [&](int qs, const bf16x8 *kf, const bf16x8 *vf, float sh, f32x16 *dkacc,
-                     f32x16 *dvacc) {
-    const unsigned char *qt = q_s + qs * 32 * ROWB;
-    const unsigned char *dt_ = do_s + qs * 32 * ROWB;
-    asm volatile("" : "+v"(rbo), "+v"(tbo));
-    f32x16 s, dp;
+  f32x16 dka[DT], dva[DT];
+  for (int base = 0; base < cnt; base += CAP) {
+    const int pc = min(CAP, cnt - base);
+    const int ntiles = ((pc << a.kv_shift) + KT - 1) / KT;
+    __syncthreads();
+    stage_list(a, idx_row, bias_row, base, pc, min(CAP, ((ntiles * KT) >> a.kv_shift) + 1), idx_s,
+               sh_s, tid);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int pos = t * KT + wave * 32 + l32;
+      const int e = pos >> a.kv_shift;
+      const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
+      const float shv = sh_s[e];
+      const bool ok = kk < a.Nk && shv > -__builtin_inff();
+      const float sh = ok ? shv : -__builtin_inff();
+      if (hh == 0) keyrow_s[wave][l32] = ok ? kk : -1;
+      const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
+      const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
+      bf16x8 kf[DS], vf[DS];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
+      for (int ds = 0; ds < DS; ++ds) {
+        kf[ds] = as_bf16x8(ld16(krp + ds * 16 + hh * 8));
+        vf[ds] = as_bf16x8(ld16(vrp + ds * 16 + hh * 8));
+      }
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const bf16x8 qa = as_bf16x8(*(const u32x4 *)(qt + (rbo ^ (32 * ds))));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
-      const bf16x8 da = as_bf16x8(*(const u32x4 *)(dt_ + (rbo ^ (32 * ds))));
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ds], dp, 0, 0, 0);
-    }
-    bf16x8 pa[2], ga[2];
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float pv[8], gv[8];
+        for (int r = 0; r < 16; ++r) {
+          dka[dt][r] = 0.f;
+          dva[dt][r] = 0.f;
+        }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int q0 = qs * 32 + 16 * ks + 8 * hf + 4 * hh;
-        const f32x4 L = *(const f32x4 *)&lq_s[q0];
-        const f32x4 Dv = *(const f32x4 *)&dq_s[q0];
+      for (int qs = 0; qs < 4; ++qs)
+        dkdv_substep<D>(q_s + qs * 32 * ROWB, do_s + qs * 32 * ROWB, lq_s + qs * 32,
+                        dq_s + qs * 32, rbo, tbo, hh, kf, vf, sh, a.scale_log2, dka, dva);
+      // the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
+      // of the wave, lane <-> dim 32 dt + l32
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int4 kr = *(const int4 *)&keyrow_s[wave][8 * g + 4 * hh];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = 8 * ks + 4 * hf + j;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, sh - L[j]));
-          pv[4 * hf + j] = p;
-          gv[4 * hf + j] = p * (dp[r] - Dv[j]);
+          const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
+          if (row >= 0) {
+            float *dkp = a.dk + ((size_t)bh * a.Nk + row) * D + l32;
+            float *dvp = a.dv + ((size_t)bh * a.Nk + row) * D + l32;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              unsafeAtomicAdd(dkp + dt * 32, dka[dt][4 * g + j] * a.scale);
+              unsafeAtomicAdd(dvp + dt * 32, dva[dt][4 * g + j]);
+            }
+          }
         }
       }
-      u32x4 wp, wg2;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        wp[e2] = pack_bf16x2(pv[2 * e2], pv[2 * e2 + 1]);
-        wg2[e2] = pack_bf16x2(gv[2 * e2], gv[2 * e2 + 1]);
-      }
-      pa[ks] = as_bf16x8(wp);
-      ga[ks] = as_bf16x8(wg2);
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 dob = tr_pair(dt_, (tbo ^ (64 * dt)) + 16 * ks * ROWB, (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
-        dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], dob, dvacc[dt], 0, 0, 0);
-        const bf16x8 qbm = tr_pair(qt, (tbo ^ (64 * dt)) + 16 * ks * ROWB, (tbo ^ (64 * dt + 32)) + (16 * ks + 8) * ROWB);
-        dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], qbm, dkacc[dt], 0, 0, 0);
-      }
-    }
-  };
-  f32x16 dka[PART ? 2 : 1][DT], dva[PART ? 2 : 1][DT];
+  }
+}
+
+// Workspace form: one workgroup per pair of query blocks (2m, 2m + 1) of a
+// slab, over the pair's union list (built by pair_union_kernel): entries
+// both blocks list run their keys against all 256 queries (each half with
+// its own entry's shift), the others against their own block's 128, and
+// every union entry's dK (unscaled) and dV rows go once into its slot.
+// Two neighbouring query blocks share a large part of their lists, so this
+// stores fewer partial rows than one slot per list entry.  The union list
+// is grouped by class (both, first only, second only), each class padded to
+// whole passes, so a pass is of one class.  A pass's rows are stored during
+// the next pass (one group of 8 keys after each of its first 4 query
+// sub-steps) from a second set of accumulators, so the stores spread over
+// the products instead of ending each pass in a burst.
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;        // row bytes
+  constexpr int DS = D / 16;         // k-steps over the head dim
+  constexpr int DT = D / 32;         // 32-wide dim tiles
+  constexpr int NW = 4;
+  constexpr int KT = 128;            // gathered keys per pass (32 per wave)
+  constexpr int QTB = 256 * ROWB;    // bytes of the pair's Q (or dO) rows
+
+  __shared__ __attribute__((aligned(16))) unsigned char q_s[QTB], do_s[QTB];
+  __shared__ __attribute__((aligned(16))) int32_t idx_s[CAP];
+  __shared__ __attribute__((aligned(16))) float2 sh_s[CAP];
+  __shared__ __attribute__((aligned(16))) float dq_s[256], lq_s[256];
+  __shared__ __attribute__((aligned(16))) int32_t keyrow2_s[2][NW][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int pl = xcd_order(blockIdx.x, a.total_wg);  // pair of the chunk
+  const int m = pl % a.npairs;
+  const int bh = a.bh0 + pl / a.npairs;
+  const int kvb = 1 << a.kv_shift;
+  const int32_t *ub = a.ublk + (size_t)pl * a.ucap;
+  const float2 *us = (const float2 *)a.ush + (size_t)pl * a.ucap;
+  const int cb0 = a.ucls[(size_t)pl * 4], cb1 = a.ucls[(size_t)pl * 4 + 1];
+  const int ulen = a.ucls[(size_t)pl * 4 + 2];
+  // key position p of the union list (entry p >> kv_shift, token p &
+  // (kvb - 1)) owns 2 D floats of the slot array: dK, then dV
+  float *const prow = a.part + ((size_t)pl * a.ucap << a.kv_shift) * (2 * D);
+
+  load_query_rows<D>(a, bh, 2 * m * 128, 256, q_s, do_s, dq_s, lq_s, tid);
+
+  int rbo = l32 * ROWB + ((hh ^ swz<D>(l32)) << 4);
+  int tbo = tr_off<D>(4 * hh, 0, lane);
+
+  const uint16_t *kbase = a.k + (size_t)bh * a.Nk * D;
+  const uint16_t *vbase = a.v + (size_t)bh * a.Nk * D;
+  f32x16 dka[2][DT], dva[2][DT];
   int base = 0;
   // the rows of keys 8 g + 4 hh + j of pass t (register 4 g + j, lane <->
   // dim 32 dt + l32) from accumulator set P, into their entries' slots
@@ -565,26 +694,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   };
-  for (base = 0; base < cnt; base += CAP) {
-    const int pc = min(CAP, cnt - base);
+  for (base = 0; base < ulen; base += CAP) {
+    const int pc = min(CAP, ulen - base);
     const int ntiles = ((pc << a.kv_shift) + KT - 1) / KT;
+    const int nst = min(CAP, ((ntiles * KT) >> a.kv_shift) + 1);
     __syncthreads();
-    stage_list(a, idx_row, bias_row, base, pc, min(CAP, ((ntiles * KT) >> a.kv_shift) + 1), idx_s,
-               sh_s, tid);
+    for (int e = tid; e < nst; e += 256) {
+      const int blk = e < pc ? ub[base + e] : -1;
+      const float2 sh = e < pc ? us[base + e] : float2{-__builtin_inff(), -__builtin_inff()};
+      idx_s[e] = blk;
+      sh_s[e] = blk >= 0 ? sh : float2{-__builtin_inff(), -__builtin_inff()};
+    }
     __syncthreads();
-    if constexpr (PART) {
-      // workspace form: tile t's rows are stored during tile t + 1 (one
-      // group of 8 keys after each of its 4 query sub-steps), so the stores
-      // spread over the products instead of ending each tile in a burst;
-      // the accumulators and the key rows alternate between two sets
+    // the phase's passes of each class, one run each: both halves (H0 = 0,
+    // NH = 2), the first only (0, 1), the second only (1, 1); class ends
+    // are whole passes
+    auto tiles_below = [&](int cend) {
+      return min(ntiles, max(0, ((cend - base) << a.kv_shift) / KT));
+    };
+    auto run = [&](auto H0_c, auto NH_c, int tb, int te) {
+      constexpr int H0 = decltype(H0_c)::value, NH = decltype(NH_c)::value;
       auto tile = [&](auto P_c, int t, bool prev) {
         constexpr int P = decltype(P_c)::value, O = 1 - P;
         const int pos = t * KT + wave * 32 + l32;
         const int e = pos >> a.kv_shift;
-        const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
-        const float shv = sh_s[e];
-        const bool ok = kk < a.Nk && shv > -__builtin_inff();
-        const float sh = ok ? shv : -__builtin_inff();
+        const int blk = idx_s[e];
+        const int kk = (max(blk, 0) << a.kv_shift) + (pos & (kvb - 1));
+        const bool ok = blk >= 0 && kk < a.Nk;
+        const float2 shv = sh_s[e];
+        const float sh0 = ok ? shv.x : -__builtin_inff(), sh1 = ok ? shv.y : -__builtin_inff();
         if (hh == 0) keyrow2_s[P][wave][l32] = ok ? kk : -1;
         const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
         const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
@@ -601,73 +739,36 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
             dka[P][dt][r] = 0.f;
             dva[P][dt][r] = 0.f;
           }
+        // the previous pass's rows are stored during the first half, so
+        // each stored group's registers are free after it
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          qs_step(qs, kf, vf, sh, dka[P], dva[P]);
-          if (prev) store_group(std::integral_constant<int, O>(), t - 1, qs);
-        }
+        for (int h = H0; h < H0 + NH; ++h)
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) {
+            const int q32 = (4 * h + qs) * 32;
+            dkdv_substep<D>(q_s + q32 * ROWB, do_s + q32 * ROWB, lq_s + q32, dq_s + q32, rbo, tbo,
+                            hh, kf, vf, h == 0 ? sh0 : sh1, a.scale_log2, dka[P], dva[P]);
+            if (h == H0 && prev) store_group(std::integral_constant<int, O>(), t - 1, qs);
+          }
       };
-      int t = 0;
-      for (; t + 1 < ntiles; t += 2) {
-        tile(std::integral_constant<int, 0>(), t, t > 0);
+      int t = tb;
+      for (; t + 1 < te; t += 2) {
+        tile(std::integral_constant<int, 0>(), t, t > tb);
         tile(std::integral_constant<int, 1>(), t + 1, true);
       }
-      if (t < ntiles) {
-        tile(std::integral_constant<int, 0>(), t, t > 0);
+      if (t < te) {
+        tile(std::integral_constant<int, 0>(), t, t > tb);
 #pragma unroll
         for (int g = 0; g < 4; ++g) store_group(std::integral_constant<int, 0>(), t, g);
-      } else if (ntiles > 0) {
+      } else if (te > tb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) store_group(std::integral_constant<int, 1>(), t - 1, g);
       }
-    } else {
-      // atomic form: each tile's rows are added into dK and dV at its end
-      for (int t = 0; t < ntiles; ++t) {
-        const int pos = t * KT + wave * 32 + l32;
-        const int e = pos >> a.kv_shift;
-        const int kk = (idx_s[e] << a.kv_shift) + (pos & (kvb - 1));
-        const float shv = sh_s[e];
-        const bool ok = kk < a.Nk && shv > -__builtin_inff();
-        const float sh = ok ? shv : -__builtin_inff();
-        if (hh == 0) keyrow2_s[0][wave][l32] = ok ? kk : -1;
-        const uint16_t *krp = kbase + (size_t)(ok ? kk : 0) * D;
-        const uint16_t *vrp = vbase + (size_t)(ok ? kk : 0) * D;
-        bf16x8 kf[DS], vf[DS];
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          kf[ds] = as_bf16x8(ld16(krp + ds * 16 + hh * 8));
-          vf[ds] = as_bf16x8(ld16(vrp + ds * 16 + hh * 8));
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            dka[0][dt][r] = 0.f;
-            dva[0][dt][r] = 0.f;
-          }
-#pragma unroll
-        for (int qs = 0; qs < 4; ++qs) qs_step(qs, kf, vf, sh, dka[0], dva[0]);
-        // the 32 keys' rows: register r <-> key 8 (r >> 2) + 4 hh + (r & 3)
-        // of the wave, lane <-> dim 32 dt + l32
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int4 kr = *(const int4 *)&keyrow2_s[0][wave][8 * g + 4 * hh];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = j == 0 ? kr.x : (j == 1 ? kr.y : (j == 2 ? kr.z : kr.w));
-            if (row >= 0) {
-              float *dkp = a.dk + ((size_t)bh * a.Nk + row) * D + l32;
-              float *dvp = a.dv + ((size_t)bh * a.Nk + row) * D + l32;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                unsafeAtomicAdd(dkp + dt * 32, dka[0][dt][4 * g + j] * a.scale);
-                unsafeAtomicAdd(dvp + dt * 32, dva[0][dt][4 * g + j]);
-              }
-            }
-          }
-        }
-      }
-    }
+    };
+    const int tb0 = tiles_below(cb0), tb1 = tiles_below(cb1);
+    run(std::integral_constant<int, 0>(), std::integral_constant<int, 2>(), 0, tb0);
+    run(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), tb0, tb1);
+    run(std::integral_constant<int, 1>(), std::integral_constant<int, 1>(), tb1, ntiles);
   }
 }
 
@@ -676,33 +777,161 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4 *p, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) p[i] = z;
 }
 
-// Block of list entry e when it contributes keys (inside [0, M), shift
-// above -inf: the rule the staging of the dkdv kernel applies), else -1.
-__device__ __forceinline__ int entry_block(const BwdArgs &a, const int32_t *idx_row,
-                                           const float *bias_row, int e) {
-  const int blk = idx_row[e];
-  const float sh = bias_row ? bias_row[e] * kLog2e : 0.f;
-  return (blk >= 0 && blk < a.M && sh > -__builtin_inff()) ? blk : -1;
+// Union list of the pair of query blocks (2m, 2m + 1) of a slab (one
+// workgroup per pair of the chunk), grouped by class: blocks both list,
+// blocks only the first lists, blocks only the second lists, each class
+// padded with empty entries (-1) to a whole number of 128-key passes.  An
+// entry holds its block and the two lists' base-2 shifts (-inf where a list
+// does not hold it).  Classes are formed when both lists are, below their
+// counts, valid (block inside [0, M), shift above -inf) and strictly
+// ascending, as the plans are; otherwise (or past 4,096 entries) the pair's
+// union is the first list, then the second, invalid entries emptied, which
+// is correct for any list.  ucls[4 pair + 0, 1, 2] = the ends of the three
+// classes in entries.
+constexpr int UCAP_LDS = 4096;
+
+__device__ __forceinline__ int find_sorted(const int32_t *l, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (l[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && l[lo] == v ? lo : -1;
 }
 
-// Key-major lists, pass 1 (FILL = false): count the entries listing each
-// block; pass 2 (FILL = true): write (row of the chunk) * max_blocks +
-// entry at the block's cursor.  One workgroup per row of the chunk.
+__global__ __launch_bounds__(256) void pair_union_kernel(BwdArgs a) {
+  __shared__ int32_t l0[UCAP_LDS], l1[UCAP_LDS];
+  __shared__ int sc[3][256];
+  const int tid = threadIdx.x;
+  const int pl = blockIdx.x;
+  const int m = pl % a.npairs;
+  const int bh = a.bh0 + pl / a.npairs;
+  const bool has1 = 2 * m + 1 < a.nqb;
+  const size_t r0 = (size_t)bh * a.nqb + 2 * m, r1 = r0 + 1;
+  const int32_t *i0 = a.idx + r0 * a.max_blocks, *i1 = a.idx + r1 * a.max_blocks;
+  const float *b0 = a.bias ? a.bias + r0 * a.max_blocks : nullptr;
+  const float *b1 = a.bias ? a.bias + r1 * a.max_blocks : nullptr;
+  auto clampc = [&](int c) { return c < 0 ? 0 : (c > a.max_blocks ? a.max_blocks : c); };
+  const int c0 = clampc(a.count[r0]), c1 = has1 ? clampc(a.count[r1]) : 0;
+  const int bpp = a.kv_shift >= 7 ? 1 : 128 >> a.kv_shift;
+  auto up = [&](int n) { return (n + bpp - 1) / bpp * bpp; };
+  int32_t *ub = a.ublk + (size_t)pl * a.ucap;
+  float2 *us = (float2 *)a.ush + (size_t)pl * a.ucap;
+  const float NINF = -__builtin_inff();
+  auto shift = [](const float *b, int e) { return b ? b[e] * kLog2e : 0.f; };
+  auto valid = [&](int blk, float sh) { return blk >= 0 && blk < a.M && sh > NINF; };
+
+  bool ok = c0 <= UCAP_LDS && c1 <= UCAP_LDS;
+  if (ok) {
+    for (int e = tid; e < c0; e += 256) {
+      const int blk = i0[e];
+      ok = ok && valid(blk, shift(b0, e)) && (e == 0 || i0[e - 1] < blk);
+      l0[e] = blk;
+    }
+    for (int e = tid; e < c1; e += 256) {
+      const int blk = i1[e];
+      ok = ok && valid(blk, shift(b1, e)) && (e == 0 || i1[e - 1] < blk);
+      l1[e] = blk;
+    }
+  }
+  if (__syncthreads_and(ok)) {
+    // thread t walks entries [lo, hi) of each list
+    const int n0 = (c0 + 255) / 256, n1 = (c1 + 255) / 256;
+    const int lo0 = min(c0, tid * n0), hi0 = min(c0, lo0 + n0);
+    const int lo1 = min(c1, tid * n1), hi1 = min(c1, lo1 + n1);
+    int nb = 0, no1 = 0;
+    for (int e = lo0; e < hi0; ++e) nb += find_sorted(l1, c1, l0[e]) >= 0;
+    for (int e = lo1; e < hi1; ++e) no1 += find_sorted(l0, c0, l1[e]) < 0;
+    sc[0][tid] = nb;
+    sc[1][tid] = (hi0 - lo0) - nb;
+    sc[2][tid] = no1;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scans
+      int v[3];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) v[c] = tid >= off ? sc[c][tid - off] : 0;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 3; ++c) sc[c][tid] += v[c];
+      __syncthreads();
+    }
+    const int NB = sc[0][255], NO0 = sc[1][255], NO1 = sc[2][255];
+    const int PB = up(NB), PO0 = up(NO0), PO1 = up(NO1);
+    int pb = sc[0][tid] - nb, po0 = PB + sc[1][tid] - ((hi0 - lo0) - nb);
+    int po1 = PB + PO0 + sc[2][tid] - no1;
+    for (int e = lo0; e < hi0; ++e) {
+      const int blk = l0[e], j = find_sorted(l1, c1, blk);
+      if (j >= 0) {
+        ub[pb] = blk;
+        us[pb++] = float2{shift(b0, e), shift(b1, j)};
+      } else {
+        ub[po0] = blk;
+        us[po0++] = float2{shift(b0, e), NINF};
+      }
+    }
+    for (int e = lo1; e < hi1; ++e) {
+      const int blk = l1[e];
+      if (find_sorted(l0, c0, blk) < 0) {
+        ub[po1] = blk;
+        us[po1++] = float2{NINF, shift(b1, e)};
+      }
+    }
+    auto pad = [&](int from, int to) {
+      for (int u = from + tid; u < to; u += 256) {
+        ub[u] = -1;
+        us[u] = float2{NINF, NINF};
+      }
+    };
+    pad(NB, PB);
+    pad(PB + NO0, PB + PO0);
+    pad(PB + PO0 + NO1, PB + PO0 + PO1);
+    if (tid == 0) {
+      a.ucls[(size_t)pl * 4] = PB;
+      a.ucls[(size_t)pl * 4 + 1] = PB + PO0;
+      a.ucls[(size_t)pl * 4 + 2] = PB + PO0 + PO1;
+    }
+  } else {
+    const int P0 = up(c0), P1 = up(c1);
+    for (int u = tid; u < P0 + P1; u += 256) {
+      const bool first = u < P0;
+      const int e = first ? u : u - P0;
+      int blk = -1;
+      float sh = NINF;
+      if (e < (first ? c0 : c1)) {
+        blk = (first ? i0 : i1)[e];
+        sh = shift(first ? b0 : b1, e);
+        if (!valid(blk, sh)) {
+          blk = -1;
+          sh = NINF;
+        }
+      }
+      ub[u] = blk;
+      us[u] = first ? float2{sh, NINF} : float2{NINF, sh};
+    }
+    if (tid == 0) {
+      a.ucls[(size_t)pl * 4] = 0;
+      a.ucls[(size_t)pl * 4 + 1] = P0;
+      a.ucls[(size_t)pl * 4 + 2] = P0 + P1;
+    }
+  }
+}
+
+// Key-major lists, pass 1 (FILL = false): count the union entries listing
+// each block; pass 2 (FILL = true): write (pair of the chunk) * ucap +
+// entry, the entry's slot, at the block's cursor.  One workgroup per pair
+// of the chunk.
 template <bool FILL>
 __global__ __launch_bounds__(256) void csr_pass_kernel(BwdArgs a) {
-  const int r = blockIdx.x;
-  const int s = r / a.nqb;
-  const size_t row_id = (size_t)(a.bh0 + s) * a.nqb + r % a.nqb;
-  const int32_t *idx_row = a.idx + row_id * a.max_blocks;
-  const float *bias_row = a.bias ? a.bias + row_id * a.max_blocks : nullptr;
-  int cnt = a.count[row_id];
-  cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
-  for (int e = threadIdx.x; e < cnt; e += 256) {
-    const int blk = entry_block(a, idx_row, bias_row, e);
+  const int pl = blockIdx.x;
+  const int s = pl / a.npairs;
+  const int32_t *ub = a.ublk + (size_t)pl * a.ucap;
+  const int n = a.ucls[(size_t)pl * 4 + 2];
+  for (int u = threadIdx.x; u < n; u += 256) {
+    const int blk = ub[u];
     if (blk < 0) continue;
     if (FILL) {
       const int pos = atomicAdd(&a.kcur[(size_t)s * a.Ms + blk], 1);
-      a.ent[(size_t)s * a.cap + pos] = r * a.max_blocks + e;
+      a.ent[(size_t)s * a.cap + pos] = pl * a.ucap + u;
     } else {
       atomicAdd(&a.kstart[(size_t)s * a.Ms + blk], 1);
     }
@@ -839,11 +1068,11 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
   hipLaunchKernelGGL(zero_kernel, dim3(zg), dim3(256), 0, stream, (f32x4 *)dv, n4);
   if (d == 128) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), dim3((unsigned)total), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, false>), dim3((unsigned)total), dim3(256), 0,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128>), dim3((unsigned)total), dim3(256), 0,
                        stream, a);
   } else {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<64>), dim3((unsigned)total), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, false>), dim3((unsigned)total), dim3(256), 0,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64>), dim3((unsigned)total), dim3(256), 0,
                        stream, a);
   }
   return status_of(hipGetLastError());
@@ -852,19 +1081,26 @@ int launch_attn_bwd(const void *q, const void *k, const void *v, const void *o, 
 namespace {
 
 struct SlabLayout {
+  int npairs, ucap;   // pairs of query blocks, union entries per pair
   size_t part_bytes;  // partial rows of one slab
-  int Ms, cap;        // ints per slab of kstart / kcur, and of ent
+  int Ms, cap;        // ints per slab of kstart / kcur, and of ent (also ublk, ush pairs)
+  int ncls;           // ints per slab of ucls
   size_t bytes;       // all of one slab
 };
 
 SlabLayout slab_layout(int Nq, int Nk, int d, int kv_block, int max_blocks) {
   SlabLayout L;
-  const size_t nqb = (size_t)(Nq + 127) / 128;
+  const int nqb = (Nq + 127) / 128;
   const size_t M = ((size_t)Nk + kv_block - 1) / kv_block;
-  L.part_bytes = nqb * max_blocks * kv_block * 2 * d * sizeof(float);  // a multiple of 512
+  const int bpp = kv_block >= 128 ? 1 : 128 / kv_block;  // blocks per 128-key pass
+  L.npairs = (nqb + 1) / 2;
+  L.ucap = 2 * max_blocks + 3 * bpp;  // both lists, three classes padded to whole passes
+  L.part_bytes = (size_t)L.npairs * L.ucap * kv_block * 2 * d * sizeof(float);  // multiple of 512
   L.Ms = (int)((M + 1 + 63) / 64 * 64);
-  L.cap = (int)((nqb * max_blocks + 63) / 64 * 64);
-  L.bytes = L.part_bytes + 2 * (size_t)L.Ms * 4 + (size_t)L.cap * 4;  // 256-byte multiples
+  L.cap = (int)(((size_t)L.npairs * L.ucap + 63) / 64 * 64);
+  L.ncls = (L.npairs * 4 + 63) / 64 * 64;
+  // 256-byte multiples each
+  L.bytes = L.part_bytes + 2 * (size_t)L.Ms * 4 + (size_t)L.cap * (4 + 4 + 8) + (size_t)L.ncls * 4;
   return L;
 }
 
@@ -872,6 +1108,11 @@ SlabLayout slab_layout(int Nq, int Nk, int d, int kv_block, int max_blocks) {
 
 size_t attn_bwd_slab_bytes(int Nq, int Nk, int d, int kv_block, int max_blocks) {
   return slab_layout(Nq, Nk, d, kv_block, max_blocks).bytes;
+}
+
+long long attn_bwd_union_entries(int Nq, int kv_block, int max_blocks) {
+  const long long bpp = kv_block >= 128 ? 1 : 128 / kv_block;
+  return (long long)((Nq + 127) / 128 + 1) / 2 * (2LL * max_blocks + 3 * bpp);
 }
 
 int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *o,
@@ -910,6 +1151,8 @@ int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *
   a.scale_log2 = scale * kLog2e;
   a.Ms = L.Ms;
   a.cap = L.cap;
+  a.npairs = L.npairs;
+  a.ucap = L.ucap;
   a.total_wg = BH * a.nqb;
   if (d == 128)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
@@ -924,20 +1167,24 @@ int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *
     a.kstart = (int32_t *)(ws + (size_t)n * L.part_bytes);
     a.kcur = a.kstart + (size_t)n * L.Ms;
     a.ent = a.kcur + (size_t)n * L.Ms;
-    a.total_wg = n * a.nqb;
+    a.ublk = a.ent + (size_t)n * L.cap;
+    a.ush = (float *)(a.ublk + (size_t)n * L.cap);
+    a.ucls = (int32_t *)(a.ush + 2 * (size_t)n * L.cap);
+    a.total_wg = n * a.npairs;
     const size_t z4 = (size_t)n * L.Ms / 4;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)min((size_t)8192, (z4 + 255) / 256)), dim3(256),
                        0, stream, (f32x4 *)a.kstart, z4);
+    hipLaunchKernelGGL(pair_union_kernel, dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((csr_pass_kernel<false>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)n), dim3(1024), 0, stream, a);
     hipLaunchKernelGGL((csr_pass_kernel<true>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
     const unsigned rg = (unsigned)(((long long)n * a.M + 3) / 4);
     if (d == 128) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, true>), dim3((unsigned)a.total_wg), dim3(256),
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<128>), dim3((unsigned)a.total_wg), dim3(256),
                          0, stream, a);
       hipLaunchKernelGGL((bwd_reduce_kernel<128>), dim3(rg), dim3(256), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, true>), dim3((unsigned)a.total_wg), dim3(256),
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<64>), dim3((unsigned)a.total_wg), dim3(256),
                          0, stream, a);
       hipLaunchKernelGGL((bwd_reduce_kernel<64>), dim3(rg), dim3(256), 0, stream, a);
     }

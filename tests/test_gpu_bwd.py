@@ -156,6 +156,47 @@ def test_bwd_edge_lists(env, variant):
     _close(g, gv, wv, "dv")
 
 
+@pytest.mark.parametrize("kvb", [4, 1, 128])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bwd_pair_classes(env, variant, kvb):
+    """The workspace form runs query blocks (2m, 2m + 1) together over the
+    union of their lists, grouped into blocks both list, the first only and
+    the second only.  Pairs built for each case: identical blocks with
+    different shifts (all shared), disjoint lists (none shared), lists that
+    share a part, a list in descending order and one with a repeated block
+    (both not ascending: the pair falls back to one list after the other),
+    an empty list beside a full one, and a last query block of 40 rows
+    alone in its pair.  KV blocks of 4 (32 blocks per 128-key pass), 1 (128)
+    and 128 (one)."""
+    bsa, g, torch = env
+    g.say(f"case bwd {variant} pair classes kv={kvb}")
+    Nq, Nk, s = 10 * 128 + 40, 1500, 40
+    nqb, M = -(-Nq // 128), -(-Nk // kvb)
+    s = min(s, M // 2)
+    q, k, v, dout = _inputs(Nq, Nk, seed=40 + kvb)
+    rng = np.random.default_rng(kvb)
+    idx = np.full((nqb, s), -1, np.int32)
+    cnt = np.full(nqb, s, np.int32)
+    perm = rng.permutation(M)
+    a, b = np.sort(perm[:s]), np.sort(perm[s:2 * s])
+    idx[0], idx[1] = a, a                                # all shared
+    idx[2], idx[3] = a, b                                # none shared
+    idx[4], idx[5] = a, np.sort(np.concatenate([a[: s // 2], b[: s - s // 2]]))  # half shared
+    idx[6], idx[7] = a[::-1], a                          # descending: fallback
+    idx[8] = a
+    idx[8, 1] = a[0]                                     # repeated block: fallback
+    idx[9], cnt[9] = b, 0                                # empty beside the pair's other
+    idx[10] = np.sort(rng.choice(M, s, replace=False))   # 40 rows, a pair of one
+    bias = rng.random(idx.shape).astype(np.float32) * 3.0
+    gq, gk, gv = _run(env, variant, q, k, v, dout, kvb, idx, bias, cnt)
+    wq, wk, wv = oat.attn_bwd(q, k, v, dout, 128, kvb, idx, bias, cnt)
+    _close(g, gq[: 9 * 128], wq[: 9 * 128], "dq")
+    assert not gq[9 * 128: 10 * 128].any()               # empty list: zero gradient
+    _close(g, gq[10 * 128:], wq[10 * 128:], "dq last block")
+    _close(g, gk, wk, "dk")
+    _close(g, gv, wv, "dv")
+
+
 @pytest.mark.parametrize("variant,slabs", [("atomic", None), ("ws", None), ("ws", 1), ("ws", 3)])
 def test_bwd_batch_heads(env, variant, slabs):
     """B = 2, H = 2 in one call: every (b, h) against the oracle.  The
