@@ -10,7 +10,8 @@
 // and dV += P^T dO over every listed occurrence.  P comes from the
 // forward's log-sum-exp, so no online softmax is needed.
 //
-// Two kernels, both one workgroup per 128-query block (4 waves):
+// Two kernels, one workgroup (4 waves) per 128-query block (the dkdv
+// kernel of the workspace variant: per pair of query blocks):
 //   * dq: wave w owns queries 32 w .. +32.  The listed blocks are gathered
 //     into a three-slot LDS ring of 32-key K and V tiles as in the forward
 //     pass, and per tile S^T = K Q^T, dP^T = V dO^T (Q and dO stay in
@@ -24,7 +25,7 @@
 //     then dV += P^T dO and dK += dS^T Q with dO and Q through the
 //     transposing read.  Each key's rows are then added into fp32 dK and dV
 //     in global memory (atomic adds: a key is listed by many query blocks),
-//     or, in the workspace variant, stored as that list entry's partial rows.
+//     or, in the workspace variant, stored as its union entry's partial rows.
 // Outputs are fp32: dQ is written; the atomic form zeroes dK and dV first,
 // the workspace form writes every row of them.  Head dims 64 and 128.
 //
@@ -33,15 +34,20 @@
 // shape the adds (one per key value per listing query block) take most of
 // the backward's time.  The variant removes them: per chunk of (b, h)
 // slabs that fits the caller's workspace,
-//   * a key-major copy of the lists is built: per KV block, the (query
-//     block, entry) pairs that list it (count with integer atomics, an
-//     exclusive scan per slab, a fill through per-block cursors);
-//   * the dkdv kernel stores each listed key's dK (unscaled) and dV rows
-//     with plain stores into the entry's own slot of a partial buffer, a
-//     pass's rows during the next pass (two sets of accumulators), so the
-//     stores spread over the products instead of ending each pass in a
-//     burst;
-//   * one wave per KV block sums its entries' partial rows in fp32 and
+//   * query blocks 2m and 2m + 1 form a pair, and the union of their lists
+//     is built, grouped into blocks both list, the first only and the
+//     second only (each padded to whole 128-key passes); neighbouring query
+//     blocks share a large part of their lists, so the union is shorter
+//     than the two lists;
+//   * a key-major copy of the union lists is built: per KV block, the
+//     (pair, union entry) slots that list it (count with integer atomics,
+//     an exclusive scan per slab, a fill through per-block cursors);
+//   * the dkdv pair kernel runs each union entry's keys against the queries
+//     of the blocks that list it and stores its dK (unscaled) and dV rows
+//     with plain stores into the entry's own slot, a pass's rows during the
+//     next pass (two sets of accumulators), so the stores spread over the
+//     products instead of ending each pass in a burst;
+//   * one wave per KV block sums its slots' partial rows in fp32 and
 //     writes dK (times the softmax scale) and dV, zero for a block no
 //     query block lists.
 // The order in which a block's entries are summed is the fill's, which

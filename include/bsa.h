@@ -19,8 +19,9 @@
  *                      and runs online softmax with P.V accumulation (same
  *                      page, section "전제와 한계", first paragraph);
  *   bsa_attn_bwd,      its gradients dQ, dK, dV with the plan held fixed
- *   bsa_attn_bwd_ws    (dK and dV by atomic adds, or by sums of per-entry
- *                      partial rows in a caller's workspace);
+ *   bsa_attn_bwd_ws    (dK and dV by atomic adds, or by sums of partial
+ *                      rows in a caller's workspace, one per entry of the
+ *                      union of two neighbouring query blocks' lists);
  *   bsa_basa_*         the shifted-window + routed-window + pooled-memory
  *                      structure of the BASA page (onedev.kr/papers/688,
  *                      sections "어떻게 동작하나" and "무엇과 다른가") turned
@@ -234,22 +235,31 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
 
 /* ------------------------------------------------------------------------
  * The same gradients as bsa_attn_bwd (same definition, arguments and
- * outputs), with no atomic adds: each listed key's dK and dV rows go into
- * a per-entry slot of the caller's workspace, and one pass per KV block
- * sums the slots of every entry that lists it and writes dk and dv (every
- * row; zero for a block no query block lists).  The order of that sum
- * varies from run to run, so the last bits of dk and dv may too.
+ * outputs), with no atomic adds.  Query blocks 2m and 2m + 1 of a (b, h)
+ * run together over the union of their lists: a block both list is one
+ * entry whose keys meet all 256 queries (each block's queries under its
+ * own entry's shift), and each union entry's dK and dV rows go into one
+ * slot of the caller's workspace.  When the two lists are not both valid
+ * and strictly ascending below their counts (the plans of bsa_sip_plan
+ * are), or hold more than 4,096 entries, the union is simply the first
+ * list followed by the second.  One pass per KV block then sums the slots
+ * of every union entry that lists it and writes dk and dv (every row; zero
+ * for a block no query block lists).  The order of that sum varies from
+ * run to run, so the last bits of dk and dv may too.
  *
  * bsa_attn_bwd_workspace_bytes (host, no GPU) reports the bytes one
- * (b, h) slab needs:
- *   nQB * max_blocks * kv_block * 2 * d * 4   partial rows (fp32),
- * plus the slab's key-major lists (about 4 * (2 M + nQB * max_blocks)).
- * The call processes as many slabs at a time as workspace_bytes holds
- * (all B*H when it holds that many) and returns BSA_ERR_WORKSPACE when it
- * holds less than one, or workspace is NULL; workspace must be 256-byte
- * aligned (BSA_ERR_ALIGN) and its contents are undefined after the call.
- * nQB * max_blocks above 2^31 - 64, or B * H * M above 2^33 (M = KV
- * blocks of Nk), returns BSA_ERR_SIZE.  Other errors are bsa_attn_bwd's.
+ * (b, h) slab needs, with P = ceil(nQB / 2) pairs, U = 2 * max_blocks +
+ * 3 * max(1, 128 / kv_block) union entries per pair:
+ *   P * U * kv_block * 2 * d * 4        partial rows (fp32),
+ * plus the key-major lists (4 * (2 (M + 1) + P * U)), the union lists
+ * (12 * P * U) and 16 * P bytes of class ends, each array padded to 64
+ * elements.  The call processes as many slabs at a time as workspace_bytes
+ * holds (all B*H when it holds that many) and returns BSA_ERR_WORKSPACE
+ * when it holds less than one, or workspace is NULL; workspace must be
+ * 256-byte aligned (BSA_ERR_ALIGN) and its contents are undefined after
+ * the call.  P * U above 2^31 - 64, U * kv_block above 2^31 - 1, or
+ * B * H * M above 2^33 (M = KV blocks of Nk), returns BSA_ERR_SIZE.  Other
+ * errors are bsa_attn_bwd's.
  * --------------------------------------------------------------------- */
 int bsa_attn_bwd_workspace_bytes(int Nq, int Nk, int d, int q_block, int kv_block,
                                  int max_blocks, size_t *bytes /* host out */);
