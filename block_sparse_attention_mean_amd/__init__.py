@@ -298,9 +298,10 @@ def bsa_attn_bwd_ws(q, k, v, out, dout, lse, idx, bias, count, q_block=128, kv_b
                     softmax_scale=0.0, dq=None, dk=None, dv=None, workspace=None, slabs=None,
                     stream=None):
     """bsa_attn_bwd without atomic adds, through a workspace of partial rows
-    (one per entry of the union of two neighbouring query blocks' lists).  Without ``workspace`` one of ``slabs`` (b, h) slabs
-    (default all B*H) is allocated; the call runs as many slabs at a time
-    as the workspace holds."""
+    (one per entry of the union of two neighbouring query blocks' lists).
+    Without ``workspace`` one of ``slabs`` (b, h) slabs (default all B*H) is
+    allocated; the call runs as many slabs at a time as the workspace
+    holds."""
     (B, H, Nq, Nk, d, L), dq, dk, dv = _bwd_outputs(q, k, v, out, dout, lse, idx, bias, count,
                                                     q_block, dq, dk, dv)
     if workspace is None:
