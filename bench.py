@@ -905,6 +905,18 @@ def main():
         for _ in range(4):
             bsa.bsa_attn_fwd(q, k, v, idx, bias, cnt, 128, kvb, out=out)
     rec["ms_per_step_plan_every_4"] = round(_time(reuse4, 3) / 4, 4)
+    # the same step captured once into a HIP graph and replayed, as a serving
+    # loop would run it (outside the timed region; no launch from the host)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    rec["ms_per_step_graph"] = round(_time(graph.replay, max(3, args.steps)), 4)
+    del graph
     # one cold call (outside the timed region): a 512 MB write evicts the
     # Infinity Cache first
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

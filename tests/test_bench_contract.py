@@ -52,6 +52,7 @@ def test_bench_line_on_the_tiny_workload():
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config"):
         assert key in rec, key
     assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["ms_per_step_graph"] > 0    # the step replayed from a captured graph
     assert rec["value"] > 0 and rec["ms_per_step"] > 0 and rec["higher_is_better"] is True
     assert rec["config"]["workload"].startswith("tiny_2x32x32")
     roof = rec["roofline"]
