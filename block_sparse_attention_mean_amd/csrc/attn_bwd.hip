@@ -41,7 +41,8 @@
 //     than the two lists;
 //   * a key-major copy of the union lists is built: per KV block, the
 //     (pair, union entry) slots that list it (count with integer atomics,
-//     an exclusive scan per slab, a fill through per-block cursors);
+//     an exclusive scan per slab, a fill through per-block cursors, then
+//     each block's slots sorted);
 //   * the dkdv pair kernel runs each union entry's keys against the queries
 //     of the blocks that list it and stores its dK (unscaled) and dV rows
 //     with plain stores into the entry's own slot, a pass's rows during the
@@ -50,8 +51,9 @@
 //   * one wave per KV block sums its slots' partial rows in fp32 and
 //     writes dK (times the softmax scale) and dV, zero for a block no
 //     query block lists.
-// The order in which a block's entries are summed is the fill's, which
-// varies from run to run, as the atomic adds' order does.
+// The fill runs in whatever order its integer atomics take, so each block's
+// slots are sorted before the sums: the workspace form gives the same bits
+// on every run, for any number of slabs per pass (the atomic form does not).
 #include <type_traits>
 
 #include "common.h"
@@ -152,7 +154,7 @@ struct BwdArgs {
   // Ms ints, ent of cap ints)
   int bh0, nslab, Ms, cap;
   float *part;
-  int32_t *kstart, *kcur, *ent;
+  int32_t *kstart, *kcur, *ent, *ents;  // ents: each block's slots in ascending order
   // pairs of query blocks per slab, union entries per pair, and the union
   // lists: block (-1 = empty), the two base-2 shifts (float2), class ends
   int npairs, ucap;
@@ -973,8 +975,35 @@ __global__ __launch_bounds__(1024) void csr_scan_kernel(BwdArgs a) {
   if (t == 1023) ks[a.M] = part[1023];
 }
 
-// dK and dV of one KV block (one wave): the sum, in fp32, of the partial
-// rows of every entry that lists it; rows at or past Nk are not written.
+// Each KV block's slot numbers in ascending order (one wave per block):
+// the fill above places them in the order its integer atomics ran, which
+// varies from run to run; summing them in slot order makes dK and dV the
+// same bits on every run and for any number of slabs per pass.  An entry's
+// rank is the number of the block's slots below it (slots are distinct).
+__global__ __launch_bounds__(256) void csr_sort_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long gw = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= (long long)a.nslab * a.M) return;
+  const int s = (int)(gw / a.M), b = (int)(gw % a.M);
+  const int32_t *ks = a.kstart + (size_t)s * a.Ms;
+  const int beg = ks[b], n = ks[b + 1] - beg;
+  const int32_t *ent = a.ent + (size_t)s * a.cap + beg;
+  int32_t *out = a.ents + (size_t)s * a.cap + beg;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int own = i0 + lane < n ? ent[i0 + lane] : 0x7fffffff;
+    int rank = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int other = j0 + lane < n ? ent[j0 + lane] : 0x7fffffff;
+#pragma unroll 16
+      for (int j = 0; j < 64; ++j) rank += __shfl(other, j, 64) < own ? 1 : 0;
+    }
+    if (i0 + lane < n) out[rank] = own;
+  }
+}
+
+// dK and dV of one KV block (one wave): the sum, in fp32 and in ascending
+// slot order, of the partial rows of every entry that lists it; rows at or
+// past Nk are not written.
 // Lane l handles the 16-byte pieces c = c0 + l + 64 u of the block's
 // kvb * 2D floats (token c / (D/2); dK for the first D/4 pieces of a
 // token, dV for the rest).
@@ -987,7 +1016,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   const int s = (int)(gw / a.M), b = (int)(gw % a.M);
   const int32_t *ks = a.kstart + (size_t)s * a.Ms;
   const int beg = ks[b], end = ks[b + 1];
-  const int32_t *ent = a.ent + (size_t)s * a.cap;
+  const int32_t *ent = a.ents + (size_t)s * a.cap;
   const int kvb = 1 << a.kv_shift;
   const size_t F4 = (size_t)kvb * (D / 2);                // pieces per entry
   const int ntok = min(kvb, a.Nk - b * kvb);
@@ -1089,7 +1118,7 @@ namespace {
 struct SlabLayout {
   int npairs, ucap;   // pairs of query blocks, union entries per pair
   size_t part_bytes;  // partial rows of one slab
-  int Ms, cap;        // ints per slab of kstart / kcur, and of ent (also ublk, ush pairs)
+  int Ms, cap;        // ints per slab of kstart / kcur, and of ent (also ents, ublk, ush pairs)
   int ncls;           // ints per slab of ucls
   size_t bytes;       // all of one slab
 };
@@ -1106,7 +1135,7 @@ SlabLayout slab_layout(int Nq, int Nk, int d, int kv_block, int max_blocks) {
   L.cap = (int)(((size_t)L.npairs * L.ucap + 63) / 64 * 64);
   L.ncls = (L.npairs * 4 + 63) / 64 * 64;
   // 256-byte multiples each
-  L.bytes = L.part_bytes + 2 * (size_t)L.Ms * 4 + (size_t)L.cap * (4 + 4 + 8) + (size_t)L.ncls * 4;
+  L.bytes = L.part_bytes + 2 * (size_t)L.Ms * 4 + (size_t)L.cap * (4 + 4 + 4 + 8) + (size_t)L.ncls * 4;
   return L;
 }
 
@@ -1173,7 +1202,8 @@ int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *
     a.kstart = (int32_t *)(ws + (size_t)n * L.part_bytes);
     a.kcur = a.kstart + (size_t)n * L.Ms;
     a.ent = a.kcur + (size_t)n * L.Ms;
-    a.ublk = a.ent + (size_t)n * L.cap;
+    a.ents = a.ent + (size_t)n * L.cap;
+    a.ublk = a.ents + (size_t)n * L.cap;
     a.ush = (float *)(a.ublk + (size_t)n * L.cap);
     a.ucls = (int32_t *)(a.ush + 2 * (size_t)n * L.cap);
     a.total_wg = n * a.npairs;
@@ -1185,6 +1215,7 @@ int launch_attn_bwd_ws(const void *q, const void *k, const void *v, const void *
     hipLaunchKernelGGL(csr_scan_kernel, dim3((unsigned)n), dim3(1024), 0, stream, a);
     hipLaunchKernelGGL((csr_pass_kernel<true>), dim3((unsigned)a.total_wg), dim3(256), 0, stream, a);
     const unsigned rg = (unsigned)(((long long)n * a.M + 3) / 4);
+    hipLaunchKernelGGL(csr_sort_kernel, dim3(rg), dim3(256), 0, stream, a);
     if (d == 128) {
       hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<128>), dim3((unsigned)a.total_wg), dim3(256),
                          0, stream, a);

@@ -244,14 +244,16 @@ int bsa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
  * are), or hold more than 4,096 entries, the union is simply the first
  * list followed by the second.  One pass per KV block then sums the slots
  * of every union entry that lists it and writes dk and dv (every row; zero
- * for a block no query block lists).  The order of that sum varies from
- * run to run, so the last bits of dk and dv may too.
+ * for a block no query block lists), summing a block's slots in
+ * ascending slot order, so dk and dv are the same bits on every run and
+ * for any workspace size.
  *
  * bsa_attn_bwd_workspace_bytes (host, no GPU) reports the bytes one
  * (b, h) slab needs, with P = ceil(nQB / 2) pairs, U = 2 * max_blocks +
  * 3 * max(1, 128 / kv_block) union entries per pair:
  *   P * U * kv_block * 2 * d * 4        partial rows (fp32),
- * plus the key-major lists (4 * (2 (M + 1) + P * U)), the union lists
+ * plus the key-major lists (4 * (2 (M + 1) + 2 P U): block ranges,
+ * cursors, and each block's slots as filled and sorted), the union lists
  * (12 * P * U) and 16 * P bytes of class ends, each array padded to 64
  * elements.  The call processes as many slabs at a time as workspace_bytes
  * holds (all B*H when it holds that many) and returns BSA_ERR_WORKSPACE

@@ -232,17 +232,17 @@ def test_attn_bwd_workspace_bytes(bsa):
     """One (b, h) slab: per pair of query blocks, room for a union list of
     2 max_blocks + 3 passes' padding entries (a pass is 128 keys, so
     128 / kv_block blocks, at least one), each with kv_block * 2d fp32
-    partial rows; the key-major lists (two arrays of M + 1 ints and one slot
-    number per union entry); the union lists themselves (a block and two
-    shifts per entry); three class ends per pair (4 ints).  Each array is
-    padded to 64 elements."""
+    partial rows; the key-major lists (two arrays of M + 1 ints and two
+    slot numbers per union entry, as filled and sorted); the union lists (a
+    block and two shifts per entry); three class ends per pair (4 ints).
+    Each array is padded to 64 elements."""
     for Nq, Nk, d, kvb, L in [(300, 300, 128, 4, 8), (75600, 75600, 128, 4, 2048),
                               (256, 260, 64, 1, 70), (1000, 1000, 128, 128, 3)]:
         got = bsa.bsa_attn_bwd_workspace_bytes(Nq, Nk, d, L, 128, kvb)
         nqb, M = -(-Nq // 128), -(-Nk // kvb)
         pad = lambda n: -(-n // 64) * 64  # noqa: E731
         pairs, ucap = -(-nqb // 2), 2 * L + 3 * max(1, 128 // kvb)
-        want = (pairs * ucap * kvb * 2 * d * 4 + 4 * 2 * pad(M + 1) + 16 * pad(pairs * ucap)
+        want = (pairs * ucap * kvb * 2 * d * 4 + 4 * 2 * pad(M + 1) + 20 * pad(pairs * ucap)
                 + 4 * pad(4 * pairs))
         assert got == want
         assert got % 256 == 0

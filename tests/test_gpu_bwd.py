@@ -197,6 +197,36 @@ def test_bwd_pair_classes(env, variant, kvb):
     _close(g, gv, wv, "dv")
 
 
+def test_bwd_ws_deterministic(env):
+    """The workspace form sums each KV block's partial rows in ascending slot
+    order, so dK and dV are the same bits on every call and for any number
+    of slabs per pass (B = 1, H = 3: all slabs in one pass, then one per
+    pass)."""
+    bsa, g, torch = env
+    g.say("case bwd ws deterministic")
+    H, N, kvb, s = 3, 1000, 4, 60
+    nqb, M = -(-N // 128), N // 4
+    qs, ks, vs, ds, Os, ls, ids, bs, cs = ([] for _ in range(9))
+    for h in range(H):
+        q, k, v, dout = _inputs(N, N, seed=200 + h)
+        idx, bias, cnt, _ = _plan(nqb, M, s, opl.SIP, seed=h)
+        O, lse = _oracle_fwd(q, k, v, kvb, idx, bias, cnt)
+        for lst, x in zip((qs, ks, vs, ds, Os, ls, ids, bs, cs),
+                          (q, k, v, dout, O, lse, idx, bias, cnt)):
+            lst.append(x)
+    st = lambda xs: np.stack(xs)[None]  # noqa: E731
+    bf = lambda xs: g.to_dev_bf16(f64_to_bf16_bits(st(xs)))  # noqa: E731
+    args = (bf(qs), bf(ks), bf(vs), bf(Os), bf(ds), g.dev_f32(st(ls)), g.dev_i32(st(ids)),
+            g.dev_f32(st(bs)), g.dev_i32(st(cs)), 128, kvb)
+    runs = [bsa.bsa_attn_bwd_ws(*args, slabs=n) for n in (None, None, 1)]
+    torch.cuda.synchronize()
+    for r, run in enumerate(runs[1:], 1):
+        for name, a_, b_ in zip(("dq", "dk", "dv"), runs[0], run):
+            assert torch.equal(a_, b_), f"call {r}: {name} differs"
+    wq, wk, wv = oat.attn_bwd(qs[0], ks[0], vs[0], ds[0], 128, kvb, ids[0], bs[0], cs[0])
+    _close(g, runs[0][1].cpu().numpy()[0, 0], wk, "h0 dk")
+
+
 @pytest.mark.parametrize("variant,slabs", [("atomic", None), ("ws", None), ("ws", 1), ("ws", 3)])
 def test_bwd_batch_heads(env, variant, slabs):
     """B = 2, H = 2 in one call: every (b, h) against the oracle.  The
