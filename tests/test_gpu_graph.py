@@ -99,3 +99,57 @@ def test_step_graph_replays(env):
             else:
                 assert torch.equal(got, want), f"replay {r} (inputs {i}): {name} differs"
         g.say(f"  replay {r} (inputs {i}) matches the eager run")
+
+
+def test_basa_noalloc_graph_replays(env):
+    """The BASA step through the allocation-free list builder (its scratch in
+    the library's fixed device array, looked up once per device by an eager
+    call first), then the attention over the lists and the un-permute,
+    captured into one graph and replayed with inputs swapped: every output
+    equals an eager run's, byte for byte."""
+    bsa, g, torch = env
+    T, Hg, Wg, H, d, wh, ww, dy, dx, ph, pw, topk, kvb = 2, 20, 26, 2, 64, 10, 10, 5, 1, 2, 2, 3, 4
+    g.say(f"case graph basa noalloc T={T} Hg={Hg} Wg={Wg} H={H} d={d}")
+    inputs = [tuple(g.to_dev_bf16(x) for x in make_qkv(T, Hg, Wg, H, d, seed=s)) for s in (5, 6)]
+    q, k, v = (torch.empty_like(x) for x in inputs[0])
+    lists = bsa.bsa_basa_plan_noalloc(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kvb,
+                                      want_routes=True)  # allocates the outputs, looks up scratch
+    o = {key: lists[key] for key in ("qp", "kp", "vp", "idx", "count", "routes")}
+    out_perm = torch.empty_like(o["qp"])
+    out = torch.empty_like(q)
+
+    def step():
+        bsa.bsa_basa_plan_noalloc(q, k, v, T, Hg, Wg, wh, ww, dy, dx, ph, pw, topk, kvb, out=o)
+        bsa.bsa_attn_fwd(o["qp"], o["kp"], o["vp"], o["idx"], None, o["count"], 128, kvb,
+                         out=out_perm)
+        bsa.bsa_window_unpermute(out_perm, T, Hg, Wg, wh, ww, dy, dx, out=out)
+
+    outs = (o["qp"], o["kp"], o["vp"], o["idx"], o["count"], o["routes"], out_perm, out)
+    eager = []
+    for i in range(2):
+        for dst, src in zip((q, k, v), inputs[i]):
+            dst.copy_(src)
+        step()
+        torch.cuda.synchronize()
+        eager.append([x.clone() for x in outs])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    names = ("qp", "kp", "vp", "idx", "count", "routes", "out_perm", "out")
+    for r, i in enumerate((1, 0, 1)):
+        for x in outs:
+            x.view(torch.int16 if x.dtype == torch.bfloat16 else x.dtype).fill_(-7)
+        for dst, src in zip((q, k, v), inputs[i]):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(names, outs, eager[i]):
+            a = got.view(torch.int16) if got.dtype == torch.bfloat16 else got
+            b = want.view(torch.int16) if want.dtype == torch.bfloat16 else want
+            assert torch.equal(a, b), f"replay {r} (inputs {i}): {name} differs"
+        g.say(f"  replay {r} (inputs {i}) matches the eager run")
