@@ -47,8 +47,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 With ``--backward`` it prints one JSON report of the backward at the
 workload: the selector's SIP plan, one forward call for the output and its
-LSE, then bsa_attn_bwd (atomic adds) and bsa_attn_bwd_ws (per-entry
-partial rows, ``--bwd-slabs`` (b, h) slabs of workspace per pass) timed
+LSE, then bsa_attn_bwd (atomic adds) and bsa_attn_bwd_ws (partial rows per
+union entry of two query blocks' lists, ``--bwd-slabs`` (b, h) slabs of
+workspace per pass) timed
 with HIP events (warmup + steps), against the algorithmic 10 d flops per
 (valid query, listed valid key) pair, and the two results compared.
 
@@ -620,7 +621,7 @@ def run_backward(args):
     for t in (dq, dk, dv):
         if not torch.isfinite(t).all():
             raise SystemExit("non-finite gradient")
-    # the workspace variant: per-entry partial rows, summed per KV block
+    # the workspace variant: partial rows per union entry, summed per KV block
     slab = bsa.bsa_attn_bwd_workspace_bytes(N, N, d, s, 128, kvb)
     nslab = max(1, min(args.bwd_slabs, H))
     log(f"[backward] workspace variant: {nslab} slabs of {slab / 2**30:.2f} GiB per pass")
