@@ -260,17 +260,19 @@ def test_bwd_batch_heads(env, variant, slabs):
             _close(g, dv.cpu().numpy()[b, h], wv, f"b{b} h{h} dv")
 
 
-def test_bwd_full_size_sampled(env):
-    """Wan2.1-14B 720p shape, one head, the oracle's SIP plan (budget 2048 of
-    18,900 4-token blocks): the device forward's output and LSE feed the
-    device backward; dQ of sampled query blocks (including the 80-row last)
-    and dK/dV of sampled KV blocks (all query blocks that list them) against
-    the oracle.  The workspace variant against the oracle on the same
-    samples, and against the atomic one on every row: dq bit for bit (the
-    same kernel), dk and dv to fp32 summation-order error."""
+@pytest.mark.parametrize("workload", ["wan14b_720p", "hunyuan_720p"])
+def test_bwd_full_size_sampled(env, workload):
+    """Wan2.1-14B 720p shape (SIP budget 2048 of 18,900 4-token blocks) and
+    HunyuanVideo 720p shape (2272 of 29,700), one head, the oracle's SIP
+    plan: the device forward's output and LSE feed the device backward; dQ
+    of sampled query blocks (including the ragged last: 80 and 16 rows) and
+    dK/dV of sampled KV blocks (all query blocks that list them) against the
+    oracle.  The workspace variant against the oracle on the same samples,
+    and against the atomic one on every row: dq bit for bit (the same
+    kernel), dk and dv to fp32 summation-order error."""
     bsa, g, torch = env
-    c = CONFIGS["wan14b_720p"]
-    g.say("case bwd full size wan14b_720p head 0")
+    c = CONFIGS[workload]
+    g.say(f"case bwd full size {workload} head 0")
     qb, kb, vb = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=0)
     db, _, _ = make_qkv(c["T"], c["Hg"], c["Wg"], 1, c["d"], seed=77)
     S, _, _ = osel.select_scores_head(qb[0, 0], kb[0, 0], 128, 4, 8, 1)
