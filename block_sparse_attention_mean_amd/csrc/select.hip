@@ -507,6 +507,23 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
     }
   }
 
+  // Sweep 2 with 8 clusters per query block takes the product the other way
+  // round, D[centroid][key] = C . K_tile^T (the same register fragments as
+  // operands A and B swapped): lane l then owns key l % 32 of the step and
+  // register r centroid row 8 (r / 4) + 4 hh + r % 4 of a sub-tile, so a
+  // query block's 8 cluster rows are 4 registers in each lane half, its sum
+  // two in-lane adds and one exchange between the halves (the same pairing
+  // as the prefix sum over 8 lanes, so the same bits), and its 32 keys of a
+  // step store as one 128-byte line.  The rows' normalisers come from LDS.
+  constexpr bool TR = PASS == 1 && CL == 3;
+  __shared__ __attribute__((aligned(16))) float beta_s[TR ? 4 : 1][2][32];
+  if constexpr (TR) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (hh == 0) beta_s[wave][u][l32] = st_m[u];
+    __syncthreads();
+  }
+
   // Consecutive steps are software-pipelined: the products of step k + 1
   // run while the epilogue of step k (its statistics or scores) runs in the
   // same wave, slice by slice, so that the vector work issues under the
@@ -522,6 +539,27 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   // step; sub-tile u holds centroid rows rho0 + 32 u + l32.
   auto epi = [&](auto p_c, int k, int j, float cs) {
     constexpr int P = decltype(p_c)::value;
+    if constexpr (TR) {
+      // slice j: (sub-tile, query block) groups j GPS .. j GPS + GPS - 1
+      constexpr int GPS = 8 / KS;
+      const int ln = fresh_lane(), lw = ln & 31, hf = ln >> 5;
+      const int col = cbeg + k * CT + lw;
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) {
+        const int grp = j * GPS + gi, u = grp >> 2, q = grp & 3;
+        const float f = rs[u] * cs;
+        const f32x4 b = *(const f32x4 *)&beta_s[wave][u][8 * q + 4 * hf];
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[P][u][4 * q + i], f, -b[i]));
+        const float p = (x[2] + x[3]) + (x[0] + x[1]);
+        const float t = p + xor32(p);
+        const int qbi = ((rho0 + 32 * u) >> 3) + q;
+        if (hf == 0 && qbi < a.nqb && col < cend) sc_bh[(unsigned)qbi * (unsigned)M + (unsigned)col] = t;
+      }
+      return;
+    }
     const bool ragged = cbeg + k * CT + CT > cend;
     if (j == 0 && ragged) {
       // the last step of the row's last chunk: keys at or past cend (the
@@ -634,13 +672,16 @@ __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], clo[u][ks], acc[P][u], 0, 0, 0);
+        acc[P][u] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(clo[u][ks], kh[ks], acc[P][u], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], clo[u][ks], acc[P][u], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], chi[u][ks], acc[P][u], 0, 0, 0);
+        acc[P][u] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(chi[u][ks], kh[ks], acc[P][u], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_f16(kh[ks], chi[u][ks], acc[P][u], 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        acc[P][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl[ks], chi[u][ks], acc[P][u], 0, 0, 0);
+        acc[P][u] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(chi[u][ks], kl[ks], acc[P][u], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_f16(kl[ks], chi[u][ks], acc[P][u], 0, 0, 0);
       ep(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
