@@ -374,9 +374,11 @@ __device__ __forceinline__ int xcd_order(int L, int total) {
 // by direct global->LDS loads and feed the A operand, while each wave keeps
 // its 64 centroid rows (two 32-row sub-tiles) split in registers as the B
 // operand.  Lane l then owns centroid row l % 32 of each sub-tile and 16 of
-// the 32 keys of a step, so the row statistics are two registers.  PASS is
-// the sweep; CL = log2 of the clusters per query block, the levels of sweep
-// 2's cross-lane cluster sum (0 in sweep 1).
+// the 32 keys of a step, so the row statistics are two registers.  Sweep 2
+// at 8 clusters swaps the two operands (D[centroid][key], see TR below) so
+// that a query block's clusters share a lane.  PASS is the sweep; CL =
+// log2 of the clusters per query block, the levels of sweep 2's cross-lane
+// cluster sum at other cluster counts (0 in sweep 1).
 template <int D, int PASS, int CL>
 __global__ __launch_bounds__(256, 2) void score_kernel(SelArgs a) {
   constexpr int KS = D / 16;
