@@ -98,11 +98,14 @@ def _inputs(Nq, Nk, seed, d=128):
     (130, 2048, 2, 600, opl.SIP, 128),
     (300, 300, 4, 20, opl.SIP, 64), (256, 260, 1, 70, opl.SIP, 64), (640, 2048, 64, 8, opl.TOPK, 64),
     (130, 2048, 2, 600, opl.SIP, 64),
+    (256, 5000, 1, 4500, opl.SIP, 128),
 ])
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_bwd_matches_oracle(env, variant, Nq, Nk, kvb, s, mode, d):
     """Ragged query and key counts (a partial last KV block), block sizes 1-128,
-    SIP shifts and top-k, lists longer than one staging phase, d = 64 and 128."""
+    SIP shifts and top-k, lists longer than one staging phase, d = 64 and 128,
+    and lists of 4,500 entries (past the 4,096 the workspace form's pair
+    union searches in LDS, so that pair takes the concatenated union)."""
     bsa, g, torch = env
     g.say(f"case bwd {variant} Nq={Nq} Nk={Nk} kv={kvb} s={s} mode={mode} d={d}")
     q, k, v, dout = _inputs(Nq, Nk, seed=Nq + kvb, d=d)
